@@ -1,0 +1,226 @@
+"""CPU reference (oracle) for the Q4_K matmul path — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+Python binding) never imports it and shares no code with it.
+
+Thin ctypes marshalling around ``q4k_oracle.c`` (plain C, double precision);
+see that file for the arithmetic and its sources.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4k_oracle.c")
+_HDR = os.path.join(_HERE, "q4k_oracle.h")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+QK = 256
+BLOCK_BYTES = 144
+RMS_EPS = 1e-6
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (OpenMP over rows, -O2, strict IEEE)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp",
+                               "-ffp-contract=off", "-fno-fast-math",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_unpack_scales.restype = None
+        L.oracle_unpack_scales.argtypes = [_p, _p, _p]
+        L.oracle_dequant_block.restype = None
+        L.oracle_dequant_block.argtypes = [_p, _p]
+        L.oracle_dequant.restype = ctypes.c_int
+        L.oracle_dequant.argtypes = [_p, _i64, _i64, _p]
+        L.oracle_gemv_rows.restype = ctypes.c_int
+        L.oracle_gemv_rows.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.oracle_gemv_rows_d.restype = ctypes.c_int
+        L.oracle_gemv_rows_d.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.oracle_gemv_batch_rows.restype = ctypes.c_int
+        L.oracle_gemv_batch_rows.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+        L.oracle_bf16_round.restype = ctypes.c_float
+        L.oracle_bf16_round.argtypes = [ctypes.c_float]
+        L.oracle_gemm_sub.restype = ctypes.c_int
+        L.oracle_gemm_sub.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                      ctypes.c_int32, _p, _p]
+        L.oracle_rms.restype = ctypes.c_double
+        L.oracle_rms.argtypes = [_p, _i64, ctypes.c_double]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_stack.restype = ctypes.c_int
+        L.oracle_stack.argtypes = [_p, _p, _p, ctypes.c_int32, _i64, ctypes.c_double, _p, _p, _p]
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ctypes.c_int32]
+        L.oracle_get_threads.restype = ctypes.c_int32
+        L.oracle_get_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    return a
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, r.size
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle call failed with status %d" % rc)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
+
+
+def half_to_double(h: int) -> float:
+    return float(_load().oracle_half_to_double(int(h)))
+
+
+def unpack_scales(s12) -> tuple[np.ndarray, np.ndarray]:
+    s = _u8(s12)
+    assert s.size == 12
+    sc = np.zeros(8, np.int32)
+    mn = np.zeros(8, np.int32)
+    _load().oracle_unpack_scales(s.ctypes.data, sc.ctypes.data, mn.ctypes.data)
+    return sc, mn
+
+
+def dequant_block(blk) -> np.ndarray:
+    b = _u8(blk)
+    assert b.size == BLOCK_BYTES
+    out = np.empty(QK, np.float32)
+    _load().oracle_dequant_block(b.ctypes.data, out.ctypes.data)
+    return out
+
+
+def dequant(w, M: int, K: int) -> np.ndarray:
+    w = _u8(w)
+    assert w.size == M * (K // QK) * BLOCK_BYTES
+    out = np.empty((M, K), np.float32)
+    _check(_load().oracle_dequant(w.ctypes.data, M, K, out.ctypes.data))
+    return out
+
+
+def gemv(w, x, M: int, K: int, rows=None) -> tuple[np.ndarray, np.ndarray]:
+    """(y, S) in double for the listed rows (all rows if None)."""
+    w = _u8(w)
+    x = np.ascontiguousarray(x)
+    r, nr = _rows(rows)
+    n = nr if r is not None else M
+    y = np.empty(n, np.float64)
+    S = np.empty(n, np.float64)
+    rp = r.ctypes.data if r is not None else None
+    if x.dtype == np.float64:
+        assert x.size == K
+        _check(_load().oracle_gemv_rows_d(w.ctypes.data, x.ctypes.data, M, K, rp, nr,
+                                          y.ctypes.data, S.ctypes.data))
+    else:
+        x = _f32(x)
+        assert x.size == K
+        _check(_load().oracle_gemv_rows(w.ctypes.data, x.ctypes.data, M, K, rp, nr,
+                                        y.ctypes.data, S.ctypes.data))
+    return y, S
+
+
+def gemv_batch(w, X, M: int, K: int, rows=None) -> tuple[np.ndarray, np.ndarray]:
+    """X f32 [N][K] -> (Y, S) double [N][rows]."""
+    w = _u8(w)
+    X = _f32(X)
+    N = X.shape[0]
+    assert X.shape[1] == K
+    r, nr = _rows(rows)
+    n = nr if r is not None else M
+    Y = np.empty((N, n), np.float64)
+    S = np.empty((N, n), np.float64)
+    _check(_load().oracle_gemv_batch_rows(w.ctypes.data, X.ctypes.data, M, K, N,
+                                          r.ctypes.data if r is not None else None, nr,
+                                          Y.ctypes.data, S.ctypes.data))
+    return Y, S
+
+
+def bf16_round(v: float) -> float:
+    return float(_load().oracle_bf16_round(float(v)))
+
+
+def gemm(w, X, M: int, K: int, rows=None, toks=None, bf16_inputs: bool = False):
+    """X f32 [P][K] -> (Y, S) double [toks][rows]."""
+    w = _u8(w)
+    X = _f32(X)
+    P = X.shape[0]
+    assert X.shape[1] == K
+    r, nr = _rows(rows)
+    t, nt = _rows(toks)
+    n_r = nr if r is not None else M
+    n_t = nt if t is not None else P
+    Y = np.empty((n_t, n_r), np.float64)
+    S = np.empty((n_t, n_r), np.float64)
+    _check(_load().oracle_gemm_sub(w.ctypes.data, X.ctypes.data, M, K, P,
+                                   r.ctypes.data if r is not None else None, nr,
+                                   t.ctypes.data if t is not None else None, nt,
+                                   1 if bf16_inputs else 0, Y.ctypes.data, S.ctypes.data))
+    return Y, S
+
+
+def rms(v, eps: float = RMS_EPS) -> float:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return float(_load().oracle_rms(v.ctypes.data, v.size, eps))
+
+
+def silu(g: float) -> float:
+    return float(_load().oracle_silu(float(g)))
+
+
+def stack(mats, shapes, n_layers: int, hidden: int, h0, eps: float = RMS_EPS,
+          want_hidden: bool = False):
+    """Decode matmul chain.  mats: 5*n_layers+1 uint8 arrays (per layer
+    mix_in, mix_out, gate, up, down; then lm_head); shapes: matching (M, K)."""
+    assert len(mats) == len(shapes) == 5 * n_layers + 1
+    arrs = [_u8(m) for m in mats]
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    Ms = np.array([s[0] for s in shapes], np.int64)
+    Ks = np.array([s[1] for s in shapes], np.int64)
+    h0 = _f32(h0)
+    assert h0.size == hidden
+    logits = np.empty(shapes[-1][0], np.float64)
+    hid = np.empty((n_layers, hidden), np.float64) if want_hidden else None
+    _check(_load().oracle_stack(ptrs, Ms.ctypes.data, Ks.ctypes.data, n_layers, hidden, eps,
+                                h0.ctypes.data, logits.ctypes.data,
+                                hid.ctypes.data if hid is not None else None))
+    return (logits, hid) if want_hidden else logits

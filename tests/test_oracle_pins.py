@@ -1,0 +1,434 @@
+"""Pins of the CPU reference (oracle) to facts outside itself.
+
+Each test checks the oracle against something it does not compute: an
+independent library (numpy's binary16, torch's bfloat16 rounding, numpy's
+float64 matmul), hand-worked blocks (tests/golden/worked_blocks.txt), closed
+forms, exact rational arithmetic, or invariants that a dropped term, a wrong
+sign or index, or a transposed operand would break.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.golden_io import load_worked_blocks
+
+QK, BB = 256, 144
+
+
+def _f32_bits(v: float) -> int:
+    return int(np.array([v], np.float32).view(np.uint32)[0])
+
+
+# ---------------------------------------------------------------- binary16
+
+def test_half_decode_exhaustive_vs_numpy():
+    """All 65,536 binary16 patterns decode as numpy's float16 does."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(h)) for h in pats], np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros and infinities are kept
+    assert math.copysign(1.0, oracle.half_to_double(0x8000)) == -1.0
+    assert oracle.half_to_double(0x7C00) == math.inf
+    assert oracle.half_to_double(0xFC00) == -math.inf
+
+
+def test_half_decode_named_values():
+    assert oracle.half_to_double(0x3C00) == 1.0
+    assert oracle.half_to_double(0x0001) == 2.0 ** -24
+    assert oracle.half_to_double(0x03FF) == 1023 * 2.0 ** -24
+    assert oracle.half_to_double(0x0400) == 2.0 ** -14
+    assert oracle.half_to_double(0x7BFF) == 65504.0
+    assert oracle.half_to_double(0xC000) == -2.0
+    assert oracle.half_to_double(0x3555) == 0.333251953125
+
+
+# ---------------------------------------------------------------- worked blocks
+
+WORKED = load_worked_blocks()
+
+
+@pytest.mark.parametrize("item", WORKED, ids=[w["id"] for w in WORKED])
+def test_worked_block_dequant(item):
+    got = oracle.dequant_block(item["block"])
+    for k, (val, sign) in enumerate(item["expect"]):
+        exp = np.float32(float(val))
+        if val == 0:
+            exp = np.float32(-0.0) if sign < 0 else np.float32(0.0)
+        assert _f32_bits(got[k]) == _f32_bits(float(exp)), (item["id"], k, got[k], exp)
+
+
+@pytest.mark.parametrize("item", [w for w in WORKED if "sc" in w], ids=lambda w: w["id"])
+def test_worked_block_scales(item):
+    sc, mn = oracle.unpack_scales(item["block"][4:16])
+    assert list(sc) == item["sc"]
+    assert list(mn) == item["m"]
+
+
+def test_scale_packing_is_a_bijection():
+    """Every 12-byte pattern maps to distinct (sc, m) fields in 0..63: the 96
+    bits carry 16 six-bit fields exactly once each (checked bit by bit)."""
+    seen = np.zeros((16, 6), np.int64)
+    for byte in range(12):
+        for bit in range(8):
+            s = np.zeros(12, np.uint8)
+            s[byte] = 1 << bit
+            sc, mn = oracle.unpack_scales(s)
+            fields = list(sc) + list(mn)
+            hits = [(f, v) for f, v in enumerate(fields) if v]
+            assert len(hits) == 1, (byte, bit, fields)
+            f, v = hits[0]
+            assert v & (v - 1) == 0 and v < 64
+            seen[f, int(v).bit_length() - 1] += 1
+    assert (seen == 1).all()
+
+
+def test_dequant_rounding_tie_is_nearest_even():
+    """E5's exact value 30965759 is a tie between f32 neighbours; RNE picks the
+    even significand, so truncation or round-half-up would both fail here."""
+    blk = next(w for w in WORKED if w["id"] == "E5")["block"]
+    got = oracle.dequant_block(blk)
+    assert got[0] == np.float32(30965760.0)
+    assert 32768 * 63 * 15 - 1 == 30965759
+
+
+def test_dequant_matrix_places_blocks_row_major():
+    M, K = 3, 512
+    w = synth.q4k_weight(synth.key(9, 1), M, K)
+    full = oracle.dequant(w, M, K)
+    for r in range(M):
+        for b in range(K // QK):
+            blk = w[r, b * BB:(b + 1) * BB]
+            assert np.array_equal(full[r, b * QK:(b + 1) * QK].view(np.uint32),
+                                  oracle.dequant_block(blk).view(np.uint32))
+
+
+def _exact_block_values(blk: np.ndarray):
+    """Exact rational weights of one block, written from the format reading
+    with Python integers and Fractions (no floating point)."""
+    def half(h):
+        s, e, f = h >> 15, (h >> 10) & 31, h & 1023
+        v = Fraction(f, 1 << 24) if e == 0 else Fraction(1024 + f) * Fraction(2) ** (e - 25)
+        return -v if s else v
+    b = [int(t) for t in blk]
+    d, dmin = half(b[0] | b[1] << 8), half(b[2] | b[3] << 8)
+    s = b[4:16]
+    sc = [s[j] & 63 for j in range(4)] + [(s[j + 4] & 15) | ((s[j - 4] >> 6) << 4) for j in range(4, 8)]
+    mn = [s[j + 4] & 63 for j in range(4)] + [(s[j + 4] >> 4) | ((s[j] >> 6) << 4) for j in range(4, 8)]
+    qs = b[16:]
+    out = []
+    for g in range(4):
+        lo = [qs[32 * g + l] & 15 for l in range(32)]
+        hi = [qs[32 * g + l] >> 4 for l in range(32)]
+        out += [d * sc[2 * g] * q - dmin * mn[2 * g] for q in lo]
+        out += [d * sc[2 * g + 1] * q - dmin * mn[2 * g + 1] for q in hi]
+    return out
+
+
+def _exact_block_values_terms(blk: np.ndarray, k: int) -> bool:
+    """True if both terms of weight k (d*sc*q and dmin*m) are exactly zero."""
+    b = [int(t) for t in blk]
+    s = b[4:16]
+    j = k // 32
+    sc = (s[j] & 63) if j < 4 else ((s[j + 4] & 15) | ((s[j - 4] >> 6) << 4))
+    mn = (s[j + 4] & 63) if j < 4 else ((s[j + 4] >> 4) | ((s[j] >> 6) << 4))
+    g, r = k // 64, k % 64
+    q = (b[16 + 32 * g + r] & 15) if r < 32 else (b[16 + 32 * g + r - 32] >> 4)
+    d_zero = (b[0] | (b[1] & 0x7F) << 8) == 0
+    m_zero = (b[2] | (b[3] & 0x7F) << 8) == 0
+    return (d_zero or sc * q == 0) and (m_zero or mn == 0)
+
+
+def test_dequant_random_blocks_vs_exact_rationals():
+    """Random blocks over every finite binary16 d/dmin: the oracle's f32 equals
+    the exact rational value rounded once to f32 (numpy's RNE cast of the exact
+    double, which holds the rational exactly)."""
+    rng = np.random.default_rng(7)
+    raw = synth.raw_bytes(synth.key(9, 2), 64 * BB).reshape(64, BB)
+    for i in range(64):
+        blk = raw[i].copy()
+        # any finite binary16 for d and dmin (exponent field != 31)
+        for off in (0, 2):
+            while True:
+                h = int(rng.integers(0, 65536))
+                if (h >> 10) & 31 != 31:
+                    break
+            blk[off], blk[off + 1] = h & 0xFF, h >> 8
+        exact = _exact_block_values(blk)
+        got = oracle.dequant_block(blk)
+        d_neg, dmin_neg = bool(blk[1] & 0x80), bool(blk[3] & 0x80)
+        for k in range(256):
+            dv = float(exact[k])
+            assert Fraction(dv) == exact[k]           # exact in double
+            if dv == 0.0:
+                # IEEE: x - x = +0; a zero product keeps its operand's sign, so
+                # the difference is -0 only for (-0) - (+0).
+                a_zero = _exact_block_values_terms(blk, k)
+                neg = a_zero and d_neg and not dmin_neg
+                dv = -0.0 if neg else 0.0
+            assert _f32_bits(got[k]) == _f32_bits(float(np.float32(dv))), (i, k)
+
+
+# ---------------------------------------------------------------- GEMV
+
+def _rand_case(seed, M, K):
+    w = synth.q4k_weight(synth.key(9, 100 + seed), M, K)
+    x = synth.normal(synth.key(9, 200 + seed), K)
+    return w, x
+
+
+def test_gemv_zero_activation_is_exact_zero():
+    M, K = 7, 768
+    w, _ = _rand_case(1, M, K)
+    y, S = oracle.gemv(w, np.zeros(K, np.float32), M, K)
+    assert np.all(y == 0.0) and np.all(S == 0.0)
+
+
+def test_gemv_one_hot_returns_dequant_column():
+    M, K = 5, 512
+    w, _ = _rand_case(2, M, K)
+    Wd = oracle.dequant(w, M, K)
+    for k in (0, 1, 31, 32, 63, 64, 200, 255, 256, 300, 511):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y, _ = oracle.gemv(w, x, M, K)
+        assert np.array_equal(y, Wd[:, k].astype(np.float64)), k
+
+
+def test_gemv_all_ones_closed_form():
+    """x = 1: y_i = sum over sub-blocks of d*sc*Q - 32*dmin*m, where Q is the
+    integer nibble sum of the sub-block.  The oracle sums f32-rounded weights,
+    so the two differ by at most 2^-24 * sum|w| (one rounding per weight)."""
+    M, K = 6, 1024
+    w, _ = _rand_case(3, M, K)
+    y, S = oracle.gemv(w, np.ones(K, np.float32), M, K)
+    for i in range(M):
+        total = Fraction(0)
+        for b in range(K // QK):
+            blk = [int(t) for t in w[i, b * BB:(b + 1) * BB]]
+            d = Fraction(oracle.half_to_double(blk[0] | blk[1] << 8))
+            dmin = Fraction(oracle.half_to_double(blk[2] | blk[3] << 8))
+            sc, mn = oracle.unpack_scales(np.array(blk[4:16], np.uint8))
+            qs = blk[16:]
+            for g in range(4):
+                Qlo = sum(qs[32 * g + l] & 15 for l in range(32))
+                Qhi = sum(qs[32 * g + l] >> 4 for l in range(32))
+                total += d * int(sc[2 * g]) * Qlo - 32 * dmin * int(mn[2 * g])
+                total += d * int(sc[2 * g + 1]) * Qhi - 32 * dmin * int(mn[2 * g + 1])
+        assert abs(Fraction(y[i]) - total) <= Fraction(2) ** -24 * Fraction(S[i]) * 1.0000001
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 256), (4, 512), (2, 512)])
+def test_gemv_bruteforce_exact_rationals(M, K):
+    """Tiny matrices: y equals the exact rational sum of fl32(w)*x to 1e-15."""
+    w, x = _rand_case(10 + M + K, M, K)
+    y, S = oracle.gemv(w, x, M, K)
+    for i in range(M):
+        acc = Fraction(0)
+        for b in range(K // QK):
+            vals = _exact_block_values(w[i, b * BB:(b + 1) * BB])
+            for k, v in enumerate(vals):
+                acc += Fraction(float(np.float32(float(v)))) * Fraction(float(x[b * QK + k]))
+        assert abs(Fraction(y[i]) - acc) <= Fraction(1, 10 ** 15) * Fraction(S[i])
+
+
+def test_gemv_matches_library_matmul_on_dequant():
+    """Non-square M != K: y equals numpy's float64 matmul of the dequantised
+    matrix (a transposed operand or wrong row stride would fail)."""
+    M, K = 37, 1280
+    w, x = _rand_case(4, M, K)
+    Wd = oracle.dequant(w, M, K).astype(np.float64)
+    y, S = oracle.gemv(w, x, M, K)
+    ref = Wd @ x.astype(np.float64)
+    assert np.all(np.abs(y - ref) <= 1e-13 * S + 1e-300)
+    assert np.allclose(S, np.abs(Wd) @ np.abs(x.astype(np.float64)), rtol=1e-13, atol=0)
+
+
+def test_gemv_linearity_and_rows_subset():
+    M, K = 9, 768
+    w, x1 = _rand_case(5, M, K)
+    x2 = synth.normal(synth.key(9, 301), K).astype(np.float64)
+    x1 = x1.astype(np.float64)
+    a, b = 0.75, -1.5
+    y1, S1 = oracle.gemv(w, x1, M, K)
+    y2, S2 = oracle.gemv(w, x2, M, K)
+    y3, _ = oracle.gemv(w, a * x1 + b * x2, M, K)
+    assert np.all(np.abs(y3 - (a * y1 + b * y2)) <= 1e-12 * (abs(a) * S1 + abs(b) * S2))
+    rows = [8, 0, 3]
+    ys, _ = oracle.gemv(w, x1, M, K, rows=rows)
+    assert np.array_equal(ys, y1[rows])
+
+
+def test_gemv_block_permutation_invariance():
+    M, K = 4, 1536
+    w, x = _rand_case(6, M, K)
+    nb = K // QK
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    wp = w.reshape(M, nb, BB)[:, perm, :].reshape(M, nb * BB).copy()
+    xp = x.reshape(nb, QK)[perm].reshape(K).copy()
+    y, S = oracle.gemv(w, x, M, K)
+    yp, _ = oracle.gemv(wp, xp, M, K)
+    assert np.all(np.abs(y - yp) <= 1e-13 * S)
+
+
+def test_gemv_batch_columns_equal_single_gemv():
+    M, K, N = 11, 512, 3
+    w, _ = _rand_case(7, M, K)
+    X = synth.activations(9, N, K)
+    Y, S = oracle.gemv_batch(w, X, M, K)
+    for n in range(N):
+        y, s = oracle.gemv(w, X[n], M, K)
+        assert np.array_equal(Y[n], y) and np.array_equal(S[n], s)
+
+
+# ---------------------------------------------------------------- bf16 / GEMM
+
+def test_bf16_round_named_ties():
+    b2f = lambda b: float(np.array([b], np.uint32).view(np.float32)[0])
+    assert oracle.bf16_round(b2f(0x3F808000)) == b2f(0x3F800000)   # tie, kept bit even
+    assert oracle.bf16_round(b2f(0x3F818000)) == b2f(0x3F820000)   # tie, kept bit odd -> up
+    assert oracle.bf16_round(b2f(0x3F808001)) == b2f(0x3F810000)   # above the tie
+    assert oracle.bf16_round(b2f(0xBF818000)) == b2f(0xBF820000)   # negative tie
+    assert oracle.bf16_round(1.0) == 1.0
+
+
+def test_bf16_round_vs_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) < 0xFE]                 # finite, away from overflow
+    ties = (bits & 0xFFFF0000) | 0x8000
+    allb = np.concatenate([bits, ties]).astype(np.uint32)
+    vals = allb.view(np.float32)
+    ref = torch.from_numpy(vals.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    got = np.array([oracle.bf16_round(float(v)) for v in vals], np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_gemm_rows_equal_gemv_per_token():
+    M, K, P = 10, 512, 4
+    w, _ = _rand_case(8, M, K)
+    X = synth.activations(9, P, K, first=10)
+    Y, S = oracle.gemm(w, X, M, K)
+    for p in range(P):
+        y, s = oracle.gemv(w, X[p], M, K)
+        assert np.array_equal(Y[p], y) and np.array_equal(S[p], s)
+    Ys, _ = oracle.gemm(w, X, M, K, rows=[9, 2], toks=[3, 0])
+    assert np.array_equal(Ys, Y[np.ix_([3, 0], [9, 2])])
+
+
+def test_gemm_bf16_inputs_vs_library_matmul():
+    """bf16 reference = numpy float64 matmul of torch-rounded bf16 operands."""
+    torch = pytest.importorskip("torch")
+    M, K, P = 12, 768, 5
+    w, _ = _rand_case(9, M, K)
+    X = synth.activations(9, P, K, first=20)
+    Wd = oracle.dequant(w, M, K)
+    Wb = torch.from_numpy(Wd).to(torch.bfloat16).to(torch.float64).numpy()
+    Xb = torch.from_numpy(X).to(torch.bfloat16).to(torch.float64).numpy()
+    ref = Xb @ Wb.T
+    Y16, S16 = oracle.gemm(w, X, M, K, bf16_inputs=True)
+    assert np.all(np.abs(Y16 - ref) <= 1e-13 * S16)
+
+
+def test_gemm_bf16_exact_inputs_equal_f32_reference():
+    """E7 weights are small integers and x with <= 8 significant bits is bf16
+    exact, so rounding the inputs to bf16 must change nothing."""
+    blk = next(w for w in WORKED if w["id"] == "E7")["block"]
+    M, K, P = 3, 512, 2
+    w = np.tile(blk, (M, K // QK))
+    rng = np.random.default_rng(3)
+    X = (rng.integers(-128, 128, (P, K)) / 16.0).astype(np.float32)
+    Y, _ = oracle.gemm(w, X, M, K)
+    Y16, _ = oracle.gemm(w, X, M, K, bf16_inputs=True)
+    assert np.array_equal(Y, Y16)
+
+
+# ---------------------------------------------------------------- glue / stack
+
+def test_rms_and_silu_closed_forms():
+    assert oracle.rms(np.full(64, 3.0), 1e-6) == math.sqrt(9.0 + 1e-6)
+    assert oracle.rms(np.array([3.0, 4.0]), 0.0) == math.sqrt(12.5)
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) == 0.0
+    assert abs(oracle.silu(1.0) - 0.7310585786300049) < 1e-16
+    # silu(x) - silu(-x) = x
+    for g in (0.3, 2.0, 7.5):
+        assert abs((oracle.silu(g) - oracle.silu(-g)) - g) < 1e-15 * (1 + g)
+
+
+def _tiny_stack(n_layers, hidden=512, mix_in=768, mix_k=512, inter=768, vocab=256, cfg=9):
+    mats, shapes = [], []
+    t = 500
+    for _ in range(n_layers):
+        for (M, K) in ((mix_in, hidden), (hidden, mix_k), (inter, hidden), (inter, hidden), (hidden, inter)):
+            mats.append(synth.q4k_weight(synth.key(cfg, t), M, K))
+            shapes.append((M, K))
+            t += 1
+    mats.append(synth.q4k_weight(synth.key(cfg, t), vocab, hidden))
+    shapes.append((vocab, hidden))
+    return mats, shapes
+
+
+def test_stack_equals_composition_of_gemvs():
+    """The chain is a composition of the pinned GEMV with rmsn/silu glue."""
+    L, H = 2, 512
+    mats, shapes = _tiny_stack(L, hidden=H)
+    h0 = synth.normal(synth.key(9, 900), H)
+    logits, hid = oracle.stack(mats, shapes, L, H, h0, want_hidden=True)
+
+    def rmsn_gemv(i, v):
+        M, K = shapes[i]
+        v = np.asarray(v, np.float64)
+        y, _ = oracle.gemv(mats[i], v / math.sqrt(np.mean(v * v) + 1e-6), M, K)
+        return y
+
+    h = h0.astype(np.float64)
+    for l in range(L):
+        b = 5 * l
+        u = rmsn_gemv(b + 0, h)
+        h = h + rmsn_gemv(b + 1, u[:shapes[b + 1][1]])
+        g = rmsn_gemv(b + 2, h)
+        a = rmsn_gemv(b + 3, h)
+        act = g / (1.0 + np.exp(-g)) * a
+        h = h + rmsn_gemv(b + 4, act)
+        assert np.allclose(hid[l], h, rtol=1e-12, atol=1e-12)
+    ref = rmsn_gemv(5 * L, h)
+    assert np.allclose(logits, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_stack_zero_layers_is_normalised_lm_head():
+    H = 256
+    mats, shapes = _tiny_stack(0, hidden=H)
+    h0 = synth.normal(synth.key(9, 901), H)
+    logits = oracle.stack(mats, shapes, 0, H, h0)
+    r = math.sqrt(np.mean(h0.astype(np.float64) ** 2) + 1e-6)
+    y, S = oracle.gemv(mats[0], h0.astype(np.float64) / r, shapes[0][0], H)
+    # numpy's pairwise mean and the oracle's running sum round differently
+    assert np.all(np.abs(logits - y) <= 1e-13 * S)
+
+
+def test_stack_rejects_broken_chain():
+    mats, shapes = _tiny_stack(1, hidden=512)
+    shapes = list(shapes)
+    shapes[1] = (512, 1024)          # mixer-out K larger than mixer-in M
+    with pytest.raises(ValueError):
+        oracle.stack(mats, shapes, 1, 512, np.zeros(512, np.float32))
+
+
+def test_thread_count_does_not_change_bits():
+    M, K = 64, 1024
+    w, x = _rand_case(12, M, K)
+    oracle.set_threads(1)
+    y1, _ = oracle.gemv(w, x, M, K)
+    oracle.set_threads(4)
+    y4, _ = oracle.gemv(w, x, M, K)
+    assert np.array_equal(y1, y4)
