@@ -1,0 +1,327 @@
+"""Python binding of libq4k (MI355X / gfx950 Q4_K matmul library).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libq4k.so``.  PyTorch supplies device memory and streams; all
+calls enqueue on ``torch.cuda.current_stream()`` and return without
+synchronising.  If the library has not been built, importing the functions
+raises instead of falling back to anything else.
+
+The names follow the C ABI in ``include/q4k.h``:
+``dequant``, ``gemv``, ``gemv_batch``, ``gemm`` and ``DecodeStack``
+(``q4k_decode_stack_*``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4k.so")
+
+QK = 256
+BLOCK_BYTES = 144
+
+Q4K_OK = 0
+STATUS = {0: "Q4K_OK", -1: "Q4K_EINVAL", -2: "Q4K_ESHAPE", -3: "Q4K_EALIGN",
+          -4: "Q4K_ENOMEM", -5: "Q4K_EHIP", -6: "Q4K_EUNSUPPORTED"}
+BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS = range(7)
+
+# Every symbol include/q4k.h declares (checked by the CPU test suite).
+EXPORTS = (
+    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
+    "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
+    "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
+    "q4k_tune_gemv", "q4k_tune_gemm", "q4k_release_workspaces",
+)
+
+_lib = None
+
+
+class Q4KError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+class MatDesc(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("mix_in", MatDesc), ("mix_out", MatDesc),
+                ("gate", MatDesc), ("up", MatDesc), ("down", MatDesc)]
+
+
+class StackDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int64), ("n_layers", ctypes.c_int32),
+                ("layers", ctypes.POINTER(LayerDesc)), ("lm_head", MatDesc),
+                ("eps", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+def load(path: str | None = None):
+    """Load libq4k.so (built by ``bit_block_quantized_gguf_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    try:
+        # Load torch's HIP runtime first so that libq4k binds to the same
+        # libamdhip64.so.7 (one runtime per process).
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise ImportError("libq4k.so is not built (run __graft_entry__.build() or "
+                          "python bit_block_quantized_gguf_amd/build.py)")
+    L = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.q4k_last_error.restype = ctypes.c_char_p
+    L.q4k_last_error.argtypes = []
+    L.q4k_version.restype = ctypes.c_int
+    L.q4k_dequant.argtypes = [p, p, i64, i64, p]
+    L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
+    L.q4k_gemv_batch.argtypes = [p, p, p, i64, i64, i64, p]
+    L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p]
+    L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
+    L.q4k_decode_stack.argtypes = [p, p, p, p]
+    L.q4k_decode_stack_buffer.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(i64)]
+    L.q4k_decode_stack_nodes.argtypes = [p, ctypes.POINTER(i64)]
+    L.q4k_decode_stack_destroy.argtypes = [p]
+    L.q4k_decode_stack_destroy.restype = None
+    L.q4k_gemv_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.q4k_gemm_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32)]
+    L.q4k_tune_gemv.argtypes = [i32, i32]
+    L.q4k_tune_gemm.argtypes = [i32]
+    L.q4k_release_workspaces.argtypes = []
+    L.q4k_release_workspaces.restype = None
+    for name in ("q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
+                 "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
+                 "q4k_decode_stack_nodes", "q4k_gemv_config", "q4k_gemm_config",
+                 "q4k_tune_gemv", "q4k_tune_gemm"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(rc: int) -> None:
+    if rc != Q4K_OK:
+        msg = load().q4k_last_error().decode(errors="replace")
+        raise Q4KError(rc, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dev_tensor(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _weights(w, M, K):
+    torch = _torch()
+    _dev_tensor(w, torch.uint8, "w")
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    if w.numel() != M * (K // QK) * BLOCK_BYTES:
+        raise ValueError("w holds %d bytes, a %dx%d Q4_K matrix needs %d"
+                         % (w.numel(), M, K, M * (K // QK) * BLOCK_BYTES))
+    return w
+
+
+def weight_shape(w) -> tuple[int, int]:
+    """(M, K) of a [M, K/256*144] uint8 super-block tensor."""
+    M, rb = w.shape
+    if rb % BLOCK_BYTES:
+        raise ValueError("row length is not a whole number of 144-byte blocks")
+    return M, rb // BLOCK_BYTES * QK
+
+
+def version() -> int:
+    return int(load().q4k_version())
+
+
+def dequant(w, M: int | None = None, K: int | None = None, out=None):
+    torch = _torch()
+    if M is None:
+        M, K = weight_shape(w)
+    _weights(w, M, K)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=w.device)
+    _dev_tensor(out, torch.float32, "out")
+    check(load().q4k_dequant(w.data_ptr(), out.data_ptr(), M, K, _stream()))
+    return out
+
+
+def gemv(w, x, y=None, M: int | None = None, K: int | None = None):
+    torch = _torch()
+    if M is None:
+        M, K = weight_shape(w)
+    _weights(w, M, K)
+    _dev_tensor(x, torch.float32, "x")
+    if x.numel() != K:
+        raise ValueError("x must have K=%d elements" % K)
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=w.device)
+    _dev_tensor(y, torch.float32, "y")
+    check(load().q4k_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    return y
+
+
+def gemv_batch(w, X, Y=None, M: int | None = None, K: int | None = None):
+    torch = _torch()
+    if M is None:
+        M, K = weight_shape(w)
+    _weights(w, M, K)
+    _dev_tensor(X, torch.float32, "X")
+    N = X.shape[0]
+    if X.numel() != N * K:
+        raise ValueError("X must be [N, K]")
+    if Y is None:
+        Y = torch.empty((N, M), dtype=torch.float32, device=w.device)
+    _dev_tensor(Y, torch.float32, "Y")
+    check(load().q4k_gemv_batch(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, N, _stream()))
+    return Y
+
+
+def gemm(w, X, Y=None, M: int | None = None, K: int | None = None):
+    torch = _torch()
+    if M is None:
+        M, K = weight_shape(w)
+    _weights(w, M, K)
+    _dev_tensor(X, torch.float32, "X")
+    P = X.shape[0]
+    if X.numel() != P * K:
+        raise ValueError("X must be [P, K]")
+    if Y is None:
+        Y = torch.empty((P, M), dtype=torch.float32, device=w.device)
+    _dev_tensor(Y, torch.float32, "Y")
+    check(load().q4k_gemm(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, P, _stream()))
+    return Y
+
+
+def gemv_config(M: int, K: int, N: int = 1) -> tuple[int, int]:
+    wk, ks = ctypes.c_int32(), ctypes.c_int32()
+    check(load().q4k_gemv_config(M, K, N, ctypes.byref(wk), ctypes.byref(ks)))
+    return wk.value, ks.value
+
+
+def gemm_config(M: int, K: int, P: int) -> int:
+    ks = ctypes.c_int32()
+    check(load().q4k_gemm_config(M, K, P, ctypes.byref(ks)))
+    return ks.value
+
+
+def tune_gemv(waves_per_group: int = 0, k_splits: int = 0) -> None:
+    check(load().q4k_tune_gemv(waves_per_group, k_splits))
+
+
+def tune_gemm(k_splits: int = 0) -> None:
+    check(load().q4k_tune_gemm(k_splits))
+
+
+def release_workspaces() -> None:
+    load().q4k_release_workspaces()
+
+
+class DecodeStack:
+    """One hipGraph per plan replaying the per-token projection/MLP chain.
+
+    ``layers``: list of dicts with keys mix_in, mix_out, gate, up, down, each a
+    uint8 device tensor [M, K/256*144]; ``lm_head`` likewise.  The tensors are
+    borrowed (kept referenced here) and must not be freed while the plan lives.
+    """
+
+    def __init__(self, layers, lm_head, hidden: int, eps: float = 1e-6, kinds=None):
+        torch = _torch()
+        self._keep = []
+        arr = (LayerDesc * max(1, len(layers)))()
+        for i, L in enumerate(layers):
+            ld = arr[i]
+            ld.kind = int(kinds[i]) if kinds is not None else 0
+            for name in ("mix_in", "mix_out", "gate", "up", "down"):
+                t = L[name]
+                M, K = weight_shape(t)
+                _weights(t, M, K)
+                self._keep.append(t)
+                setattr(ld, name, MatDesc(t.data_ptr(), M, K))
+        M, K = weight_shape(lm_head)
+        _weights(lm_head, M, K)
+        self._keep.append(lm_head)
+        self.hidden = hidden
+        self.vocab = M
+        self.n_layers = len(layers)
+        desc = StackDesc(hidden, len(layers), arr, MatDesc(lm_head.data_ptr(), M, K),
+                         float(eps), 0)
+        self._desc_layers = arr
+        h = ctypes.c_void_p()
+        check(load().q4k_decode_stack_create(ctypes.byref(desc), _stream(), ctypes.byref(h)))
+        self._h = h
+        self._device = torch.cuda.current_device()
+
+    def __call__(self, h_in, logits=None):
+        torch = _torch()
+        _dev_tensor(h_in, torch.float32, "h_in")
+        if h_in.numel() != self.hidden:
+            raise ValueError("h_in must have %d elements" % self.hidden)
+        if logits is None:
+            logits = torch.empty(self.vocab, dtype=torch.float32, device=h_in.device)
+        _dev_tensor(logits, torch.float32, "logits")
+        check(load().q4k_decode_stack(self._h, h_in.data_ptr(), logits.data_ptr(), _stream()))
+        return logits
+
+    def run_no_copy(self, h_in):
+        """Launch one token and leave the logits in the arena (see ``buffer``)."""
+        torch = _torch()
+        _dev_tensor(h_in, torch.float32, "h_in")
+        check(load().q4k_decode_stack(self._h, h_in.data_ptr(), None, _stream()))
+
+    def buffer_ptr(self, layer: int, which: int) -> tuple[int, int]:
+        ptr, n = ctypes.c_void_p(), ctypes.c_int64()
+        check(load().q4k_decode_stack_buffer(self._h, layer, which, ctypes.byref(ptr),
+                                             ctypes.byref(n)))
+        return ptr.value, n.value
+
+    def buffer(self, layer: int, which: int):
+        """Device tensor viewing an arena buffer (valid until the next token)."""
+        torch = _torch()
+        ptr, n = self.buffer_ptr(layer, which)
+        view = _DeviceView(ptr, n)
+        return torch.as_tensor(view, device="cuda")
+
+    def nodes(self) -> int:
+        n = ctypes.c_int64()
+        check(load().q4k_decode_stack_nodes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().q4k_decode_stack_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class _DeviceView:
+    """Zero-copy description of a device float32 buffer for torch.as_tensor."""
+
+    def __init__(self, ptr: int, n: int):
+        self.__cuda_array_interface__ = {"shape": (n,), "typestr": "<f4", "data": (ptr, False),
+                                         "version": 2, "strides": None}

@@ -1,0 +1,108 @@
+// q4k_internal.hpp — host-side declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4k.h"
+
+namespace q4k {
+
+// ---------------------------------------------------------------- errors
+int fail(int code, const char *fmt, ...);
+void clear_error();
+int hip_fail(hipError_t e, const char *what);
+
+#define Q4K_HIP(call)                                                   \
+    do {                                                                \
+        hipError_t e_ = (call);                                         \
+        if (e_ != hipSuccess) return ::q4k::hip_fail(e_, #call);        \
+    } while (0)
+
+// ---------------------------------------------------------------- workspace
+// Split-K partial sums and per-tile arrival counters.  Counters start at zero
+// and every kernel that uses one returns it to zero, so no clearing work is
+// ever enqueued on the hot path (and none is recorded into a graph).
+struct Workspace {
+    float *partials = nullptr;
+    size_t partial_floats = 0;
+    unsigned *counters = nullptr;
+    size_t n_counters = 0;
+};
+
+// Workspace of (current device, stream), grown to at least the given sizes.
+// Growth synchronises the stream before the old buffers are released.
+int stream_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters,
+                     Workspace *out);
+
+// Allocate a zeroed workspace owned by the caller (used by stack plans).
+int alloc_workspace(size_t partial_floats, size_t n_counters, Workspace *out);
+void free_workspace(Workspace *ws);
+
+// ---------------------------------------------------------------- GEMV
+enum GemvEpilogue : int {
+    EPI_PLAIN = 0,   // y = W x
+    EPI_SCALE = 1,   // y = (W x) / rms(x)
+    EPI_RESID = 2,   // y = resid + (W x) / rms(x)
+    EPI_SWIGLU = 3,  // g = (Wg x)/rms(x), v = (Wu x)/rms(x), y = silu(g) * v
+};
+
+struct GemvParams {
+    const uint8_t *w0;      // first matrix (M x K super-blocks)
+    const uint8_t *w1;      // second matrix (EPI_SWIGLU), same shape
+    const float *x;         // [nv][K], vector stride x_stride floats
+    int64_t x_stride;
+    float *y;               // [nv][M], vector stride y_stride floats
+    int64_t y_stride;
+    float *y_g;             // EPI_SWIGLU: scaled gate output [M]
+    float *y_v;             // EPI_SWIGLU: scaled up output [M]
+    int32_t M, K, nb;       // nb = K / 256
+    int64_t row_bytes;      // nb * 144
+    int32_t ks;             // K splits across workgroups (grid.y)
+    float *ws;              // ks > 1: partials [ks][nmat][nv][M]
+    unsigned *cnt;          // ks > 1: one arrival counter per 64-row tile
+    const float *in_sq;     // EPI_SCALE/RESID/SWIGLU: per-64-row-tile sum of squares of x
+    int32_t in_sq_n;        // number of partials to add (ceil(K/64))
+    int32_t in_len;         // divisor of the mean (K)
+    const float *resid;     // EPI_RESID: residual [M]
+    float *out_sq;          // EPI != PLAIN: per-64-row-tile sum of squares of y
+    float eps;
+};
+
+struct GemvLaunch {
+    int wk;  // waves per workgroup (K split inside a workgroup)
+    int ks;  // K splits across workgroups
+};
+
+// Pick waves-per-group and cross-group splits for a GEMV shape.
+GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat);
+
+// Workspace needs of a launch.
+size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat);
+size_t gemv_counters(int64_t M);
+
+// Enqueue one GEMV kernel.  nv in {1,2,4,8,16} for EPI_PLAIN; nv = 1 otherwise.
+int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,
+                hipStream_t stream);
+
+// Per-64-row-tile sum of squares of v[0..n) (used to seed the stack).
+int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
+
+// Tuning override for benchmarks (0 = heuristic).
+void set_gemv_override(int wk, int ks);
+
+// ---------------------------------------------------------------- dequant
+int launch_dequant(const uint8_t *w, float *out, int64_t M, int64_t K, hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMM
+struct GemmLaunch {
+    int ks;  // K splits across workgroups
+};
+GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P);
+size_t gemm_partial_floats(const GemmLaunch &L, int64_t M, int64_t P);
+size_t gemm_counters(int64_t M, int64_t P);
+int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
+                const GemmLaunch &L, const Workspace &ws, hipStream_t stream);
+void set_gemm_override(int ks);
+
+}  // namespace q4k

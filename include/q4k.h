@@ -1,0 +1,221 @@
+/*
+ * q4k.h — C ABI of the MI355X (gfx950) Q4_K weight-only-quantised matmul
+ * library (libq4k.so).
+ *
+ * What it computes.  The pages ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis",
+ * TL;DR, §2 decode profile and §4b batched-GEMV witness; "Qwen3.6-27B on Apple
+ * M3 Pro — the llama.cpp parity bar", architecture list) describe a
+ * single-stream Qwen3.6-27B decode/prefill whose time is dominated by matmuls
+ * against weights kept resident as raw GGUF q4_k blocks, multiplied by an f32
+ * activation.  This library provides those matmuls: dequantisation, the
+ * batch-1 GEMV, an N-vector GEMV that reads the weights once, the prefill GEMM
+ * (bf16 MFMA), and the per-token chain of projection/MLP GEMVs replayed as one
+ * HIP graph — the one-submission-per-token decode that the diagnosis page
+ * names as the lever (§4).
+ *
+ * Weight format (public GGUF Q4_K convention; the pages name the format only).
+ * A matrix of M rows and K columns (K a multiple of 256) is M rows of K/256
+ * consecutive 144-byte super-blocks, each covering 256 consecutive weights:
+ *   bytes 0..1   d     binary16, little-endian
+ *   bytes 2..3   dmin  binary16, little-endian
+ *   bytes 4..15  eight 6-bit scales sc[] and eight 6-bit mins m[]:
+ *                s[j]&63 = sc[j], s[j+4]&63 = m[j] (j<4);
+ *                sc[j] = (s[j+4]&15) | (s[j-4]>>6)<<4,
+ *                m[j]  = (s[j+4]>>4) | (s[j]>>6)<<4     (j>=4)
+ *   bytes 16..143 quants: in 32-byte group g, byte l holds weight 64g+l (low
+ *                nibble) and weight 64g+32+l (high nibble)
+ * Weight k (sub-block j = k/32) is  w = d*sc[j]*q - dmin*m[j].
+ * The row stride is K/256*144 bytes; every block is 16-byte aligned when the
+ * base pointer is.
+ *
+ * Conventions for every entry point.
+ *  - Pointers are DEVICE pointers owned by the caller (e.g. from hipMalloc or a
+ *    torch CUDA tensor).  The library never frees them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; results are valid once the stream
+ *    has been synchronised.  Outputs are overwritten (not accumulated).
+ *  - Inputs and outputs must not alias.
+ *  - Arguments are validated before anything is enqueued; on error nothing is
+ *    enqueued, a negative q4k_status is returned and q4k_last_error() gives a
+ *    message (per calling thread).
+ *  - M, N or P equal to 0 is a valid no-op.  K must be a positive multiple of
+ *    256.  Dimensions are limited to 2^31-1 rows/columns.
+ *  - Required alignment: 16 bytes for w, x/X, y/Y and out.
+ *  - Results are deterministic: the same call on the same inputs returns the
+ *    same bits (all reductions run in a fixed order; no float atomics).
+ *  - Split-K partial sums live in a per-(device, stream) workspace that the
+ *    library allocates on first use and keeps until q4k_release_workspaces()
+ *    or process exit.  Calls queued on one stream are ordered; calls on
+ *    different streams use different workspaces.  Make the first call on a
+ *    stream outside HIP graph capture.
+ *  - Non-finite d/dmin propagate as IEEE arithmetic does; they are outside
+ *    the tested contract.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4K_BLOCK_WEIGHTS 256
+#define Q4K_BLOCK_BYTES 144
+
+typedef enum {
+    Q4K_OK = 0,
+    Q4K_EINVAL = -1,      /* null pointer with nonzero size, or bad enum/flag */
+    Q4K_ESHAPE = -2,      /* negative dims, K not a positive multiple of 256, chain mismatch */
+    Q4K_EALIGN = -3,      /* a pointer is not 16-byte aligned */
+    Q4K_ENOMEM = -4,      /* device or host allocation failed */
+    Q4K_EHIP = -5,        /* a HIP runtime call or kernel launch failed */
+    Q4K_EUNSUPPORTED = -6 /* no gfx950 device, or a size beyond the supported range */
+} q4k_status;
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char *q4k_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int q4k_version(void);
+
+/*
+ * Dequantise: out[i][k] = w_ik as f32, row-major [M][K].
+ * Bit-exact: the value is the exact d*sc*q - dmin*m rounded once to f32, the
+ * same for any evaluation order (every product is exact in f32).
+ */
+int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
+
+/*
+ * Batch-1 GEMV: y[i] = sum_k w_ik * x[k], x f32 [K], y f32 [M].
+ * The decode matmul ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §2 decode
+ * profile and §3): bandwidth-bound, one pass over the weight bytes.
+ * f32 accumulation; |y - exact| stays within 1e-4 * sum_k |w_ik x_k| + 1e-6.
+ */
+int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+
+/*
+ * N-vector GEMV in one launch, weights read once:
+ *   Y[n][i] = sum_k w_ik * X[n][k],  X f32 [N][K], Y f32 [N][M].
+ * The batched witness of "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4b,
+ * with N distinct activation vectors.  Any N >= 0; the kernels handle up to 16
+ * vectors per weight pass.
+ */
+int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
+                   void *stream);
+
+/*
+ * Prefill GEMM:  Y[p][i] = sum_k w_ik * X[p][k],  X f32 [P][K], Y f32 [P][M].
+ * The prompt-phase matmul ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §2
+ * prefill phases and §4b; "Qwen3.6-27B on Apple M3 Pro — the llama.cpp
+ * parity bar", the compute-bound prefill argument).  Weight tiles are
+ * dequantised to bf16 (round to nearest even) in LDS, X is rounded to bf16,
+ * products accumulate in f32 on the matrix cores.
+ */
+int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
+             void *stream);
+
+/* ------------------------------------------------------------------------
+ * Decode stack: the per-token chain of projection and MLP GEMVs of a
+ * hybrid Gated-DeltaNet / attention model, with the activation kept on the
+ * device and the whole chain replayed as ONE hipGraph launch per token
+ * ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4, the one-submission-per-
+ * token lever; layer shapes from "Qwen3.6-27B on Apple M3 Pro — the llama.cpp
+ * parity bar", architecture list).
+ *
+ * Per layer l (rmsn(v) = v / sqrt(mean(v^2) + eps), no gain):
+ *   u      = W_in  rmsn(h)                     mixer-in projection
+ *   h_mid  = h + W_out rmsn(u[0 : mix_out.K])  stand-in mixer + out projection
+ *   g      = W_gate rmsn(h_mid),  v = W_up rmsn(h_mid)
+ *   a      = silu(g) * v
+ *   h      = h_mid + W_down rmsn(a)
+ * and finally logits = W_lm rmsn(h).  The stand-in mixer (first mix_out.K
+ * outputs of the mixer-in projection) replaces the Gated-DeltaNet recurrence
+ * and attention body, which are not matmuls.
+ * ---------------------------------------------------------------------- */
+
+typedef struct {
+    const void *w; /* borrowed device pointer to the super-blocks; must outlive the plan */
+    int64_t M, K;
+} q4k_mat;
+
+typedef struct {
+    int32_t kind; /* 0 = Gated-DeltaNet-shaped, 1 = attention-shaped (informational) */
+    q4k_mat mix_in, mix_out, gate, up, down;
+} q4k_layer;
+
+typedef struct {
+    int64_t hidden;          /* residual width (K of mix_in/gate/up/lm_head, M of mix_out/down) */
+    int32_t n_layers;        /* >= 0 */
+    const q4k_layer *layers; /* n_layers entries, copied at create time */
+    q4k_mat lm_head;
+    float eps;               /* RMS epsilon, e.g. 1e-6 */
+    int32_t flags;           /* reserved, must be 0 */
+} q4k_stack_desc;
+
+typedef struct q4k_stack q4k_stack; /* opaque plan: owns its graph and activation arena */
+
+/* Validate the chain, allocate the arena, capture and instantiate the graph.
+ * Synchronises `stream`.  Requirements: every K is a multiple of 256;
+ * mix_in.K = gate.K = up.K = lm_head.K = hidden; mix_out.M = down.M = hidden;
+ * mix_out.K <= mix_in.M; gate.M = up.M = down.K. */
+int q4k_decode_stack_create(const q4k_stack_desc *desc, void *stream, q4k_stack **out);
+
+/* One token: copy h_in (f32 [hidden], device) into the arena, launch the
+ * graph, copy the logits (f32 [lm_head.M], device) out.  logits may be NULL
+ * to leave them in the arena only.  Enqueue-only; h_in/logits must stay valid
+ * until the stream reaches this point.  A plan must not run on two streams
+ * at once. */
+int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *stream);
+
+/* Arena buffers of the last token, for per-stage checks.  `which`:
+ *   Q4K_BUF_H     residual stream entering layer `layer` (layer = n_layers:
+ *                 the final residual that feeds lm_head)        [hidden]
+ *   Q4K_BUF_U     mixer-in output u of `layer`                  [mix_in.M]
+ *   Q4K_BUF_HMID  h_mid of `layer`                              [hidden]
+ *   Q4K_BUF_G     gate output g of `layer` (after rmsn scaling) [gate.M]
+ *   Q4K_BUF_V     up output v of `layer`                        [gate.M]
+ *   Q4K_BUF_A     silu(g) * v of `layer`                        [gate.M]
+ *   Q4K_BUF_LOGITS logits (layer ignored)                       [lm_head.M]
+ * Sets *ptr to the device address and *n to the element count. */
+enum {
+    Q4K_BUF_H = 0, Q4K_BUF_U = 1, Q4K_BUF_HMID = 2, Q4K_BUF_G = 3,
+    Q4K_BUF_V = 4, Q4K_BUF_A = 5, Q4K_BUF_LOGITS = 6
+};
+int q4k_decode_stack_buffer(q4k_stack *s, int32_t layer, int32_t which,
+                            const float **ptr, int64_t *n);
+
+/* Number of kernel nodes in the plan's graph (for launch-overhead accounting). */
+int q4k_decode_stack_nodes(q4k_stack *s, int64_t *n_nodes);
+
+/* Free the plan (graph, arena, workspace).  NULL-safe.  Synchronises the
+ * device work the plan may still have in flight. */
+void q4k_decode_stack_destroy(q4k_stack *s);
+
+/* ------------------------------------------------------------------------
+ * Launch-shape reporting and benchmark knobs.
+ * ---------------------------------------------------------------------- */
+
+/* Waves per workgroup and cross-workgroup K splits that q4k_gemv /
+ * q4k_gemv_batch pick for a shape (N vectors). */
+int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
+                    int32_t *k_splits);
+
+/* K splits that q4k_gemm picks for a shape. */
+int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *k_splits);
+
+/* Force the GEMV launch shape (waves_per_group in {2,4,8}, k_splits in
+ * 1..64) or the GEMM K splits; 0 restores the shape heuristics.  Process-wide
+ * and not synchronised with calls in flight: meant for benchmark sweeps. */
+int q4k_tune_gemv(int32_t waves_per_group, int32_t k_splits);
+int q4k_tune_gemm(int32_t k_splits);
+
+/* Free the split-K workspaces of all (device, stream) pairs.  Synchronises
+ * the device first.  Safe to call at any time when no call is in flight. */
+void q4k_release_workspaces(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4K_H */

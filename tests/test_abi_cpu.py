@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching a device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_block_quantized_gguf_amd as q4k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4k.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4k_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4k.LIB_PATH):
+        pytest.fail("libq4k.so is not built; run __graft_entry__.build()")
+    return q4k.load()
+
+
+def test_header_symbols_are_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", q4k.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    assert sorted(q4k.EXPORTS) == declared
+
+
+def test_library_is_gfx950_only():
+    """The offload bundle of the library names gfx950 as its only GPU target."""
+    blob = open(q4k.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_version(lib):
+    assert lib.q4k_version() == 10000
+
+
+P = 0x10000  # fake, 16-byte aligned "device" address: never dereferenced
+
+
+@pytest.mark.parametrize("M,K,code", [(-1, 256, -2), (4, 0, -2), (4, 100, -2), (4, 257, -2),
+                                      (4, -256, -2), (1 << 31, 256, -6)])
+def test_gemv_shape_errors(lib, M, K, code):
+    assert lib.q4k_gemv(P, P, P, M, K, None) == code
+    assert lib.q4k_last_error()
+
+
+def test_null_and_alignment_errors(lib):
+    assert lib.q4k_gemv(None, P, P, 4, 256, None) == -1
+    assert lib.q4k_gemv(P, None, P, 4, 256, None) == -1
+    assert lib.q4k_gemv(P, P, None, 4, 256, None) == -1
+    assert lib.q4k_gemv(P + 4, P, P, 4, 256, None) == -3
+    assert lib.q4k_gemv(P, P + 8, P, 4, 256, None) == -3
+    assert lib.q4k_dequant(P, P + 2, 4, 256, None) == -3
+    assert b"aligned" in lib.q4k_last_error()
+    assert lib.q4k_gemv_batch(P, P, P, 4, 256, -1, None) == -2
+    assert lib.q4k_gemm(P, P, P, 4, 256, -3, None) == -2
+    assert b"P must be" in lib.q4k_last_error()
+
+
+def test_zero_sizes_are_noops(lib):
+    # nothing is enqueued and no device is touched
+    assert lib.q4k_gemv(None, None, None, 0, 256, None) == 0
+    assert lib.q4k_dequant(None, None, 0, 512, None) == 0
+    assert lib.q4k_gemv_batch(None, None, None, 5, 256, 0, None) == 0
+    assert lib.q4k_gemm(None, None, None, 5, 256, 0, None) == 0
+    assert lib.q4k_last_error() == b""
+
+
+def test_stack_create_validation(lib):
+    out = ctypes.c_void_p()
+    assert lib.q4k_decode_stack_create(None, None, ctypes.byref(out)) == -1
+    mk = lambda M, K: q4k.MatDesc(P, M, K)
+    L = (q4k.LayerDesc * 1)()
+    L[0].mix_in, L[0].mix_out = mk(768, 512), mk(512, 512)
+    L[0].gate, L[0].up, L[0].down = mk(1024, 512), mk(1024, 512), mk(512, 1024)
+    d = q4k.StackDesc(512, 1, L, mk(300, 512), 1e-6, 0)
+    bad = [
+        ("flags", lambda d: setattr(d, "flags", 1), -1),
+        ("hidden", lambda d: setattr(d, "hidden", 500), -2),
+        ("mixout", lambda d: setattr(L[0], "mix_out", mk(512, 1024)), -2),
+        ("down", lambda d: setattr(L[0], "down", mk(512, 768)), -2),
+        ("lm", lambda d: setattr(d, "lm_head", mk(300, 256)), -2),
+        ("align", lambda d: setattr(L[0], "gate", q4k.MatDesc(P + 4, 1024, 512)), -3),
+    ]
+    for name, mut, code in bad:
+        L[0].mix_in, L[0].mix_out = mk(768, 512), mk(512, 512)
+        L[0].gate, L[0].up, L[0].down = mk(1024, 512), mk(1024, 512), mk(512, 1024)
+        d = q4k.StackDesc(512, 1, L, mk(300, 512), 1e-6, 0)
+        mut(d)
+        assert lib.q4k_decode_stack_create(ctypes.byref(d), None, ctypes.byref(out)) == code, name
+        assert not out.value
+    lib.q4k_decode_stack_destroy(None)  # NULL-safe
+
+
+def test_stack_entry_points_reject_null(lib):
+    n = ctypes.c_int64()
+    ptr = ctypes.c_void_p()
+    assert lib.q4k_decode_stack(None, P, P, None) == -1
+    assert lib.q4k_decode_stack_buffer(None, 0, 0, ctypes.byref(ptr), ctypes.byref(n)) == -1
+    assert lib.q4k_decode_stack_nodes(None, ctypes.byref(n)) == -1
+
+
+def test_launch_shape_reports(lib):
+    for (M, K) in [(17408, 5120), (5120, 17408), (5120, 6144), (16480, 5120), (248320, 5120),
+                   (512, 1024), (1024, 512), (1, 256)]:
+        wk, ks = q4k.gemv_config(M, K, 1)
+        nb = K // 256
+        assert wk in (2, 4, 8) and 1 <= ks <= 64
+        assert ks == 1 or ks * wk <= nb
+    assert q4k.gemm_config(5120, 17408, 256) >= 1
+
+
+def test_tuning_knobs_validate(lib):
+    assert lib.q4k_tune_gemv(3, 0) == -1
+    assert lib.q4k_tune_gemv(4, 65) == -1
+    assert lib.q4k_tune_gemm(-1) == -1
+    q4k.tune_gemv(8, 3)
+    assert q4k.gemv_config(17408, 5120) == (8, 2)   # capped so each wave keeps a block
+    q4k.tune_gemv(0, 0)
+    q4k.tune_gemm(0)
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the CPU reference and has no CPU fallback."""
+    pkg = os.path.join(ROOT, "bit_block_quantized_gguf_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text, f
+                assert "q4k_oracle" not in text, f
