@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X Q4_K matmul path; prints ONE JSON line.
+
+Headline (`value`): Q4_K GEMV HBM throughput of the batch-1 MLP block of
+Qwen3.6-27B — gate 17408x5120, up 17408x5120, down 5120x17408, each its own
+launch (the SwiGLU between them belongs to the caller and is computed once,
+outside the timed region).  One step = those three GEMVs on synthetic random
+Q4_K weights (d, dmin ~U(1e-4, 1e-3) in binary16, uniform scale/min bytes and
+nibbles) and an N(0,1) f32 activation.  Weights are COLD: each matrix is held
+in 4 distinct copies (12 x 50 MB = 601 MB in rotation, above the 256 MB
+Infinity Cache), so every launch streams its bytes from HBM.
+
+Also measured and reported in the same line:
+  * decode_stack: the full 64-layer per-token matmul chain (48 GDN-shaped +
+    16 attention-shaped layers, 64 MLP blocks, lm_head 248320x5120; 14.41 GB
+    of Q4_K) replayed as one hipGraph per token: us/token vs the weight-read
+    roofline 14,412,349,440 B / 8 TB/s;
+  * prefill_gemm: bf16-MFMA GEMM for both MLP shapes at P = 256, 512, 1024
+    (TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak);
+  * gemv_batch: N = 1, 2, 4, 8, 16 vectors on the 17408x5120 weight;
+  * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound);
+  * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
+    launch over its HIP-event duration, against 8 TB/s;
+  * cpu_baseline: the CPU oracle (double precision, all host cores) on the
+    same three GEMVs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+QK, BB = 256, 144
+METRIC = "Q4_K GEMV HBM GB/s (% peak); decode-stack µs/token; prefill GEMM TFLOP/s"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_mlp_17408x5120_traffic.json")
+GEMV_SOURCES = ["bit_block_quantized_gguf_amd/csrc/q4k_gemv.hip",
+                "bit_block_quantized_gguf_amd/csrc/q4k_device.hpp"]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def wbytes(M, K):
+    return M * (K // QK) * BB
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sections", default="gemv,batch,small,gemm,stack,cpu",
+                    help="comma list of gemv,batch,small,gemm,stack,cpu")
+    ap.add_argument("--copies", type=int, default=4, help="cold-rotation copies per MLP matrix")
+    ap.add_argument("--stack-tokens", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one "
+              "GPU); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    sections = set(s.strip() for s in args.sections.split(",") if s.strip())
+
+    import numpy as np
+    import torch
+
+    import bit_block_quantized_gguf_amd as q4k
+    import synth
+    from synth import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    q4k.load()
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    def upload(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded SplitMix64 Q4_K blocks, N(0,1) f32 activations)"}
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "cus": props.multi_processor_count}
+
+    # ------------------------------------------------------------ MLP GEMVs
+    M_in, K_in = wl.INTER, wl.HIDDEN
+    mlp_bytes = {name: wbytes(M, K) for name, M, K in wl.MLP}
+    step_bytes = sum(mlp_bytes.values())
+    x = synth.activations(2, 1, wl.HIDDEN)[0]
+    xd = upload(x)
+    if "gemv" in sections:
+        log("generating MLP weights (%d copies of each)" % args.copies)
+        copies = {}
+        for i, (name, M, K) in enumerate(wl.MLP):
+            hw = synth.q4k_weight(synth.key(2, i), M, K)
+            copies[name] = [upload(hw) for _ in range(args.copies)]
+        y_gate = torch.empty(M_in, device=dev)
+        y_up = torch.empty(M_in, device=dev)
+        y_down = torch.empty(wl.HIDDEN, device=dev)
+        q4k.gemv(copies["gate"][0], xd, y_gate)
+        q4k.gemv(copies["up"][0], xd, y_up)
+        a = (torch.nn.functional.silu(y_gate) * y_up).contiguous()   # caller's SwiGLU, untimed
+        torch.cuda.synchronize()
+
+        def step(i, evs=None):
+            c = i % args.copies
+            for j, (name, w, xin, y) in enumerate((("gate", copies["gate"][c], xd, y_gate),
+                                                   ("up", copies["up"][c], xd, y_up),
+                                                   ("down", copies["down"][c], a, y_down))):
+                if evs is not None:
+                    evs[j][0].record(stream)
+                q4k.gemv(w, xin, y)
+                if evs is not None:
+                    evs[j][1].record(stream)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        # wall-clock step timing (no per-kernel events inside)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        # per-launch HIP-event timing on the launch stream: all timed steps
+        # are enqueued back to back and the stream is synchronised once, so
+        # each event pair brackets one GEMV call (main kernel plus, for split
+        # tiles, its reduce kernel) as the GPU executed it
+        per = {n: [] for n in ("gate", "up", "down")}
+        all_evs = []
+        for i in range(args.steps):
+            evs = [(ev(), ev()) for _ in range(3)]
+            step(i, evs)
+            all_evs.append(evs)
+        torch.cuda.synchronize()
+        for evs in all_evs:
+            for j, n in enumerate(("gate", "up", "down")):
+                per[n].append(evs[j][0].elapsed_time(evs[j][1]) * 1e3)   # us
+        kern = {n: float(np.mean(v)) for n, v in per.items()}
+        kern_med = {n: float(np.median(v)) for n, v in per.items()}
+        gpu_us = sum(kern.values())
+        out["ms_per_step"] = wall * 1e3
+        out["value"] = step_bytes / wall / 1e9
+        out["unit"] = "GB/s"
+        out["config"] = {
+            "workload": "Qwen3.6-27B MLP block at batch 1: Q4_K GEMVs gate 17408x5120, "
+                        "up 17408x5120, down 5120x17408 (SwiGLU by the caller), cold weights",
+            "bytes_per_step": step_bytes, "copies_in_rotation": 3 * args.copies,
+            "launch_shape": {"17408x5120": q4k.gemv_config(17408, 5120),
+                             "5120x17408": q4k.gemv_config(5120, 17408)}}
+        out["gemv_mlp"] = {n: {"us_mean": kern[n], "us_median": kern_med[n],
+                               "GBps": mlp_bytes[n] / kern[n] / 1e3,
+                               "frac_hbm": mlp_bytes[n] / kern[n] / 1e3 / HBM_PEAK_GBS}
+                           for n in kern}
+        out["gemv_mlp"]["kernel_sum_us"] = gpu_us
+        achieved = mlp_bytes["gate"] / kern["gate"] / 1e3
+        traffic = None
+        if os.path.exists(PROFILE_TRAFFIC):
+            with open(PROFILE_TRAFFIC) as f:
+                tr = json.load(f)
+            if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+                traffic = tr.get("hbm_bytes_per_launch")
+        out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                           "kernel": "q4k_gemv on gate 17408x5120 (gemv_kernel<1,1,PLAIN> + gemv_reduce_kernel)",
+                           "algorithmic_bytes_per_launch": mlp_bytes["gate"] + 4 * (5120 + 17408)}
+        log("MLP GEMVs: step %.2f us wall, kernels %s" % (wall * 1e6, kern))
+        del copies
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ batched
+    if "batch" in sections:
+        M, K = wl.BATCH_SHAPE
+        hw = synth.q4k_weight(synth.key(4, 0), M, K)
+        ncop = 12
+        ws = [upload(hw) for _ in range(ncop)]
+        res = []
+        for N in wl.BATCH_N:
+            X = upload(synth.activations(4, N, K))
+            Y = torch.empty((N, M), device=dev)
+            for i in range(3):
+                q4k.gemv_batch(ws[i % ncop], X, Y)
+            torch.cuda.synchronize()
+            pairs = []
+            for i in range(max(10, args.steps)):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                q4k.gemv_batch(ws[i % ncop], X, Y)
+                e1.record(stream)
+                pairs.append((e0, e1))
+            torch.cuda.synchronize()
+            ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+            t = float(np.mean(ts))
+            roof_us = max(wbytes(M, K) / HBM_PEAK_GBS / 1e3, 2.0 * M * K * N / 157.3e12 * 1e6)
+            res.append({"N": N, "us": t, "us_per_vector": t / N,
+                        "effective_GBps": N * wbytes(M, K) / t / 1e3,
+                        "weight_GBps": wbytes(M, K) / t / 1e3,
+                        "roofline_us": roof_us, "frac_roofline": roof_us / t})
+        out["gemv_batch"] = res
+        log("batched: %s" % [(r["N"], round(r["us"], 2)) for r in res])
+        del ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ small GEMVs
+    if "small" in sections:
+        res = []
+        for (M, K) in wl.SINGLE:
+            hw = synth.q4k_weight(synth.key(1, 0), M, K)
+            wd = upload(hw)
+            xs = upload(synth.activations(1, 1, K)[0])
+            y = torch.empty(M, device=dev)
+            for _ in range(5):
+                q4k.gemv(wd, xs, y)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(50):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                q4k.gemv(wd, xs, y)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            res.append({"M": M, "K": K, "us_median": float(np.median(ts)), "bytes": wbytes(M, K)})
+        out["gemv_small"] = res
+
+    # ------------------------------------------------------------ prefill GEMM
+    if "gemm" in sections:
+        res = []
+        for si, (M, K) in enumerate(wl.PREFILL_SHAPES):
+            wd = upload(synth.q4k_weight(synth.key(5, si), M, K))
+            for P in wl.PREFILL_P:
+                X = upload(synth.activations(5, P, K))
+                Y = torch.empty((P, M), device=dev)
+                for _ in range(3):
+                    q4k.gemm(wd, X, Y)
+                torch.cuda.synchronize()
+                pairs = []
+                for _ in range(max(10, args.steps // 2)):
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                    q4k.gemm(wd, X, Y)
+                    e1.record(stream)
+                    pairs.append((e0, e1))
+                torch.cuda.synchronize()
+                ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+                t = float(np.mean(ts))
+                tf = 2.0 * M * K * P / t / 1e6
+                res.append({"M": M, "K": K, "P": P, "us": t, "TFLOPs": tf,
+                            "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "k_splits": q4k.gemm_config(M, K, P)})
+                del X, Y
+        out["prefill_gemm"] = res
+        log("gemm: %s" % [(r["M"], r["P"], round(r["TFLOPs"], 1)) for r in res])
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode stack
+    if "stack" in sections:
+        L = wl.N_LAYERS
+        log("generating the %d-layer stack (%.2f GB)" % (L, wl.stack_bytes() / 1e9))
+        buf = None
+        layers = []
+        for l in range(L):
+            d = {}
+            for name, (M, K) in wl.layer_shapes(l).items():
+                n = wbytes(M, K)
+                if buf is None or buf.size < n:
+                    buf = np.empty(wbytes(wl.VOCAB, wl.HIDDEN), np.uint8)
+                hw = synth.q4k_weight(wl.stack_tensor_key(l, name), M, K,
+                                      out=buf[:n].reshape(M, -1))
+                d[name] = upload(hw)
+            layers.append(d)
+        n = wbytes(wl.VOCAB, wl.HIDDEN)
+        lm = upload(synth.q4k_weight(wl.stack_tensor_key(None, "lm_head"), wl.VOCAB, wl.HIDDEN,
+                                     out=buf[:n].reshape(wl.VOCAB, -1)))
+        del buf
+        log("capturing the decode graph")
+        stk = q4k.DecodeStack(layers, lm, hidden=wl.HIDDEN,
+                              kinds=[1 if wl.is_attention(l) else 0 for l in range(L)])
+        h0 = upload(synth.activations(3, 1, wl.HIDDEN)[0])
+        logits = torch.empty(wl.VOCAB, device=dev)
+        for _ in range(3):
+            stk(h0, logits)
+        torch.cuda.synchronize()
+        pairs = []
+        t0 = time.perf_counter()
+        for _ in range(args.stack_tokens):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            stk(h0, logits)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        wall_tok = (time.perf_counter() - t0) / args.stack_tokens * 1e6
+        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        tot = wl.stack_bytes()
+        roof = tot / HBM_PEAK_GBS / 1e3
+        med = float(np.median(ts))
+        out["decode_stack"] = {"us_per_token_median": med, "us_per_token_mean": float(np.mean(ts)),
+                               "us_per_token_wall": wall_tok, "tokens": args.stack_tokens,
+                               "weight_bytes": tot, "roofline_us": roof, "frac_roofline": roof / med,
+                               "GBps": tot / med / 1e3, "graph_nodes": stk.nodes()}
+        log("stack: %.1f us/token (roofline %.1f)" % (med, roof))
+        stk.close()
+        del layers, lm
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
+    if "cpu" in sections:
+        import oracle
+        oracle.set_threads(os.cpu_count() or 1)
+        ws = [synth.q4k_weight(synth.key(2, i), M, K) for i, (_, M, K) in enumerate(wl.MLP)]
+        a_h = synth.activations(2, 1, wl.INTER, first=1)[0]
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            for wh, (_, M, K) in zip(ws, wl.MLP):
+                oracle.gemv(wh, x if K == wl.HIDDEN else a_h, M, K)
+            reps += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": reps * step_bytes / dt / 1e9, "unit": "GB/s",
+                               "cores": oracle.get_threads(), "kind": "oracle",
+                               "sample": "%d repeats of the three full MLP GEMVs (gate, up, down; "
+                                         "%.2f s), double-precision oracle, rows over all threads"
+                                         % (reps, dt)}
+    if "value" not in out:
+        out["value"] = None
+        out["unit"] = "GB/s"
+        out["ms_per_step"] = None
+        out["config"] = {"workload": "sections: " + ",".join(sorted(sections))}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

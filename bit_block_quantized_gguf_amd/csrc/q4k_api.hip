@@ -256,13 +256,13 @@ void q4k_release_workspaces(void) {
 /* Benchmark knobs: force the GEMV waves-per-group / K splits and the GEMM K
  * splits (0 restores the shape heuristics).  Not thread-safe with respect to
  * concurrent calls; meant for sweeps. */
-int q4k_tune_gemv(int32_t waves_per_group, int32_t k_splits) {
+int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
     clear_error();
-    if (waves_per_group != 0 && waves_per_group != 2 && waves_per_group != 4 &&
-        waves_per_group != 8)
-        return fail(Q4K_EINVAL, "waves_per_group must be 0, 2, 4 or 8");
-    if (k_splits < 0 || k_splits > 64) return fail(Q4K_EINVAL, "k_splits must be in 0..64");
-    set_gemv_override(waves_per_group, k_splits);
+    if (waves_per_group != 0 && waves_per_group != 4)
+        return fail(Q4K_EINVAL, "waves_per_group must be 0 or 4");
+    if (workgroups < 0 || workgroups > (1 << 20))
+        return fail(Q4K_EINVAL, "workgroups must be in 0..2^20");
+    set_gemv_override(workgroups);
     return Q4K_OK;
 }
 
@@ -275,15 +275,15 @@ int q4k_tune_gemm(int32_t k_splits) {
 
 /* Launch configuration the heuristics pick for a shape (for reports). */
 int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
-                    int32_t *k_splits) {
+                    int32_t *workgroups) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
-    if (!waves_per_group || !k_splits) return fail(Q4K_EINVAL, "NULL output");
+    if (!waves_per_group || !workgroups) return fail(Q4K_EINVAL, "NULL output");
     int nv = 16;
     while (nv > 1 && nv > N) nv >>= 1;
     const GemvLaunch L = choose_gemv_launch(M, K, nv, 1);
     *waves_per_group = L.wk;
-    *k_splits = L.ks;
+    *workgroups = L.ks;
     return Q4K_OK;
 }
 

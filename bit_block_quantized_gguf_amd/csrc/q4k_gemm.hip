@@ -25,9 +25,10 @@
 //   * Output layout of the 32x32 MFMA: lane l holds column l%32 (a W row)
 //     and rows 8(v/4) + 4(l/32) + v%4 (tokens) of accumulator v, so each
 //     store instruction writes 32 consecutive floats of a token row.
-//   * For short M the K range is split across workgroups; the last-arriving
-//     workgroup of a tile adds the partials in split order (deterministic)
-//     and resets the tile's counter.
+//   * For short M the K range is split across workgroups: each split writes
+//     its partial tile to a workspace and a second kernel adds the splits in
+//     order (deterministic; no cross-workgroup synchronisation inside a
+//     kernel).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -55,7 +56,6 @@ struct GemmParams {
     int32_t ks;
     int32_t row_tiles;
     float *ws;
-    unsigned *cnt;
 };
 
 __device__ __forceinline__ bf16x8 dequant8(uint32_t q0, uint32_t q1, float ds, float dm) {
@@ -156,43 +156,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmParams p) {
     // ---- epilogue ----
     const int col = row0 + 32 * wave + (lane & 31);   // W row = Y column
     const bool col_ok = col < p.M;
-    if (p.ks > 1) {
-        const int tile = tt * p.row_tiles + rt;
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tok = tok0 + 32 * ti + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (col_ok && tok < p.P)
-                    p.ws[((int64_t)split * p.P + tok) * p.M + col] = acc[ti][v];
-            }
-        __threadfence();
-        __syncthreads();
-        __shared__ unsigned last;
-        if (tid == 0) last = atomicAdd(&p.cnt[tile], 1u) == (unsigned)(p.ks - 1);
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tok = tok0 + 32 * ti + 8 * (v >> 2) + 4 * h + (v & 3);
-                float s = 0.f;
-                if (col_ok && tok < p.P)
-                    for (int sp = 0; sp < p.ks; ++sp)
-                        s += p.ws[((int64_t)sp * p.P + tok) * p.M + col];
-                acc[ti][v] = s;
-            }
-        if (tid == 0) p.cnt[tile] = 0u;
-    }
+    // K split across workgroups: this split's partial tile goes to the
+    // workspace; a second kernel adds the splits in order.
+    float *out = p.ks > 1 ? p.ws + (int64_t)split * p.P * p.M : p.Y;
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int tok = tok0 + 32 * ti + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (col_ok && tok < p.P) p.Y[(int64_t)tok * p.M + col] = acc[ti][v];
+            if (col_ok && tok < p.P) out[(int64_t)tok * p.M + col] = acc[ti][v];
         }
+}
+
+// Y[i] = sum over splits of ws[s][i], in split order (one element per thread).
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ ws,
+                                                          float *__restrict__ Y, int64_t n,
+                                                          int ks) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float t = ws[i];
+    for (int s = 1; s < ks; ++s) t += ws[(int64_t)s * n + i];
+    Y[i] = t;
 }
 
 std::atomic<int> g_override_ks{0};
@@ -220,7 +204,9 @@ size_t gemm_partial_floats(const GemmLaunch &L, int64_t M, int64_t P) {
 }
 
 size_t gemm_counters(int64_t M, int64_t P) {
-    return (size_t)(((M + BM - 1) / BM) * ((P + BN - 1) / BN));
+    (void)M;
+    (void)P;
+    return 0;
 }
 
 int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
@@ -237,12 +223,19 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     p.ks = L.ks;
     p.row_tiles = (int32_t)((M + BM - 1) / BM);
     p.ws = ws.partials;
-    p.cnt = ws.counters;
     const dim3 grid((unsigned)p.row_tiles, (unsigned)((P + BN - 1) / BN), (unsigned)L.ks);
     if (grid.y > 65535 || grid.z > 65535)
         return fail(Q4K_EUNSUPPORTED, "gemm: P or split count too large");
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, stream, p);
     Q4K_HIP(hipGetLastError());
+    if (L.ks > 1) {
+        const int64_t n = P * M;
+        const int64_t groups = (n + 255) / 256;
+        if (groups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: output too large");
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)groups), dim3(256), 0, stream,
+                           (const float *)ws.partials, Y, n, L.ks);
+        Q4K_HIP(hipGetLastError());
+    }
     return Q4K_OK;
 }
 

@@ -3,35 +3,57 @@
 //
 // The decode matmul is bandwidth-bound ("Mac Qwen3.6-27B Metal Q4_K perf
 // diagnosis", §2-§4): every weight byte is read once and the job is to stream
-// them at HBM speed.  Mapping on the CDNA4 execution model:
+// the bytes at HBM speed while spending as few vector instructions per weight
+// as possible.  Mapping on the CDNA4 execution model:
 //
-//  * A wave owns 64 consecutive rows, one row per lane, and walks a range of
-//    super-block columns.  All lanes of a wave therefore need the same 256
-//    activations at the same time: those are fetched with scalar loads (the
-//    activation pointer is in the constant address space) and enter every
-//    FMA as an SGPR operand — no vector-memory traffic and no LDS for x.
-//  * Each lane streams its row's 144-byte block as nine 16-byte loads; the
-//    next block's loads are issued before the current block is computed.
+//  * Work unit = 64 "lane rows" x 4 consecutive super-blocks (64 rows of one
+//    matrix, or 32 rows of gate plus the same 32 rows of up for the fused
+//    SwiGLU).  A workgroup of 4 waves copies the unit's 64 row segments of
+//    576 bytes into LDS with 16-byte loads in address order, so each wave
+//    instruction reads contiguous bytes and every row contributes one 576-byte
+//    run (144-byte runs measured ~30% slower on HBM).  LDS rows are padded to
+//    592 bytes, which makes the row-strided reads below conflict-free.
+//  * Wave w then computes block w of the unit for all 64 lane rows, one row
+//    per lane.  All lanes need the same 256 activations at the same time:
+//    they arrive by scalar loads (constant address space) and enter every FMA
+//    as an SGPR operand.  The wave index goes through readfirstlane so the
+//    compiler can prove those addresses wave-uniform.
 //  * Per weight the VALU work is one byte-to-float conversion and one FMA
-//    (plus one AND per four weights); the scale/min algebra is applied once
-//    per 32-weight sub-block:  y += d*sc * sum(q*x) - dmin*m * sum(x).
-//    High nibbles are converted in place (16*q) and their scale carries the
-//    exact factor 1/16.  The per-sub-block sums of x are formed once per
-//    block by the wave (one 16-byte load per lane, a 3-step butterfly).
-//  * K is split across the waves of a workgroup (reduced through LDS in a
-//    fixed order) and, for short M, across workgroups: partials go to a
-//    workspace and the last-arriving workgroup of a row tile (per-tile
-//    atomic counter) adds them in split order, so results are deterministic.
-//    The counter is returned to zero by that workgroup.
+//    (plus one AND per four weights).  Per block the scale/min algebra is
+//       y += d * sum_j sc_j * T_j  -  dmin * sum_j m_j * X_j
+//    with T_j = sum(q*x) and X_j = sum(x) over sub-block j; high nibbles are
+//    converted in place (16*q) and their partial sum carries the exact factor
+//    1/16.  X_j comes from one 16-byte load per lane and a 3-step butterfly.
+//  * The loads of unit u+1 are issued into registers before unit u is
+//    computed (the activation-sum load goes first, so the in-order vmcnt wait
+//    for it does not drain the prefetch), then copied to LDS between two
+//    workgroup barriers.
+//  * Launch: exactly as many workgroups as fit on the device at once; each
+//    takes a contiguous range of units in (row tile, K) order, accumulating a
+//    row tile's blocks in registers.  A tile whose units all fall in one
+//    workgroup is finished there (four waves added in LDS in wave order, then
+//    the epilogue).  A tile split between workgroups leaves one partial per
+//    workgroup, and a second kernel adds them in workgroup order and applies
+//    the epilogue.  Results are deterministic and no cross-workgroup fence is
+//    needed inside a kernel.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
 #include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace q4k {
 
 namespace {
+
+constexpr int WK = 4;                    // waves per workgroup = blocks per unit
+constexpr int SEG = WK * kBlockBytes;    // 576 bytes of a row per unit
+constexpr int SEGP = SEG + 16;           // padded LDS row stride
+constexpr int CH_ROW = SEG / 16;         // 36 16-byte chunks per row segment
+constexpr int CH_THREAD = 9;             // 64 * 36 / 256 chunks per thread per unit
 
 __device__ __forceinline__ float wave_sum(float v) {
     // xor butterfly: partners add the same two values, so every lane ends
@@ -45,280 +67,405 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// acc[n] += sum over the block of w * x_n (factored form).
 template <int NV>
-__device__ __forceinline__ void sub_block_sums(const float *x, int64_t xs, int j, int lane,
-                                               float (&xsum)[NV][8]) {
+__device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk, int64_t xs,
+                                          const float4 (&xq)[NV], float (&acc)[NV]) {
+    const float d = half_lo(b[0].x);
+    const float dmin = half_hi(b[0].x);
+    const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
+    float A_lo[NV], A_hi[NV], B[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) A_lo[n] = A_hi[n] = B[n] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float tl[NV], th[NV];
+#pragma unroll
+        for (int n = 0; n < NV; ++n) tl[n] = th[n] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+            const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float q = ubyte(lo, bb);
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+                    tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+            const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const float q = ubyte(hi, bb);
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+                    th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
+            }
+        }
+        const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            A_lo[n] = fmaf(sl, tl[n], A_lo[n]);
+            A_hi[n] = fmaf(sh, th[n], A_hi[n]);
+        }
+    }
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
-        const float4 v = *reinterpret_cast<const float4 *>(x + n * xs + 256 * j + 4 * lane);
-        float s = (v.x + v.y) + (v.z + v.w);
+        // per-sub-block sums of x: lanes 8s..8s+7 hold sub-block s's 32 values
+        float s = (xq[n].x + xq[n].y) + (xq[n].z + xq[n].w);
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb)
-            xsum[n][sb] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb));
+            B[n] = fmaf(min_of(sc, sb),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
+        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f, A_lo[n]), -dmin * B[n]);
     }
 }
 
-template <int NMAT>
-__device__ __forceinline__ void load_blocks(const uint8_t *const (&rp)[NMAT], int j,
-                                            uint4 (&b)[NMAT][9]) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        const uint8_t *p = rp[m] + (int64_t)j * kBlockBytes;
-#pragma unroll
-        for (int i = 0; i < 9; ++i) b[m][i] = ldg16(p + 16 * i);
-    }
+// Inverse RMS of an input vector from its per-32-element sums of squares.
+__device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
+    float ss = 0.f;
+    for (int i = lane; i < p.in_sq_n; i += 64) ss += p.in_sq[i];
+    ss = wave_sum(ss);
+    return 1.0f / sqrtf(ss / (float)p.in_len + p.eps);
 }
 
-// acc[n] += sum over the block of w * x_n (factored per sub-block).
-template <int NV>
-__device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk, int64_t xs,
-                                          const float (&xsum)[NV][8], float (&acc)[NV]) {
-    constexpr int C = NV >= 4 ? 1 : (NV == 2 ? 2 : 4);  // independent FMA chains per sum
-    const float d = half_lo(b[0].x);
-    const float dmin = half_hi(b[0].x);
-    const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        float tl[NV][C], th[NV][C];
-#pragma unroll
-        for (int n = 0; n < NV; ++n)
-#pragma unroll
-            for (int c = 0; c < C; ++c) tl[n][c] = th[n][c] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-            const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
-            const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const float ql = ubyte(lo, bb);
-                const float qh = ubyte(hi, bb);
-#pragma unroll
-                for (int n = 0; n < NV; ++n) {
-                    cfloat *xp = as_const(xblk + n * xs + 64 * g);
-                    tl[n][bb % C] = fmaf(ql, xp[4 * i + bb], tl[n][bb % C]);
-                    th[n][bb % C] = fmaf(qh, xp[32 + 4 * i + bb], th[n][bb % C]);
-                }
-            }
-        }
-        const float dl = d * scale_of(sc, 2 * g);
-        const float dh = d * scale_of(sc, 2 * g + 1) * 0.0625f;  // exact: undoes the 16*q
-        const float ml = dmin * min_of(sc, 2 * g);
-        const float mh = dmin * min_of(sc, 2 * g + 1);
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            float tls = tl[n][0], ths = th[n][0];
-#pragma unroll
-            for (int c = 1; c < C; ++c) {
-                tls += tl[n][c];
-                ths += th[n][c];
-            }
-            float a = acc[n];
-            a = fmaf(dl, tls, a);
-            a = fmaf(-ml, xsum[n][2 * g], a);
-            a = fmaf(dh, ths, a);
-            a = fmaf(-mh, xsum[n][2 * g + 1], a);
-            acc[n] = a;
-        }
-    }
-}
-
-template <int NV, int NMAT, int EPI, int WK>
-__global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p) {
-    constexpr int NA = NMAT * NV;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x;
-    const int split = blockIdx.y;
-    const int row = tile * 64 + lane;
-    const int rowc = row < p.M ? row : p.M - 1;
-    const int nchunks = p.ks * WK;
-    const int chunk = split * WK + wave;
-    const int jb = (int)(((int64_t)chunk * p.nb) / nchunks);
-    const int je = (int)(((int64_t)(chunk + 1) * p.nb) / nchunks);
-
-    const uint8_t *rp[NMAT];
-    rp[0] = p.w0 + (int64_t)rowc * p.row_bytes;
-    if constexpr (NMAT == 2) rp[1] = p.w1 + (int64_t)rowc * p.row_bytes;
-
-    float acc[NMAT][NV];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int n = 0; n < NV; ++n) acc[m][n] = 0.f;
-
-    uint4 cur[NMAT][9];
-    if (jb < je) load_blocks<NMAT>(rp, jb, cur);
-    for (int j = jb; j < je; ++j) {
-        uint4 nxt[NMAT][9];
-        const bool more = j + 1 < je;
-        if (more) load_blocks<NMAT>(rp, j + 1, nxt);
-        float xsum[NV][8];
-        sub_block_sums<NV>(p.x, p.x_stride, j, lane, xsum);
-        const float *xblk = p.x + 256 * (int64_t)j;
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) block_dot<NV>(cur[m], xblk, p.x_stride, xsum, acc[m]);
-        if (more) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                for (int i = 0; i < 9; ++i) cur[m][i] = nxt[m][i];
-        }
-    }
-
-    // ---- reduce the WK waves of the group (fixed order) ----
-    float tot[NA];
-    if constexpr (WK > 1) {
-        __shared__ float red[WK][NA][64];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int n = 0; n < NV; ++n) red[wave][m * NV + n][lane] = acc[m][n];
-        __syncthreads();
-        if (wave != 0) return;
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            float s = red[0][a][lane];
-#pragma unroll
-            for (int w = 1; w < WK; ++w) s += red[w][a][lane];
-            tot[a] = s;
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int n = 0; n < NV; ++n) tot[m * NV + n] = acc[m][n];
-    }
-
-    // ---- reduce the K splits across workgroups: last arriver, split order ----
-    if (p.ks > 1) {
-        if (row < p.M) {
-#pragma unroll
-            for (int a = 0; a < NA; ++a) p.ws[((int64_t)split * NA + a) * p.M + row] = tot[a];
-        }
-        __threadfence();
-        unsigned prev = 0;
-        if (lane == 0) prev = atomicAdd(&p.cnt[tile], 1u);
-        prev = __shfl(prev, 0);
-        if (prev != (unsigned)(p.ks - 1)) return;
-        __threadfence();
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            float s = 0.f;
-            if (row < p.M)
-                for (int sp = 0; sp < p.ks; ++sp) s += p.ws[((int64_t)sp * NA + a) * p.M + row];
-            tot[a] = s;
-        }
-        if (lane == 0) p.cnt[tile] = 0u;
-    }
-
-    // ---- epilogue (one lane per row) ----
+// Epilogue for one wave holding the final sums of a tile's 64 lane rows.
+// NMAT == 1: lane = output row (row0 + lane).  NMAT == 2: lanes 0..31 hold the
+// gate rows row0 + lane, lanes 32..63 the up rows of the same indices.
+template <int NV, int NMAT, int EPI>
+__device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane,
+                                         const float (&tot)[NV]) {
     if constexpr (EPI == EPI_PLAIN) {
+        const int row = row0 + lane;
         if (row < p.M) {
 #pragma unroll
             for (int n = 0; n < NV; ++n) p.y[(int64_t)n * p.y_stride + row] = tot[n];
         }
     } else {
-        float ss = 0.f;
-        for (int i = lane; i < p.in_sq_n; i += 64) ss += p.in_sq[i];
-        ss = wave_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)p.in_len + p.eps);
+        const float inv = inv_rms(p, lane);
         float val;
-        if constexpr (EPI == EPI_SCALE) {
-            val = tot[0] * inv;
-        } else if constexpr (EPI == EPI_RESID) {
-            val = fmaf(tot[0], inv, p.resid[rowc]);
-        } else {
-            const float g = tot[0] * inv;
-            const float v = tot[NV] * inv;
-            if (row < p.M) {
+        int row;
+        bool ok;
+        if constexpr (EPI == EPI_SWIGLU) {
+            const float mine = tot[0] * inv;
+            const float other = __shfl(mine, (lane + 32) & 63);
+            row = row0 + (lane & 31);
+            ok = lane < 32 && row < p.M;
+            const float g = mine, v = other;
+            val = g / (1.0f + expf(-g)) * v;
+            if (ok) {
                 p.y_g[row] = g;
                 p.y_v[row] = v;
             }
-            val = g / (1.0f + expf(-g)) * v;
+        } else {
+            row = row0 + lane;
+            ok = row < p.M;
+            const int rowc = ok ? row : p.M - 1;
+            if constexpr (EPI == EPI_SCALE) val = tot[0] * inv;
+            else val = fmaf(tot[0], inv, p.resid[rowc]);
         }
-        if (row < p.M) p.y[row] = val;
-        const float sq = wave_sum(row < p.M ? val * val : 0.f);
-        if (lane == 0) p.out_sq[tile] = sq;
+        if (ok) p.y[row] = val;
+        // sums of squares per 32 output rows (lanes 0..31 and 32..63)
+        float sq = ok ? val * val : 0.f;
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 8);
+        sq += __shfl_xor(sq, 4);
+        sq += __shfl_xor(sq, 2);
+        sq += __shfl_xor(sq, 1);
+        if ((lane & 31) == 0) {
+            const int granule = row0 / 32 + (lane >> 5);
+            if ((NMAT == 1 || lane == 0) && granule * 32 < p.M) p.out_sq[granule] = sq;
+        }
     }
+}
+
+// Unit bookkeeping shared by the main and the reduce kernel.
+struct Units {
+    int upt;      // units per row tile = ceil(nb / 4)
+    int64_t U;    // total units = tiles * upt
+    int G;        // workgroups in the main grid
+    __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
+    // workgroup whose range contains unit u
+    __device__ __forceinline__ int owner(int64_t u) const {
+        return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
+    }
+};
+
+template <int NV, int NMAT, int EPI>
+__global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const Units un) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * SEGP];
+    __shared__ float red[WK][NV][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int ROWS = 64 / NMAT;  // output rows per tile
+    const int g = blockIdx.x;
+    const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = (int)(ua / un.upt);
+
+    // this thread's copy chunks of a full unit: lane row r = q / 36, chunk c = q % 36
+    int coff[CH_THREAD];  // byte offset inside the row's 576-byte segment
+    int crow[CH_THREAD];  // lane row
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;
+        crow[i] = q / CH_ROW;
+        coff[i] = 16 * (q - crow[i] * CH_ROW);
+    }
+    uint4 reg[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    // Loads of unit u: a uniform tile base (SGPRs) plus a 32-bit lane offset;
+    // rows past M are clamped to the last row (their results are not stored).
+    auto fetch = [&](int64_t u) {
+        const int t = (int)(u / un.upt);
+        const int j0 = (int)(u - (int64_t)t * un.upt) * WK;
+        const int valid = min(WK, p.nb - j0) * kBlockBytes;  // bytes per row segment
+        const int rmax = min(ROWS - 1, p.M - 1 - t * ROWS);
+        const int64_t base = (int64_t)t * ROWS * p.row_bytes + (int64_t)j0 * kBlockBytes;
+        const uint8_t *b0 = p.w0 + base;
+        const uint8_t *b1 = NMAT == 2 ? p.w1 + base : b0;
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i) {
+            const int r = NMAT == 2 ? (crow[i] & 31) : crow[i];
+            const uint32_t off =
+                (uint32_t)min(r, rmax) * (uint32_t)p.row_bytes + (uint32_t)coff[i];
+            const uint8_t *src = (NMAT == 2 && crow[i] >= 32) ? b1 : b0;
+            if (coff[i] < valid) reg[i] = ldg16(src + off);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i)
+            *reinterpret_cast<uint4 *>(&stage[crow[i] * SEGP + coff[i]]) = reg[i];
+    };
+
+    float acc[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) acc[n] = 0.f;
+
+    fetch(ua);
+    commit();
+    __syncthreads();
+    int64_t seg0 = ua;
+    for (int64_t u = ua; u < ub; ++u) {
+        const int t = (int)(u / un.upt);
+        const int j = (int)(u - (int64_t)t * un.upt) * WK + wave;  // this wave's block
+        const bool active = j < p.nb;
+        // activation sums for this block first, then the next unit's loads
+        float4 xq[NV];
+        if (active) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n)
+                xq[n] = *reinterpret_cast<const float4 *>(p.x + n * p.x_stride + 256 * (int64_t)j +
+                                                          4 * lane);
+        }
+        const bool more = u + 1 < ub;
+        if (more) fetch(u + 1);
+        if (active) {
+            const uint8_t *lp = &stage[lane * SEGP + wave * kBlockBytes];
+            uint4 b[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) b[i] = *reinterpret_cast<const uint4 *>(lp + 16 * i);
+            block_dot<NV>(b, p.x + 256 * (int64_t)j, p.x_stride, xq, acc);
+        }
+        const bool seg_end = !more || (u + 1) / un.upt != t;
+        if (seg_end) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                red[wave][n][lane] = acc[n];
+                acc[n] = 0.f;
+            }
+        }
+        __syncthreads();
+        if (seg_end && wave == 0) {
+            float tot[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                float s = red[0][n][lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) s += red[w][n][lane];
+                tot[n] = s;
+            }
+            const bool whole = seg0 == (int64_t)t * un.upt && u + 1 == (int64_t)(t + 1) * un.upt;
+            if (whole) {
+                epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot);
+            } else {
+                const int slot = t == first_tile ? 0 : 1;
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+                    p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane] = tot[n];
+            }
+        }
+        if (seg_end) seg0 = u + 1;
+        if (more) commit();
+        __syncthreads();
+    }
+}
+
+// Adds the partials of tiles split between workgroups (workgroup order) and
+// applies the epilogue.  Tiles finished by one workgroup are skipped.
+template <int NV, int NMAT, int EPI>
+__global__ __launch_bounds__(64) void gemv_reduce_kernel(const GemvParams p, const Units un) {
+    const int lane = threadIdx.x;
+    constexpr int ROWS = 64 / NMAT;
+    const int t = blockIdx.x;
+    const int gf = un.owner((int64_t)t * un.upt);
+    const int gl = un.owner((int64_t)(t + 1) * un.upt - 1);
+    if (gf == gl) return;
+    float tot[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) tot[n] = 0.f;
+    for (int g = gf; g <= gl; ++g) {
+        const int ft = (int)(un.begin(g) / un.upt);
+        const int slot = t == ft ? 0 : 1;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) tot[n] += p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane];
+    }
+    epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot);
 }
 
 __global__ __launch_bounds__(64) void sumsq_kernel(const float *__restrict__ v, int64_t n,
                                                    float *__restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
     const float a = i < n ? v[i] : 0.f;
-    const float s = wave_sum(a * a);
-    if (threadIdx.x == 0) out[blockIdx.x] = s;
+    float s = a * a;
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    const int64_t granule = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 5);
+    if ((threadIdx.x & 31) == 0 && granule * 32 < n) out[granule] = s;
 }
 
-std::atomic<int> g_override_wk{0};
-std::atomic<int> g_override_ks{0};
+std::atomic<int> g_override_groups{0};
+
+// Resident workgroups of each kernel instance on a device (occupancy queries
+// are not free, so they are cached).
+std::mutex g_occ_mutex;
+std::map<std::pair<int, const void *>, int> g_occ;
+
+int resident_groups(const void *fn, int *out) {
+    int dev = 0;
+    Q4K_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(g_occ_mutex);
+    auto key = std::make_pair(dev, fn);
+    auto it = g_occ.find(key);
+    if (it == g_occ.end()) {
+        int per_cu = 0, cus = 0;
+        Q4K_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * WK, 0));
+        Q4K_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        it = g_occ.emplace(key, std::max(1, per_cu) * std::max(1, cus)).first;
+    }
+    *out = it->second;
+    return Q4K_OK;
+}
+
+int64_t units_of(int64_t M, int64_t K, int nmat) {
+    const int64_t rows = 64 / nmat;
+    return ((M + rows - 1) / rows) * ((K / 256 + WK - 1) / WK);
+}
 
 template <int NV, int NMAT, int EPI>
-int launch_wk(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
-    const dim3 grid((unsigned)((p.M + 63) / 64), (unsigned)L.ks);
-    switch (L.wk) {
-        case 2: hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI, 2>), grid, dim3(128), 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI, 4>), grid, dim3(256), 0, stream, p); break;
-        case 8: hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI, 8>), grid, dim3(512), 0, stream, p); break;
-        default: return fail(Q4K_EINVAL, "unsupported waves-per-group %d", L.wk);
+int groups_for(int64_t M, int64_t K, int *G) {
+    int res = 0;
+    const int o = g_override_groups.load();
+    if (o <= 0) {
+        int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res);
+        if (rc) return rc;
     }
+    const int64_t g = o > 0 ? (int64_t)o : (int64_t)res;
+    *G = (int)std::max<int64_t>(1, std::min<int64_t>(g, units_of(M, K, NMAT)));
+    return Q4K_OK;
+}
+
+template <int NV, int NMAT, int EPI>
+int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
+    constexpr int ROWS = 64 / NMAT;
+    const int64_t tiles = (p.M + ROWS - 1) / ROWS;
+    Units un;
+    un.upt = (p.nb + WK - 1) / WK;
+    un.U = tiles * un.upt;
+    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
+    if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
+    hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
+                       stream, p, un);
     Q4K_HIP(hipGetLastError());
+    // Every workgroup range starts on a tile boundary only when each tile is
+    // one unit, or when the tiles divide evenly among the workgroups.
+    const bool split = un.upt > 1 && (un.G > tiles || tiles % un.G != 0);
+    if (split) {
+        hipLaunchKernelGGL((gemv_reduce_kernel<NV, NMAT, EPI>), dim3((unsigned)tiles), dim3(64), 0,
+                           stream, p, un);
+        Q4K_HIP(hipGetLastError());
+    }
     return Q4K_OK;
 }
 
 }  // namespace
 
-void set_gemv_override(int wk, int ks) {
-    g_override_wk = wk;
-    g_override_ks = ks;
-}
+void set_gemv_override(int groups) { g_override_groups = groups; }
 
-GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat) {
-    (void)nv;
-    (void)nmat;
-    const int64_t tiles = (M + 63) / 64;
-    const int64_t nb = K / 256;
+GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat, int epi) {
     GemvLaunch L;
-    L.wk = 4;
-    // Aim for ~8 waves per CU across 256 CUs so that enough 16-byte loads are
-    // in flight to cover HBM latency; keep at least one block per wave.
-    const double target_waves = 2048.0;
-    int64_t ks = (int64_t)(target_waves / (double)(tiles * L.wk) + 0.5);
-    ks = std::max<int64_t>(1, std::min<int64_t>(ks, std::max<int64_t>(1, nb / L.wk)));
-    L.ks = (int)std::min<int64_t>(ks, 64);
-    const int owk = g_override_wk.load(), oks = g_override_ks.load();
-    if (owk > 0) L.wk = owk;
-    if (oks > 0) L.ks = (int)std::min<int64_t>(oks, std::max<int64_t>(1, nb));
-    if ((int64_t)L.ks * L.wk > nb) L.ks = (int)std::max<int64_t>(1, nb / L.wk);
+    L.wk = WK;
+    int G = 0;
+    int rc;
+    if (nmat == 2) rc = groups_for<1, 2, EPI_SWIGLU>(M, K, &G);
+    else if (epi == EPI_SCALE) rc = groups_for<1, 1, EPI_SCALE>(M, K, &G);
+    else if (epi == EPI_RESID) rc = groups_for<1, 1, EPI_RESID>(M, K, &G);
+    else if (nv >= 16) rc = groups_for<16, 1, EPI_PLAIN>(M, K, &G);
+    else if (nv >= 8) rc = groups_for<8, 1, EPI_PLAIN>(M, K, &G);
+    else if (nv >= 4) rc = groups_for<4, 1, EPI_PLAIN>(M, K, &G);
+    else if (nv >= 2) rc = groups_for<2, 1, EPI_PLAIN>(M, K, &G);
+    else rc = groups_for<1, 1, EPI_PLAIN>(M, K, &G);
+    if (rc != Q4K_OK || G < 1) {
+        // no device to query (e.g. host-only callers): assume 4 workgroups per CU, 256 CUs
+        clear_error();
+        const int o = g_override_groups.load();
+        G = (int)std::max<int64_t>(1, std::min<int64_t>(o > 0 ? o : 1024, units_of(M, K, nmat)));
+    }
+    L.ks = G;
     return L;
 }
 
 size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat) {
-    return L.ks > 1 ? (size_t)L.ks * (size_t)nmat * (size_t)nv * (size_t)M : 0;
+    (void)M;
+    (void)nmat;
+    return (size_t)L.ks * 2 * (size_t)nv * 64;
 }
 
-size_t gemv_counters(int64_t M) { return (size_t)((M + 63) / 64); }
+size_t gemv_counters(int64_t M) {
+    (void)M;
+    return 0;
+}
 
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,
                 hipStream_t stream) {
     if (nmat == 1 && epi == EPI_PLAIN) {
         switch (nv) {
-            case 1: return launch_wk<1, 1, EPI_PLAIN>(p, L, stream);
-            case 2: return launch_wk<2, 1, EPI_PLAIN>(p, L, stream);
-            case 4: return launch_wk<4, 1, EPI_PLAIN>(p, L, stream);
-            case 8: return launch_wk<8, 1, EPI_PLAIN>(p, L, stream);
-            case 16: return launch_wk<16, 1, EPI_PLAIN>(p, L, stream);
+            case 1: return launch_t<1, 1, EPI_PLAIN>(p, L, stream);
+            case 2: return launch_t<2, 1, EPI_PLAIN>(p, L, stream);
+            case 4: return launch_t<4, 1, EPI_PLAIN>(p, L, stream);
+            case 8: return launch_t<8, 1, EPI_PLAIN>(p, L, stream);
+            case 16: return launch_t<16, 1, EPI_PLAIN>(p, L, stream);
             default: return fail(Q4K_EINVAL, "unsupported vector count %d", nv);
         }
     }
     if (nv != 1) return fail(Q4K_EINVAL, "fused epilogues take one vector");
-    if (nmat == 1 && epi == EPI_SCALE) return launch_wk<1, 1, EPI_SCALE>(p, L, stream);
-    if (nmat == 1 && epi == EPI_RESID) return launch_wk<1, 1, EPI_RESID>(p, L, stream);
-    if (nmat == 2 && epi == EPI_SWIGLU) return launch_wk<1, 2, EPI_SWIGLU>(p, L, stream);
+    if (nmat == 1 && epi == EPI_SCALE) return launch_t<1, 1, EPI_SCALE>(p, L, stream);
+    if (nmat == 1 && epi == EPI_RESID) return launch_t<1, 1, EPI_RESID>(p, L, stream);
+    if (nmat == 2 && epi == EPI_SWIGLU) return launch_t<1, 2, EPI_SWIGLU>(p, L, stream);
     return fail(Q4K_EINVAL, "unsupported GEMV variant");
 }
 

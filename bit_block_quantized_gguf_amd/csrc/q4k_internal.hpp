@@ -58,24 +58,25 @@ struct GemvParams {
     float *y_v;             // EPI_SWIGLU: scaled up output [M]
     int32_t M, K, nb;       // nb = K / 256
     int64_t row_bytes;      // nb * 144
-    int32_t ks;             // K splits across workgroups (grid.y)
-    float *ws;              // ks > 1: partials [ks][nmat][nv][M]
-    unsigned *cnt;          // ks > 1: one arrival counter per 64-row tile
-    const float *in_sq;     // EPI_SCALE/RESID/SWIGLU: per-64-row-tile sum of squares of x
-    int32_t in_sq_n;        // number of partials to add (ceil(K/64))
+    int32_t ks;             // unused by the GEMV (the launch carries the grid)
+    float *ws;              // partials of tiles split between workgroups [groups][2][nv][64]
+    unsigned *cnt;          // unused by the GEMV
+    const float *in_sq;     // EPI_SCALE/RESID/SWIGLU: per-32-element sums of squares of x
+    int32_t in_sq_n;        // number of partials to add (ceil(K/32))
     int32_t in_len;         // divisor of the mean (K)
     const float *resid;     // EPI_RESID: residual [M]
-    float *out_sq;          // EPI != PLAIN: per-64-row-tile sum of squares of y
+    float *out_sq;          // EPI != PLAIN: per-32-row sums of squares of y
     float eps;
 };
 
 struct GemvLaunch {
-    int wk;  // waves per workgroup (K split inside a workgroup)
-    int ks;  // K splits across workgroups
+    int wk;  // waves per workgroup (= super-blocks per unit), fixed at 4
+    int ks;  // workgroups in the grid (each takes a contiguous range of units)
 };
 
-// Pick waves-per-group and cross-group splits for a GEMV shape.
-GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat);
+// Launch shape for a GEMV: as many workgroups as fit on the current device
+// (from the kernel's occupancy), capped by the number of work units.
+GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat, int epi = EPI_PLAIN);
 
 // Workspace needs of a launch.
 size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat);
@@ -85,11 +86,11 @@ size_t gemv_counters(int64_t M);
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,
                 hipStream_t stream);
 
-// Per-64-row-tile sum of squares of v[0..n) (used to seed the stack).
+// Per-32-element sums of squares of v[0..n) (used to seed the stack).
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
 
-// Tuning override for benchmarks (0 = heuristic).
-void set_gemv_override(int wk, int ks);
+// Tuning override for benchmarks: workgroup count (0 = occupancy-based).
+void set_gemv_override(int groups);
 
 // ---------------------------------------------------------------- dequant
 int launch_dequant(const uint8_t *w, float *out, int64_t M, int64_t K, hipStream_t stream);

@@ -14,7 +14,7 @@
 //                    g, v, a = silu(g) * v                (EPI_SWIGLU, gate|up in one pass)
 //                    h'    = h_mid + W_down rmsn(a)       (EPI_RESID)
 //   logits = W_lm rmsn(h)                                 (EPI_SCALE)
-// Every GEMV's epilogue writes the per-64-row-tile sums of squares of its
+// Every GEMV's epilogue writes the per-32-row sums of squares of its
 // output; the consumer adds them in a fixed order to get its input's RMS, so
 // RMS normalisation costs no extra pass and no extra node.
 #include "q4k_internal.hpp"
@@ -60,7 +60,8 @@ int check_mat(const q4k_mat &m, const char *name, int layer) {
     return Q4K_OK;
 }
 
-int64_t tiles_of(int64_t n) { return (n + 63) / 64; }
+// number of 32-element sum-of-squares granules of a vector
+int64_t tiles_of(int64_t n) { return (n + 31) / 32; }
 
 GemvParams base_params(const q4k_mat &m) {
     GemvParams p = {};
@@ -83,7 +84,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
     if (rc) return rc;
     ++n;
     auto run = [&](GemvParams p, int nmat, int epi, int64_t M, int64_t K) -> int {
-        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat);
+        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
         p.ks = L.ks;
         p.ws = s->ws.partials;
         p.cnt = s->ws.counters;
@@ -220,8 +221,8 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         return r;
     };
     size_t max_partials = 0, max_counters = 0;
-    auto need = [&](int64_t M, int64_t K, int nmat) {
-        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat);
+    auto need = [&](int64_t M, int64_t K, int nmat, int epi) {
+        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
         max_partials = std::max(max_partials, gemv_partial_floats(L, M, 1, nmat));
         max_counters = std::max(max_counters, gemv_counters(M));
     };
@@ -238,14 +239,14 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         s->sq_u.push_back(take(sqo, tiles_of(L.mix_in.M)));
         s->sq_hmid.push_back(take(sqo, tiles_of(H)));
         s->sq_a.push_back(take(sqo, tiles_of(L.gate.M)));
-        need(L.mix_in.M, L.mix_in.K, 1);
-        need(L.mix_out.M, L.mix_out.K, 1);
-        need(L.gate.M, L.gate.K, 2);
-        need(L.down.M, L.down.K, 1);
+        need(L.mix_in.M, L.mix_in.K, 1, EPI_SCALE);
+        need(L.mix_out.M, L.mix_out.K, 1, EPI_RESID);
+        need(L.gate.M, L.gate.K, 2, EPI_SWIGLU);
+        need(L.down.M, L.down.K, 1, EPI_RESID);
     }
     s->off_logits = take(off, s->lm_head.M);
     s->sq_logits = take(sqo, tiles_of(s->lm_head.M));
-    need(s->lm_head.M, s->lm_head.K, 1);
+    need(s->lm_head.M, s->lm_head.K, 1, EPI_SCALE);
     s->arena_floats = off;
     s->sq_floats = sqo;
 

@@ -43,9 +43,9 @@
  *  - Required alignment: 16 bytes for w, x/X, y/Y and out.
  *  - Results are deterministic: the same call on the same inputs returns the
  *    same bits (all reductions run in a fixed order; no float atomics).
- *  - Split-K partial sums live in a per-(device, stream) workspace that the
- *    library allocates on first use and keeps until q4k_release_workspaces()
- *    or process exit.  Calls queued on one stream are ordered; calls on
+ *  - Partial sums of work split between workgroups live in a per-(device,
+ *    stream) workspace that the library allocates on first use and keeps
+ *    until q4k_release_workspaces() or process exit.  Calls queued on one stream are ordered; calls on
  *    different streams use different workspaces.  Make the first call on a
  *    stream outside HIP graph capture.
  *  - Non-finite d/dmin propagate as IEEE arithmetic does; they are outside
@@ -197,18 +197,21 @@ void q4k_decode_stack_destroy(q4k_stack *s);
  * Launch-shape reporting and benchmark knobs.
  * ---------------------------------------------------------------------- */
 
-/* Waves per workgroup and cross-workgroup K splits that q4k_gemv /
- * q4k_gemv_batch pick for a shape (N vectors). */
+/* Launch shape that q4k_gemv / q4k_gemv_batch pick for a shape (N
+ * vectors): waves per workgroup (always 4) and the number of workgroups
+ * (as many as the device holds at once for that kernel, at most one per
+ * 64-row x 4-block work unit).  Without a device the count assumes 1024. */
 int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
-                    int32_t *k_splits);
+                    int32_t *workgroups);
 
 /* K splits that q4k_gemm picks for a shape. */
 int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *k_splits);
 
-/* Force the GEMV launch shape (waves_per_group in {2,4,8}, k_splits in
- * 1..64) or the GEMM K splits; 0 restores the shape heuristics.  Process-wide
- * and not synchronised with calls in flight: meant for benchmark sweeps. */
-int q4k_tune_gemv(int32_t waves_per_group, int32_t k_splits);
+/* Force the GEMV workgroup count (workgroups in 1..2^20, capped at the
+ * number of work units; waves_per_group must be 0 or 4) or the GEMM K
+ * splits; 0 restores the defaults.  Process-wide and not synchronised with
+ * calls in flight: meant for benchmark sweeps. */
+int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups);
 int q4k_tune_gemm(int32_t k_splits);
 
 /* Free the split-K workspaces of all (device, stream) pairs.  Synchronises

@@ -119,19 +119,21 @@ def test_stack_entry_points_reject_null(lib):
 def test_launch_shape_reports(lib):
     for (M, K) in [(17408, 5120), (5120, 17408), (5120, 6144), (16480, 5120), (248320, 5120),
                    (512, 1024), (1024, 512), (1, 256)]:
-        wk, ks = q4k.gemv_config(M, K, 1)
-        nb = K // 256
-        assert wk in (2, 4, 8) and 1 <= ks <= 64
-        assert ks == 1 or ks * wk <= nb
+        wk, groups = q4k.gemv_config(M, K, 1)
+        units = -(-M // 64) * -(-(K // 256) // 4)
+        assert wk == 4 and 1 <= groups <= units
     assert q4k.gemm_config(5120, 17408, 256) >= 1
 
 
 def test_tuning_knobs_validate(lib):
     assert lib.q4k_tune_gemv(3, 0) == -1
-    assert lib.q4k_tune_gemv(4, 65) == -1
+    assert lib.q4k_tune_gemv(8, 0) == -1
+    assert lib.q4k_tune_gemv(4, -1) == -1
     assert lib.q4k_tune_gemm(-1) == -1
-    q4k.tune_gemv(8, 3)
-    assert q4k.gemv_config(17408, 5120) == (8, 2)   # capped so each wave keeps a block
+    q4k.tune_gemv(4, 300)
+    assert q4k.gemv_config(17408, 5120) == (4, 300)
+    q4k.tune_gemv(0, 5000)
+    assert q4k.gemv_config(17408, 5120) == (4, 1360)   # at most one workgroup per unit
     q4k.tune_gemv(0, 0)
     q4k.tune_gemm(0)
 

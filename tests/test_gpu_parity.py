@@ -140,12 +140,13 @@ def test_gemv_deterministic_and_split_variants(q4k):
     assert np.array_equal(bits(y0), bits(y1))
     yr, S = oracle.gemv(w, x, M, K)
     try:
-        for wk in (2, 4, 8):
-            for ks in (1, 3, 8, 17):
-                q4k.tune_gemv(wk, ks)
-                note("gemv split wk=%d ks=%d" % (wk, ks))
-                y = down(q4k.gemv(wd, xd, M=M, K=K))
-                assert_gemv(y, yr, S, "wk=%d ks=%d" % (wk, ks))
+        for groups in (1, 7, 80, 81, 200, 333, 1024, 1360, 5000):
+            q4k.tune_gemv(0, groups)
+            note("gemv groups=%d" % groups)
+            y = down(q4k.gemv(wd, xd, M=M, K=K))
+            assert_gemv(y, yr, S, "groups=%d" % groups)
+            y2 = down(q4k.gemv(wd, xd, M=M, K=K))
+            assert np.array_equal(bits(y), bits(y2)), groups
     finally:
         q4k.tune_gemv(0, 0)
 
