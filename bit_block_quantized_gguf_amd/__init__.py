@@ -89,9 +89,9 @@ def load(path: str | None = None):
     L.q4k_decode_stack_destroy.argtypes = [p]
     L.q4k_decode_stack_destroy.restype = None
     L.q4k_gemv_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
-    L.q4k_gemm_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32)]
+    L.q4k_gemm_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.q4k_tune_gemv.argtypes = [i32, i32]
-    L.q4k_tune_gemm.argtypes = [i32]
+    L.q4k_tune_gemm.argtypes = [i32, i32]
     L.q4k_release_workspaces.argtypes = []
     L.q4k_release_workspaces.restype = None
     for name in ("q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
@@ -219,18 +219,20 @@ def gemv_config(M: int, K: int, N: int = 1) -> tuple[int, int]:
     return wk.value, ks.value
 
 
-def gemm_config(M: int, K: int, P: int) -> int:
-    ks = ctypes.c_int32()
-    check(load().q4k_gemm_config(M, K, P, ctypes.byref(ks)))
-    return ks.value
+def gemm_config(M: int, K: int, P: int) -> tuple[int, int]:
+    """(tile_tokens, k_splits) that q4k_gemm picks for the shape."""
+    tt, ks = ctypes.c_int32(), ctypes.c_int32()
+    check(load().q4k_gemm_config(M, K, P, ctypes.byref(tt), ctypes.byref(ks)))
+    return tt.value, ks.value
 
 
 def tune_gemv(waves_per_group: int = 0, k_splits: int = 0) -> None:
     check(load().q4k_tune_gemv(waves_per_group, k_splits))
 
 
-def tune_gemm(k_splits: int = 0) -> None:
-    check(load().q4k_tune_gemm(k_splits))
+def tune_gemm(tile_tokens: int = 0, k_splits: int = 0) -> None:
+    """Force the GEMM tile width (0, 128 or 256 tokens) and K splits (0: automatic)."""
+    check(load().q4k_tune_gemm(tile_tokens, k_splits))
 
 
 def release_workspaces() -> None:

@@ -240,7 +240,8 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
     Q4K_TRY(check_device());
     const GemmLaunch L = choose_gemm_launch(M, K, P);
     Workspace ws;
-    Q4K_TRY(stream_workspace((hipStream_t)stream, gemm_partial_floats(L, M, P),
+    Q4K_TRY(stream_workspace((hipStream_t)stream,
+                             gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P),
                              gemm_counters(M, P), &ws));
     return launch_gemm((const uint8_t *)w, X, Y, M, K, P, L, ws, (hipStream_t)stream);
 }
@@ -266,10 +267,12 @@ int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
     return Q4K_OK;
 }
 
-int q4k_tune_gemm(int32_t k_splits) {
+int q4k_tune_gemm(int32_t tile_tokens, int32_t k_splits) {
     clear_error();
+    if (tile_tokens != 0 && tile_tokens != 128 && tile_tokens != 256)
+        return fail(Q4K_EINVAL, "tile_tokens must be 0, 128 or 256");
     if (k_splits < 0 || k_splits > 64) return fail(Q4K_EINVAL, "k_splits must be in 0..64");
-    set_gemm_override(k_splits);
+    set_gemm_override(tile_tokens / 32, k_splits);
     return Q4K_OK;
 }
 
@@ -287,11 +290,13 @@ int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
     return Q4K_OK;
 }
 
-int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *k_splits) {
+int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32_t *k_splits) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
-    if (!k_splits) return fail(Q4K_EINVAL, "NULL output");
-    *k_splits = choose_gemm_launch(M, K, P).ks;
+    if (!tile_tokens || !k_splits) return fail(Q4K_EINVAL, "NULL output");
+    const GemmLaunch L = choose_gemm_launch(M, K, P);
+    *tile_tokens = 32 * L.r;
+    *k_splits = L.ks;
     return Q4K_OK;
 }
 

@@ -122,20 +122,29 @@ def test_launch_shape_reports(lib):
         wk, groups = q4k.gemv_config(M, K, 1)
         units = -(-M // 64) * -(-(K // 256) // 4)
         assert wk == 4 and 1 <= groups <= units
-    assert q4k.gemm_config(5120, 17408, 256) >= 1
+    tt, ks = q4k.gemm_config(5120, 17408, 256)
+    assert tt in (128, 256) and 1 <= ks <= 17408 // 256
 
 
 def test_tuning_knobs_validate(lib):
     assert lib.q4k_tune_gemv(3, 0) == -1
     assert lib.q4k_tune_gemv(8, 0) == -1
     assert lib.q4k_tune_gemv(4, -1) == -1
-    assert lib.q4k_tune_gemm(-1) == -1
+    assert lib.q4k_tune_gemm(0, -1) == -1
+    assert lib.q4k_tune_gemm(0, 65) == -1
+    assert lib.q4k_tune_gemm(64, 0) == -1
+    q4k.tune_gemm(256, 3)
+    assert q4k.gemm_config(17408, 5120, 512) == (256, 3)
+    q4k.tune_gemm(128, 0)
+    assert q4k.gemm_config(17408, 5120, 512)[0] == 128
+    q4k.tune_gemm(0, 64)
+    assert q4k.gemm_config(17408, 5120, 512)[1] == 20        # capped at K/256 super-blocks
     q4k.tune_gemv(4, 300)
     assert q4k.gemv_config(17408, 5120) == (4, 300)
     q4k.tune_gemv(0, 5000)
     assert q4k.gemv_config(17408, 5120) == (4, 1360)   # at most one workgroup per unit
     q4k.tune_gemv(0, 0)
-    q4k.tune_gemm(0)
+    q4k.tune_gemm(0, 0)
 
 
 def test_product_path_has_no_oracle_or_fallback():

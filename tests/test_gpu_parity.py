@@ -216,15 +216,24 @@ def _check_gemm(Y, w, X, M, K, rows, toks, what):
         assert c >= COS_MIN, "%s token %d cosine %.9f" % (what, t, c)
 
 
+@pytest.mark.parametrize("tile,ks", [(0, 0), (128, 1), (128, 3), (256, 1), (256, 2)])
 @pytest.mark.parametrize("M,K,P", [(300, 512, 1), (300, 512, 7), (128, 256, 128), (129, 768, 130),
-                                   (520, 1024, 200), (64, 4096, 33)])
-def test_gemm_small(q4k, M, K, P):
+                                   (520, 1024, 200), (64, 4096, 33), (257, 2048, 257),
+                                   (256, 1280, 128)])
+def test_gemm_small(q4k, M, K, P, tile, ks):
+    """Ragged rows and tokens around both tile widths; one, two, odd and even
+    super-block counts per split (0: automatic)."""
     w, _ = _case(5, M + P, M, K)
     X = synth.activations(5, P, K, first=M)
-    note("gemm %dx%d P=%d" % (M, K, P))
-    Y = down(q4k.gemm(up(w), up(X), M=M, K=K))
+    note("gemm %dx%d P=%d tile=%d ks=%d" % (M, K, P, tile, ks))
+    try:
+        q4k.tune_gemm(tile, ks)
+        Y = down(q4k.gemm(up(w), up(X), M=M, K=K))
+    finally:
+        q4k.tune_gemm(0, 0)
     toks = np.arange(P)
-    _check_gemm(Y, w, X, M, K, np.arange(M), toks, "gemm %dx%d P=%d" % (M, K, P))
+    _check_gemm(Y, w, X, M, K, np.arange(M), toks,
+                "gemm %dx%d P=%d tile=%d ks=%d" % (M, K, P, tile, ks))
 
 
 def _sample(n, rng, k=48, tile=128):
@@ -271,13 +280,13 @@ def test_gemm_split_k_variants_agree(q4k):
     rows, toks = _sample(M, rng, 24), _sample(P, rng, 8)
     try:
         outs = []
-        for ks in (1, 2, 4, 8):
-            q4k.tune_gemm(ks)
-            note("gemm ks=%d" % ks)
+        for tt, ks in ((128, 1), (128, 2), (128, 3), (128, 7), (256, 1), (256, 4), (256, 64)):
+            q4k.tune_gemm(tt, ks)
+            note("gemm tile=%d ks=%d" % (tt, ks))
             Y = down(q4k.gemm(wd, Xd, M=M, K=K))
-            _check_gemm(Y, w, X, M, K, rows, toks, "ks=%d" % ks)
+            _check_gemm(Y, w, X, M, K, rows, toks, "tile=%d ks=%d" % (tt, ks))
             outs.append(Y)
         Y2 = down(q4k.gemm(wd, Xd, M=M, K=K))
         assert np.array_equal(bits(Y2), bits(outs[-1]))          # deterministic
     finally:
-        q4k.tune_gemm(0)
+        q4k.tune_gemm(0, 0)
