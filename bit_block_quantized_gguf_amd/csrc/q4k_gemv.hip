@@ -18,8 +18,9 @@
 //    they arrive by scalar loads (constant address space) and enter every FMA
 //    as an SGPR operand.  The wave index goes through readfirstlane so the
 //    compiler can prove those addresses wave-uniform.
-//  * Per weight the VALU work is one byte-to-float conversion and one FMA
-//    (plus one AND per four weights).  Per block the scale/min algebra is
+//  * Per weight the VALU work is one FMA taking the nibble as a binary16
+//    operand (v_fma_mix_f32), plus an AND and two byte permutes per four
+//    weights.  Per block the scale/min algebra is
 //       y += d * sum_j sc_j * T_j  -  dmin * sum_j m_j * X_j
 //    with T_j = sum(q*x) and X_j = sum(x) over sub-block j; high nibbles are
 //    converted in place (16*q) and their partial sum carries the exact factor
@@ -67,10 +68,29 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Bytes 2k, 2k+1 of v (k = 0, 1) as the two 16-bit halves of a dword.
+__device__ __forceinline__ half2v byte_pair(uint32_t v, int k) {
+    return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, v, k ? 0x0C030C02u : 0x0C010C00u));
+}
+
 // acc[n] += sum over the block of w * x_n (factored form).
+//
+// A nibble value c (0..15, or 16q for a high nibble kept in place) sitting in
+// a 16-bit half is, read as binary16, the subnormal c * 2^-24 exactly, and
+// v_fma_mix_f32 takes such a half as an operand.  So each weight costs one
+// FMA (no byte-to-float conversion): the sums T_j carry the exact factor
+// 2^-24, removed at the end by a power-of-two scaling (exact, so the sums
+// equal the unscaled ones unless a product falls below the f32 normal range).
 template <int NV>
 __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk, int64_t xs,
                                           const float4 (&xq)[NV], float (&acc)[NV]) {
+    // Up to two vectors the nibbles go through v_fma_mix_f32; with more, one
+    // conversion per weight is shared by NV FMAs and the extra registers of
+    // the byte permutes cost more than they save.
+    constexpr bool MIX = NV <= 2;
+    constexpr float kScale = MIX ? 16777216.0f : 1.0f;  // 2^24 removes the binary16 subnormal scale
     const float d = half_lo(b[0].x);
     const float dmin = half_hi(b[0].x);
     const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
@@ -82,28 +102,50 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
         float tl[NV], th[NV];
 #pragma unroll
         for (int n = 0; n < NV; ++n) tl[n] = th[n] = 0.f;
+        if constexpr (MIX) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-            const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
+            for (int half = 0; half < 2; ++half) {
+                float(&t)[NV] = half ? th : tl;
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const float q = ubyte(lo, bb);
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+                    const uint32_t c = and_mask(v, half ? 0xF0F0F0F0u : 0x0F0F0F0Fu);  // q or 16*q
+                    cfloat *xr = as_const(xblk + 64 * g + 32 * half + 4 * i);
 #pragma unroll
-                for (int n = 0; n < NV; ++n)
-                    tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
+                    for (int k = 0; k < 2; ++k) {
+                        const half2v q2 = byte_pair(c, k);
+#pragma unroll
+                        for (int n = 0; n < NV; ++n) {
+                            t[n] = fmaf((float)q2.x, xr[n * xs + 2 * k], t[n]);
+                            t[n] = fmaf((float)q2.y, xr[n * xs + 2 * k + 1], t[n]);
+                        }
+                    }
+                }
             }
-        }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-            const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+                const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const float q = ubyte(hi, bb);
+                for (int bb = 0; bb < 4; ++bb) {
+                    const float q = ubyte(lo, bb);
 #pragma unroll
-                for (int n = 0; n < NV; ++n)
-                    th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
+                    for (int n = 0; n < NV; ++n)
+                        tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+                const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const float q = ubyte(hi, bb);
+#pragma unroll
+                    for (int n = 0; n < NV; ++n)
+                        th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
+                }
             }
         }
         const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
@@ -124,7 +166,7 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
         for (int sb = 0; sb < 8; ++sb)
             B[n] = fmaf(min_of(sc, sb),
                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
-        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f, A_lo[n]), -dmin * B[n]);
+        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f * kScale, A_lo[n] * kScale), -dmin * B[n]);
     }
 }
 
@@ -226,9 +268,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
     for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
     // Loads of unit u: a uniform tile base (SGPRs) plus a 32-bit lane offset;
     // rows past M are clamped to the last row (their results are not stored).
-    auto fetch = [&](int64_t u) {
-        const int t = (int)(u / un.upt);
-        const int j0 = (int)(u - (int64_t)t * un.upt) * WK;
+    // Unit u = t * upt + k is passed as (t, k): no 64-bit division in the loop.
+    auto fetch = [&](int t, int k) {
+        const int j0 = k * WK;
         const int valid = min(WK, p.nb - j0) * kBlockBytes;  // bytes per row segment
         const int rmax = min(ROWS - 1, p.M - 1 - t * ROWS);
         const int64_t base = (int64_t)t * ROWS * p.row_bytes + (int64_t)j0 * kBlockBytes;
@@ -236,11 +278,11 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         const uint8_t *b1 = NMAT == 2 ? p.w1 + base : b0;
 #pragma unroll
         for (int i = 0; i < CH_THREAD; ++i) {
-            const int r = NMAT == 2 ? (crow[i] & 31) : crow[i];
-            const uint32_t off =
-                (uint32_t)min(r, rmax) * (uint32_t)p.row_bytes + (uint32_t)coff[i];
-            const uint8_t *src = (NMAT == 2 && crow[i] >= 32) ? b1 : b0;
-            if (coff[i] < valid) reg[i] = ldg16(src + off);
+            const int cr = crow[i], co = coff[i];
+            const int r = NMAT == 2 ? (cr & 31) : cr;
+            const uint32_t off = (uint32_t)min(r, rmax) * (uint32_t)p.row_bytes + (uint32_t)co;
+            const uint8_t *src = (NMAT == 2 && cr >= 32) ? b1 : b0;
+            if (co < valid) reg[i] = ldg16(src + off);
         }
     };
     auto commit = [&]() {
@@ -253,14 +295,16 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
 #pragma unroll
     for (int n = 0; n < NV; ++n) acc[n] = 0.f;
 
-    fetch(ua);
+    int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);  // unit u = t*upt + k
+    fetch(t, k);
     commit();
     __syncthreads();
-    int64_t seg0 = ua;
+    bool seg_first = k == 0;  // the current tile's range started at its first unit
     for (int64_t u = ua; u < ub; ++u) {
-        const int t = (int)(u / un.upt);
-        const int j = (int)(u - (int64_t)t * un.upt) * WK + wave;  // this wave's block
+        const int j = k * WK + wave;  // this wave's block
         const bool active = j < p.nb;
+        const bool last_of_tile = k + 1 == un.upt;
+        const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
         // activation sums for this block first, then the next unit's loads
         float4 xq[NV];
         if (active) {
@@ -270,7 +314,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
                                                           4 * lane);
         }
         const bool more = u + 1 < ub;
-        if (more) fetch(u + 1);
+        if (more) fetch(tn, kn);
         if (active) {
             const uint8_t *lp = &stage[lane * SEGP + wave * kBlockBytes];
             uint4 b[9];
@@ -278,7 +322,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
             for (int i = 0; i < 9; ++i) b[i] = *reinterpret_cast<const uint4 *>(lp + 16 * i);
             block_dot<NV>(b, p.x + 256 * (int64_t)j, p.x_stride, xq, acc);
         }
-        const bool seg_end = !more || (u + 1) / un.upt != t;
+        const bool seg_end = !more || last_of_tile;
         if (seg_end) {
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
@@ -296,7 +340,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
                 for (int w = 1; w < WK; ++w) s += red[w][n][lane];
                 tot[n] = s;
             }
-            const bool whole = seg0 == (int64_t)t * un.upt && u + 1 == (int64_t)(t + 1) * un.upt;
+            const bool whole = seg_first && last_of_tile;
             if (whole) {
                 epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot);
             } else {
@@ -306,7 +350,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
                     p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane] = tot[n];
             }
         }
-        if (seg_end) seg0 = u + 1;
+        if (seg_end) seg_first = true;
+        t = tn;
+        k = kn;
         if (more) commit();
         __syncthreads();
     }
