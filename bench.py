@@ -69,7 +69,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sections", default="gemv,batch,small,gemm,stack,cpu",
-                    help="comma list of gemv,batch,small,gemm,stack,cpu")
+                    help="comma list of gemv,batch,small,gemm,stack,cpu (and copy: the "
+                         "256 MiB device copy that calibrates the PMC traffic counters)")
     ap.add_argument("--copies", type=int, default=4, help="cold-rotation copies per MLP matrix")
     ap.add_argument("--stack-tokens", type=int, default=20)
     args = ap.parse_args()
@@ -126,16 +127,12 @@ def main():
         a = (torch.nn.functional.silu(y_gate) * y_up).contiguous()   # caller's SwiGLU, untimed
         torch.cuda.synchronize()
 
-        def step(i, evs=None):
+        def step(i):
             c = i % args.copies
-            for j, (name, w, xin, y) in enumerate((("gate", copies["gate"][c], xd, y_gate),
-                                                   ("up", copies["up"][c], xd, y_up),
-                                                   ("down", copies["down"][c], a, y_down))):
-                if evs is not None:
-                    evs[j][0].record(stream)
+            for name, w, xin, y in (("gate", copies["gate"][c], xd, y_gate),
+                                    ("up", copies["up"][c], xd, y_up),
+                                    ("down", copies["down"][c], a, y_down)):
                 q4k.gemv(w, xin, y)
-                if evs is not None:
-                    evs[j][1].record(stream)
 
         for i in range(args.warmup):
             step(i)
@@ -146,20 +143,23 @@ def main():
             step(i)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / args.steps
-        # per-launch HIP-event timing on the launch stream: all timed steps
-        # are enqueued back to back and the stream is synchronised once, so
-        # each event pair brackets one GEMV call (main kernel plus, for split
-        # tiles, its reduce kernel) as the GPU executed it
+        # Per-matrix launch duration from HIP events on the launch stream: one
+        # event pair around a burst of `steps` back-to-back launches of that
+        # matrix (cold copies in rotation), so the average is the kernel time
+        # plus the inter-kernel gap, as in the step, without event overhead
+        # between launches.  Repeated 3 times; mean and median of the bursts.
         per = {n: [] for n in ("gate", "up", "down")}
-        all_evs = []
-        for i in range(args.steps):
-            evs = [(ev(), ev()) for _ in range(3)]
-            step(i, evs)
-            all_evs.append(evs)
-        torch.cuda.synchronize()
-        for evs in all_evs:
-            for j, n in enumerate(("gate", "up", "down")):
-                per[n].append(evs[j][0].elapsed_time(evs[j][1]) * 1e3)   # us
+        ins = {"gate": (xd, y_gate), "up": (xd, y_up), "down": (a, y_down)}
+        for rep in range(3):
+            for n in ("gate", "up", "down"):
+                xin, y = ins[n]
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for i in range(args.steps):
+                    q4k.gemv(copies[n][i % args.copies], xin, y)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per[n].append(e0.elapsed_time(e1) * 1e3 / args.steps)   # us per launch
         kern = {n: float(np.mean(v)) for n, v in per.items()}
         kern_med = {n: float(np.median(v)) for n, v in per.items()}
         gpu_us = sum(kern.values())
@@ -186,7 +186,9 @@ def main():
                 traffic = tr.get("hbm_bytes_per_launch")
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "q4k_gemv on gate 17408x5120 (gemv_kernel<1,1,PLAIN> + gemv_reduce_kernel)",
+                           "kernel": "q4k_gemv on gate 17408x5120 (gemv_kernel<1,1,PLAIN>, one row tile "
+                                     "per workgroup, no reduce launch)",
+                           "timing": "HIP events around bursts of back-to-back launches (kernel + gap)",
                            "algorithmic_bytes_per_launch": mlp_bytes["gate"] + 4 * (5120 + 17408)}
         log("MLP GEMVs: step %.2f us wall, kernels %s" % (wall * 1e6, kern))
         del copies
@@ -327,6 +329,21 @@ def main():
         stk.close()
         del layers, lm
         torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ counter calibration
+    if "copy" in sections:
+        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # readings under rocprofv3 --pmc give the factors that turn those
+        # counters into bytes for the GEMV dispatches profiled in the same run.
+        n = 256 << 20
+        src = torch.ones(n // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"bytes_each_way": n, "launches": 3}
+        del src, dst
 
     # ------------------------------------------------------------ CPU baseline
     if "cpu" in sections:

@@ -228,14 +228,22 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
     }
 }
 
-// Unit bookkeeping shared by the main and the reduce kernel.
+// Unit bookkeeping shared by the main and the reduce kernel.  The divisions
+// run in 32 bits when the products fit (64-bit division is a long scalar
+// sequence on this ISA).
 struct Units {
     int upt;      // units per row tile = ceil(nb / 4)
     int64_t U;    // total units = tiles * upt
     int G;        // workgroups in the main grid
-    __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
+    bool small;   // (U + 1) * G < 2^32
+    __device__ __forceinline__ int64_t begin(int g) const {
+        if (small) return (int64_t)((uint32_t)g * (uint32_t)U / (uint32_t)G);
+        return (int64_t)g * U / G;
+    }
     // workgroup whose range contains unit u
     __device__ __forceinline__ int owner(int64_t u) const {
+        if (small)
+            return (int)(((uint32_t)(u + 1) * (uint32_t)G + (uint32_t)U - 1) / (uint32_t)U) - 1;
         return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
     }
 };
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
     const int g = blockIdx.x;
     const int64_t ua = un.begin(g), ub = un.begin(g + 1);
     if (ua >= ub) return;
-    const int first_tile = (int)(ua / un.upt);
+    const int first_tile = un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
 
     // this thread's copy chunks of a full unit: lane row r = q / 36, chunk c = q % 36
     int coff[CH_THREAD];  // byte offset inside the row's 576-byte segment
@@ -372,7 +380,8 @@ __global__ __launch_bounds__(64) void gemv_reduce_kernel(const GemvParams p, con
 #pragma unroll
     for (int n = 0; n < NV; ++n) tot[n] = 0.f;
     for (int g = gf; g <= gl; ++g) {
-        const int ft = (int)(un.begin(g) / un.upt);
+        const int64_t bg = un.begin(g);
+        const int ft = un.small ? (int)((uint32_t)bg / (uint32_t)un.upt) : (int)(bg / un.upt);
         const int slot = t == ft ? 0 : 1;
 #pragma unroll
         for (int n = 0; n < NV; ++n) tot[n] += p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane];
@@ -399,9 +408,9 @@ std::atomic<int> g_override_groups{0};
 // Resident workgroups of each kernel instance on a device (occupancy queries
 // are not free, so they are cached).
 std::mutex g_occ_mutex;
-std::map<std::pair<int, const void *>, int> g_occ;
+std::map<std::pair<int, const void *>, std::pair<int, int>> g_occ;  // -> (resident groups, CUs)
 
-int resident_groups(const void *fn, int *out) {
+int resident_groups(const void *fn, int *out, int *cus_out) {
     int dev = 0;
     Q4K_HIP(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lock(g_occ_mutex);
@@ -411,9 +420,11 @@ int resident_groups(const void *fn, int *out) {
         int per_cu = 0, cus = 0;
         Q4K_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * WK, 0));
         Q4K_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-        it = g_occ.emplace(key, std::max(1, per_cu) * std::max(1, cus)).first;
+        it = g_occ.emplace(key, std::make_pair(std::max(1, per_cu) * std::max(1, cus),
+                                               std::max(1, cus))).first;
     }
-    *out = it->second;
+    *out = it->second.first;
+    *cus_out = it->second.second;
     return Q4K_OK;
 }
 
@@ -422,15 +433,21 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
     return ((M + rows - 1) / rows) * ((K / 256 + WK - 1) / WK);
 }
 
+// Workgroup count.  One vector with at least one row tile per CU: one tile
+// per workgroup (measured as fast as filling every resident slot, and no
+// partials, so no reduce launch).  Otherwise every resident slot, ranges
+// splitting tiles (the N-vector kernels run fewer waves per CU and need them).
 template <int NV, int NMAT, int EPI>
 int groups_for(int64_t M, int64_t K, int *G) {
-    int res = 0;
+    int res = 0, cus = 0;
     const int o = g_override_groups.load();
+    int64_t g = o;
     if (o <= 0) {
-        int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res);
+        int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res, &cus);
         if (rc) return rc;
+        const int64_t tiles = (M + 64 / NMAT - 1) / (64 / NMAT);
+        g = (NV == 1 && tiles >= cus) ? tiles : res;
     }
-    const int64_t g = o > 0 ? (int64_t)o : (int64_t)res;
     *G = (int)std::max<int64_t>(1, std::min<int64_t>(g, units_of(M, K, NMAT)));
     return Q4K_OK;
 }
@@ -443,6 +460,7 @@ int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     un.upt = (p.nb + WK - 1) / WK;
     un.U = tiles * un.upt;
     un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
+    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
                        stream, p, un);
