@@ -29,14 +29,15 @@
 //    computed (the activation-sum load goes first, so the in-order vmcnt wait
 //    for it does not drain the prefetch), then copied to LDS between two
 //    workgroup barriers.
-//  * Launch: exactly as many workgroups as fit on the device at once; each
-//    takes a contiguous range of units in (row tile, K) order, accumulating a
-//    row tile's blocks in registers.  A tile whose units all fall in one
-//    workgroup is finished there (four waves added in LDS in wave order, then
-//    the epilogue).  A tile split between workgroups leaves one partial per
-//    workgroup, and a second kernel adds them in workgroup order and applies
-//    the epilogue.  Results are deterministic and no cross-workgroup fence is
-//    needed inside a kernel.
+//  * Launch: one 64-row tile per workgroup when there are at least as many
+//    tiles as CUs (one vector), else as many workgroups as fit on the device
+//    at once; each takes a contiguous range of units in (row tile, K) order,
+//    accumulating a row tile's blocks in registers.  A tile whose units all
+//    fall in one workgroup is finished there (four waves added in LDS in wave
+//    order, then the epilogue).  A tile split between workgroups is finished
+//    by its last-arriving contributor, which adds the partials in workgroup
+//    order (see finish_split_tile): deterministic, no second kernel, and no
+//    cache-wide fence.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -171,9 +172,22 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
 }
 
 // Inverse RMS of an input vector from its per-32-element sums of squares.
+// Up to 1024 granules (K <= 32768) every lane issues its loads before adding
+// them (in the same order as the plain loop), so the latency is paid once.
 __device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
     float ss = 0.f;
-    for (int i = lane; i < p.in_sq_n; i += 64) ss += p.in_sq[i];
+    if (p.in_sq_n <= 16 * 64) {
+        float v[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int i = lane + 64 * c;
+            v[c] = i < p.in_sq_n ? p.in_sq[i] : 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) ss += v[c];
+    } else {
+        for (int i = lane; i < p.in_sq_n; i += 64) ss += p.in_sq[i];
+    }
     ss = wave_sum(ss);
     return 1.0f / sqrtf(ss / (float)p.in_len + p.eps);
 }
@@ -183,7 +197,7 @@ __device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
 // gate rows row0 + lane, lanes 32..63 the up rows of the same indices.
 template <int NV, int NMAT, int EPI>
 __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane,
-                                         const float (&tot)[NV]) {
+                                         const float (&tot)[NV], float inv) {
     if constexpr (EPI == EPI_PLAIN) {
         const int row = row0 + lane;
         if (row < p.M) {
@@ -191,7 +205,6 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
             for (int n = 0; n < NV; ++n) p.y[(int64_t)n * p.y_stride + row] = tot[n];
         }
     } else {
-        const float inv = inv_rms(p, lane);
         float val;
         int row;
         bool ok;
@@ -247,6 +260,62 @@ struct Units {
         return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
     }
 };
+
+// A tile whose units are split between workgroups: each contributor stores
+// its partial sums with device-coherent stores (they bypass the per-XCD L2
+// copies, so no cache write-back or invalidation is needed), waits until they
+// have completed, and counts itself in on the tile's arrival counter.  The
+// last contributor adds all partials in workgroup order — the same sum
+// whichever workgroup arrives last — applies the epilogue and resets the
+// counter to zero for the next launch.  Counters start at zero when the
+// workspace is allocated.  The partials are loaded in chunks of 16 / NV
+// contributors, all loads of a chunk in flight together.
+template <int NV, int NMAT, int EPI>
+__device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Units &un, int g,
+                                                  int t, int slot, int lane,
+                                                  const float (&tot)[NV], float inv) {
+    constexpr int ROWS = 64 / NMAT;
+    constexpr int CH = NV >= 16 ? 1 : 16 / NV;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+        __hip_atomic_store(&p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane], tot[n],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores have completed
+    const int gf = un.owner((int64_t)t * un.upt);
+    const int gl = un.owner((int64_t)(t + 1) * un.upt - 1);
+    unsigned old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(&p.cnt[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (unsigned)(gl - gf)) return;  // not the last contributor
+    if (lane == 0) __hip_atomic_store(&p.cnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float sum[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) sum[n] = 0.f;
+    for (int c0 = gf; c0 <= gl; c0 += CH) {
+        float part[CH][NV];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int g2 = c0 + c;
+            if (g2 <= gl) {
+                const int64_t bg = un.begin(g2);
+                const int ft = un.small ? (int)((uint32_t)bg / (uint32_t)un.upt) : (int)(bg / un.upt);
+                const int sl = t == ft ? 0 : 1;
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+                    part[c][n] = __hip_atomic_load(&p.ws[(((int64_t)g2 * 2 + sl) * NV + n) * 64 + lane],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (c0 + c <= gl) {
+#pragma unroll
+                for (int n = 0; n < NV; ++n) sum[n] += part[c][n];
+            }
+    }
+    epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, sum, inv);
+}
 
 template <int NV, int NMAT, int EPI>
 __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const Units un) {
@@ -305,6 +374,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
 
     int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);  // unit u = t*upt + k
     fetch(t, k);
+    // the epilogue's 1/rms(x), read while the first unit is in flight
+    const float inv = EPI == EPI_PLAIN ? 1.f : inv_rms(p, lane);
     commit();
     __syncthreads();
     bool seg_first = k == 0;  // the current tile's range started at its first unit
@@ -349,14 +420,11 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
                 tot[n] = s;
             }
             const bool whole = seg_first && last_of_tile;
-            if (whole) {
-                epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot);
-            } else {
-                const int slot = t == first_tile ? 0 : 1;
-#pragma unroll
-                for (int n = 0; n < NV; ++n)
-                    p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane] = tot[n];
-            }
+            if (whole)
+                epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot, inv);
+            else
+                finish_split_tile<NV, NMAT, EPI>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot,
+                                                 inv);
         }
         if (seg_end) seg_first = true;
         t = tn;
@@ -364,29 +432,6 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         if (more) commit();
         __syncthreads();
     }
-}
-
-// Adds the partials of tiles split between workgroups (workgroup order) and
-// applies the epilogue.  Tiles finished by one workgroup are skipped.
-template <int NV, int NMAT, int EPI>
-__global__ __launch_bounds__(64) void gemv_reduce_kernel(const GemvParams p, const Units un) {
-    const int lane = threadIdx.x;
-    constexpr int ROWS = 64 / NMAT;
-    const int t = blockIdx.x;
-    const int gf = un.owner((int64_t)t * un.upt);
-    const int gl = un.owner((int64_t)(t + 1) * un.upt - 1);
-    if (gf == gl) return;
-    float tot[NV];
-#pragma unroll
-    for (int n = 0; n < NV; ++n) tot[n] = 0.f;
-    for (int g = gf; g <= gl; ++g) {
-        const int64_t bg = un.begin(g);
-        const int ft = un.small ? (int)((uint32_t)bg / (uint32_t)un.upt) : (int)(bg / un.upt);
-        const int slot = t == ft ? 0 : 1;
-#pragma unroll
-        for (int n = 0; n < NV; ++n) tot[n] += p.ws[(((int64_t)g * 2 + slot) * NV + n) * 64 + lane];
-    }
-    epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, tot);
 }
 
 __global__ __launch_bounds__(64) void sumsq_kernel(const float *__restrict__ v, int64_t n,
@@ -465,14 +510,6 @@ int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
                        stream, p, un);
     Q4K_HIP(hipGetLastError());
-    // Every workgroup range starts on a tile boundary only when each tile is
-    // one unit, or when the tiles divide evenly among the workgroups.
-    const bool split = un.upt > 1 && (un.G > tiles || tiles % un.G != 0);
-    if (split) {
-        hipLaunchKernelGGL((gemv_reduce_kernel<NV, NMAT, EPI>), dim3((unsigned)tiles), dim3(64), 0,
-                           stream, p, un);
-        Q4K_HIP(hipGetLastError());
-    }
     return Q4K_OK;
 }
 
@@ -510,8 +547,7 @@ size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat) {
 }
 
 size_t gemv_counters(int64_t M) {
-    (void)M;
-    return 0;
+    return (size_t)((M + 31) / 32);  // one arrival counter per tile (32 rows for the fused gate|up)
 }
 
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,

@@ -60,7 +60,7 @@ struct GemvParams {
     int64_t row_bytes;      // nb * 144
     int32_t ks;             // unused by the GEMV (the launch carries the grid)
     float *ws;              // partials of tiles split between workgroups [groups][2][nv][64]
-    unsigned *cnt;          // unused by the GEMV
+    unsigned *cnt;          // per-tile arrival counters of split tiles (zero between launches)
     const float *in_sq;     // EPI_SCALE/RESID/SWIGLU: per-32-element sums of squares of x
     int32_t in_sq_n;        // number of partials to add (ceil(K/32))
     int32_t in_len;         // divisor of the mean (K)
