@@ -273,7 +273,7 @@ def main():
                 tf = 2.0 * M * K * P / t / 1e6
                 res.append({"M": M, "K": K, "P": P, "us": t, "TFLOPs": tf,
                             "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
-                            "tile_tokens_k_splits": list(q4k.gemm_config(M, K, P))})
+                            "tile_tokens_workgroups": list(q4k.gemm_config(M, K, P))})
                 del X, Y
         out["prefill_gemm"] = res
         log("gemm: %s" % [(r["M"], r["P"], round(r["TFLOPs"], 1)) for r in res])

@@ -220,19 +220,20 @@ def gemv_config(M: int, K: int, N: int = 1) -> tuple[int, int]:
 
 
 def gemm_config(M: int, K: int, P: int) -> tuple[int, int]:
-    """(tile_tokens, k_splits) that q4k_gemm picks for the shape."""
-    tt, ks = ctypes.c_int32(), ctypes.c_int32()
-    check(load().q4k_gemm_config(M, K, P, ctypes.byref(tt), ctypes.byref(ks)))
-    return tt.value, ks.value
+    """(tile_tokens, workgroups) that q4k_gemm picks for the shape."""
+    tt, wg = ctypes.c_int32(), ctypes.c_int32()
+    check(load().q4k_gemm_config(M, K, P, ctypes.byref(tt), ctypes.byref(wg)))
+    return tt.value, wg.value
 
 
-def tune_gemv(waves_per_group: int = 0, k_splits: int = 0) -> None:
-    check(load().q4k_tune_gemv(waves_per_group, k_splits))
+def tune_gemv(waves_per_group: int = 0, workgroups: int = 0) -> None:
+    """Force the GEMV workgroup count (0: automatic); waves_per_group must be 0 or 4."""
+    check(load().q4k_tune_gemv(waves_per_group, workgroups))
 
 
-def tune_gemm(tile_tokens: int = 0, k_splits: int = 0) -> None:
-    """Force the GEMM tile width (0, 128 or 256 tokens) and K splits (0: automatic)."""
-    check(load().q4k_tune_gemm(tile_tokens, k_splits))
+def tune_gemm(tile_tokens: int = 0, workgroups: int = 0) -> None:
+    """Force the GEMM tile width (0, 128 or 256 tokens) and workgroup count (0: automatic)."""
+    check(load().q4k_tune_gemm(tile_tokens, workgroups))
 
 
 def release_workspaces() -> None:

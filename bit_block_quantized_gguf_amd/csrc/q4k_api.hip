@@ -254,9 +254,9 @@ void q4k_release_workspaces(void) {
     g_ws.clear();
 }
 
-/* Benchmark knobs: force the GEMV waves-per-group / K splits and the GEMM K
- * splits (0 restores the shape heuristics).  Not thread-safe with respect to
- * concurrent calls; meant for sweeps. */
+/* Benchmark knobs: force the GEMV workgroup count and the GEMM tile width and
+ * workgroup count (0 restores the shape heuristics).  Not thread-safe with
+ * respect to concurrent calls; meant for sweeps. */
 int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
     clear_error();
     if (waves_per_group != 0 && waves_per_group != 4)
@@ -267,12 +267,13 @@ int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
     return Q4K_OK;
 }
 
-int q4k_tune_gemm(int32_t tile_tokens, int32_t k_splits) {
+int q4k_tune_gemm(int32_t tile_tokens, int32_t workgroups) {
     clear_error();
     if (tile_tokens != 0 && tile_tokens != 128 && tile_tokens != 256)
         return fail(Q4K_EINVAL, "tile_tokens must be 0, 128 or 256");
-    if (k_splits < 0 || k_splits > 64) return fail(Q4K_EINVAL, "k_splits must be in 0..64");
-    set_gemm_override(tile_tokens / 32, k_splits);
+    if (workgroups < 0 || workgroups > 4096)
+        return fail(Q4K_EINVAL, "workgroups must be in 0..4096");
+    set_gemm_override(tile_tokens / 32, workgroups);
     return Q4K_OK;
 }
 
@@ -290,13 +291,15 @@ int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
     return Q4K_OK;
 }
 
-int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32_t *k_splits) {
+int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32_t *workgroups) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
-    if (!tile_tokens || !k_splits) return fail(Q4K_EINVAL, "NULL output");
+    if (!tile_tokens || !workgroups) return fail(Q4K_EINVAL, "NULL output");
     const GemmLaunch L = choose_gemm_launch(M, K, P);
     *tile_tokens = 32 * L.r;
-    *k_splits = L.ks;
+    // the launch caps the count at the number of work items
+    const int64_t tiles = ((M + 255) / 256) * ((P + 32 * L.r - 1) / (32 * L.r));
+    *workgroups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(L.ks, tiles * (K / 256)));
     return Q4K_OK;
 }
 

@@ -34,10 +34,14 @@
 //  * Output layout of the 32x32 MFMA: lane l holds column l%32 (a W row) and
 //    rows 8(v/4) + 4(l/32) + v%4 (tokens) of accumulator v, so each store
 //    instruction writes 32 consecutive floats of a token row.
-//  * When there are too few tiles to fill the chip the K range is split
-//    across workgroups: each split writes its partial tile to a workspace and
-//    a second kernel adds the splits in order (deterministic; no
-//    cross-workgroup synchronisation inside a kernel).
+//  * Stream-K scheduling: the (tile, super-block) work items, tile-major,
+//    are cut into one equal contiguous range per workgroup (by default one
+//    workgroup per CU), so every CU gets the same number of super-blocks
+//    whatever the tile count.  A tile wholly inside a range is written to Y;
+//    a range's first and last tile, when the range starts or ends inside
+//    them, go to two partial slots of the workgroup, and a fix-up kernel adds
+//    each cut tile's pieces in workgroup order (ascending K).  Deterministic;
+//    no cross-workgroup synchronisation inside a kernel.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -65,6 +69,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// Stream-K partition: the (tile, super-block) work items, tile-major, are
+// split into G equal contiguous ranges, one per workgroup.  Tile t covers W
+// rows 256 (t mod rtiles) .. +255 and tokens BN (t div rtiles) .. +BN-1.
+struct SKUnits {
+    int nb;       // super-blocks per row (work items per tile)
+    int rtiles;   // 256-row tiles
+    int64_t U;    // total work items = tiles * nb
+    int G;        // workgroups
+    __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
+    // workgroup whose range contains item u
+    __device__ __forceinline__ int owner(int64_t u) const {
+        return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
+    }
+};
 
 struct GemmParams {
     const uint8_t *w;
@@ -118,20 +137,23 @@ struct WBlock {
 // buffer, the X slice of step s+1 is copied into the other buffer, and the W
 // bytes of the next super-block are loaded into the other register set; the
 // copies are spread over the step's MFMA blocks.
+// One segment: super-blocks [jb, je) of tile `tile`.  A whole tile is written
+// to Y; a part of a tile goes to the workgroup's partial slot (0: the first
+// tile of its range, 1: the last) for the fix-up kernel.  xs: the two LDS X
+// buffers (BN tokens x 128 columns each).
 template <int T>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
+__device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits &su, int g,
+                                             int tile, int jb, int je, int slot,
+                                             __bf16 (*xs)[32 * T * KS]) {
     constexpr int BN = 32 * T;
-    // buffer `half` holds X columns [256j + 128 half, +128) of the tile's tokens
-    __shared__ __attribute__((aligned(1024))) __bf16 xs[2][BN * KS];
-
-    const int tid = threadIdx.x;
+    // opaque per segment: nothing derived from the thread index is hoisted out
+    // of the caller's segment loop and kept live across the main loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rt = blockIdx.x, tt = blockIdx.y, split = blockIdx.z;
+    const int rt = tile % su.rtiles, tt = tile / su.rtiles;
     const int row0 = rt * BM, tok0 = tt * BN;
-    // K range of this split in whole super-blocks [jb, je)
-    const int jb = (int)(((int64_t)split * p.nb) / p.ks);
-    const int je = (int)(((int64_t)(split + 1) * p.nb) / p.ks);
     const int h = lane >> 5;
 
     // W row pointers of the lane's two row groups (rows past M clamp to M-1)
@@ -299,30 +321,82 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
     }
 
     // ---- epilogue ----
-    float *out = p.ks > 1 ? p.ws + (int64_t)split * p.P * p.M : p.Y;
+    // A whole tile goes to Y; a part of one to the partial slot, laid out
+    // [token][column] like Y's tile with a row stride of BM.
+    const bool whole = jb == 0 && je == p.nb;
+    float *out = whole ? p.Y + (int64_t)tok0 * p.M + row0
+                       : p.ws + ((int64_t)g * 2 + slot) * (BM * BN);
+    const int ld = whole ? p.M : BM;
+    const int cmax = whole ? p.M - row0 : BM, tmax = whole ? p.P - tok0 : BN;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int col = row0 + 64 * wave + 32 * r + (lane & 31);  // W row = Y column
-        const bool col_ok = col < p.M;
+        const int cl = 64 * wave + 32 * r + (lane & 31);  // W row = Y column
+        const bool col_ok = cl < cmax;
 #pragma unroll
         for (int ti = 0; ti < T; ++ti)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int tok = tok0 + 32 * ti + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (col_ok && tok < p.P) out[(int64_t)tok * p.M + col] = acc[r][ti][v];
+                const int tl = 32 * ti + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (col_ok && tl < tmax) out[(int64_t)tl * ld + cl] = acc[r][ti][v];
             }
     }
 }
 
-// Y[i] = sum over splits of ws[s][i], in split order (one element per thread).
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ ws,
-                                                          float *__restrict__ Y, int64_t n,
-                                                          int ks) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float t = ws[i];
-    for (int s = 1; s < ks; ++s) t += ws[(int64_t)s * n + i];
-    Y[i] = t;
+template <int T>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const SKUnits su) {
+    // buffer `half` holds X columns [256j + 128 half, +128) of the tile's tokens
+    __shared__ __attribute__((aligned(1024))) __bf16 xs[2][32 * T * KS];
+    const int g = blockIdx.x;
+    const int64_t ua = su.begin(g), ub = su.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = (int)(ua / su.nb);
+    int64_t u = ua;
+    while (u < ub) {
+        const int tile = (int)(u / su.nb);
+        const int64_t tb = (int64_t)tile * su.nb;
+        const int jb = (int)(u - tb);
+        const int je = (int)((ub < tb + su.nb ? ub : tb + su.nb) - tb);
+        gemm_segment<T>(p, su, g, tile, jb, je, tile == first_tile ? 0 : 1, xs);
+        u = tb + je;
+    }
+}
+
+// Cut tiles: Y = sum of the contributors' partial tiles, in workgroup order
+// (ascending K).  blockIdx.x + 1 = range boundary b; the tile it falls in is
+// fixed up by the first boundary that cuts it, so whole tiles launch nothing
+// and no tile is done twice.  blockIdx.y: FT tokens of the tile; thread:
+// one column, FT independent loads per contributor.
+constexpr int FT = 8;
+template <int T>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmParams p, const SKUnits su) {
+    constexpr int BN = 32 * T;
+    const int bnd = blockIdx.x + 1;
+    const int64_t ub = su.begin(bnd);
+    const int tile = (int)(ub / su.nb);
+    const int64_t tb = (int64_t)tile * su.nb;
+    if (ub == tb || su.begin(bnd - 1) > tb) return;  // not a cut, or cut by an earlier boundary
+    const int gf = su.owner(tb), gl = su.owner(tb + su.nb - 1);
+    const int rt = tile % su.rtiles, tt = tile / su.rtiles;
+    const int cl = threadIdx.x;  // column of the tile
+    const int col = rt * BM + cl;
+    const int tl0 = blockIdx.y * FT;
+    const int tok0 = tt * BN + tl0;
+    if (col >= p.M || tok0 >= p.P) return;
+    float s[FT];
+#pragma unroll
+    for (int i = 0; i < FT; ++i) s[i] = 0.f;
+    for (int w = gf; w <= gl; ++w) {
+        const int slot = su.begin(w) / su.nb == tile ? 0 : 1;
+        const float *src = p.ws + ((int64_t)w * 2 + slot) * (BM * BN) + (int64_t)tl0 * BM + cl;
+        float v[FT];
+#pragma unroll
+        for (int i = 0; i < FT; ++i) v[i] = src[i * BM];
+#pragma unroll
+        for (int i = 0; i < FT; ++i) s[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < FT; ++i)
+        if (tok0 + i < p.P) p.Y[(int64_t)(tok0 + i) * p.M + col] = s[i];
 }
 
 std::atomic<int> g_override_ks{0};
@@ -332,45 +406,115 @@ int64_t padded_tokens(int64_t P) { return (P + TOK_PAD - 1) / TOK_PAD * TOK_PAD;
 
 }  // namespace
 
-void set_gemm_override(int token_groups, int ks) {
+void set_gemm_override(int token_groups, int workgroups) {
     g_override_t = token_groups;
-    g_override_ks = ks;
+    g_override_ks = workgroups;
 }
 
-// Tile and split choice.  Every workgroup holds a CU to itself (LDS and
-// register file), so the chip runs 256 workgroups at a time; the cost model
-// counts rounds of 256 times the per-workgroup work (super-blocks per split
-// times the measured time of one super-block for the tile width) plus the
-// traffic of the split partials (written once, read once by the reduction),
-// and picks the cheapest (tile width, split count).
+// Tile choice and grid.  Every workgroup holds a CU to itself (LDS and
+// register file), so the grid is one workgroup per CU and the stream-K
+// partition gives each the same number of super-block items.  The cost model
+// per tile width: items per workgroup times the measured time of one item,
+// plus the traffic of the partial tiles (each workgroup writes at most two,
+// the fix-up kernel reads them back) and the fix-up launch.
+namespace {
+int device_cus() {
+    static std::atomic<int> cached{0};
+    int c = cached.load();
+    if (c > 0) return c;
+    int dev = 0;
+    c = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            c = v;
+    }
+    cached = c;
+    return c;
+}
+
+SKUnits sk_units(int64_t M, int64_t K, int64_t P, int t, int G) {
+    SKUnits su;
+    su.nb = (int)(K / 256);
+    su.rtiles = (int)((M + BM - 1) / BM);
+    const int64_t tiles = (int64_t)su.rtiles * ((P + 32 * t - 1) / (32 * t));
+    su.U = tiles * su.nb;
+    su.G = (int)std::max<int64_t>(1, std::min<int64_t>(G, su.U));
+    return su;
+}
+
+// A range boundary falls inside a tile unless every range is whole tiles.
+bool has_split_tiles(const SKUnits &su) {
+    const int64_t tiles = su.U / su.nb;
+    return !(tiles % su.G == 0);
+}
+}  // namespace
+
+// Partial tiles the workgroups write (a range's first and last tile when the
+// range starts or ends inside it), and how many tiles need the fix-up.
+static void split_pieces(const SKUnits &su, int64_t &pieces, int64_t &split_tiles) {
+    pieces = 0;
+    split_tiles = 0;
+    int64_t last_split = -1;
+    for (int g = 0; g < su.G; ++g) {
+        const int64_t ua = (int64_t)g * su.U / su.G, ub = (int64_t)(g + 1) * su.U / su.G;
+        if (ua >= ub) continue;
+        const int64_t t0 = ua / su.nb, t1 = (ub - 1) / su.nb;
+        const bool cut0 = ua % su.nb != 0 || (t0 == t1 && ub % su.nb != 0);
+        const bool cut1 = t1 != t0 && ub % su.nb != 0;
+        if (cut0) {
+            ++pieces;
+            if (t0 != last_split) ++split_tiles, last_split = t0;
+        }
+        if (cut1) {
+            ++pieces;
+            if (t1 != last_split) ++split_tiles, last_split = t1;
+        }
+    }
+}
+
+// Tile width and workgroup count.  Every workgroup holds a CU to itself (LDS
+// and register file).  The cost model takes the longest range (work items
+// times the measured time of one super-block of one tile at that width),
+// plus, when some tile is cut, the partial tiles a workgroup writes (at about
+// 32 GB/s per CU with every CU writing) and the fix-up launch with its
+// traffic (partials read, Y written; about 12 TB/s measured, the partials
+// being still in cache).
 GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P) {
-    const int64_t nb = K / 256;
-    const int ot = g_override_t.load(), oks = g_override_ks.load();
-    GemmLaunch best{1, 4};
+    const int ot = g_override_t.load(), og = g_override_ks.load();
+    const int G = og > 0 ? og : device_cus();
+    GemmLaunch best{G, 4};
     double best_cost = 1e300;
     for (int t : {4, 8}) {
         if (ot != 0 && t != ot) continue;
-        const int64_t tiles = ((M + BM - 1) / BM) * ((P + 32 * t - 1) / (32 * t));
-        const double sb_us = t == 8 ? 6.0 : 3.6;  // one super-block of one tile (measured)
-        for (int64_t ks = 1; ks <= 16 && nb / ks >= 2; ++ks) {
-            if (oks != 0 && ks != std::min<int64_t>(oks, nb)) continue;
-            const int64_t rounds = (tiles * ks + 255) / 256;
-            double cost = rounds * (double)((nb + ks - 1) / ks) * sb_us;
-            if (ks > 1) cost += (double)(2 * ks + 1) * P * M * 4 / 5.0e6;  // bytes / (5 TB/s), in us
-            if (cost < best_cost - 1e-9) {
-                best_cost = cost;
-                best.ks = (int)ks;
-                best.r = t;
-            }
+        const SKUnits su = sk_units(M, K, P, t, G);
+        const double item_us = t == 8 ? 8.4 : 5.0;  // one super-block of one tile (measured)
+        const int64_t per = (su.U + su.G - 1) / su.G;
+        double cost = per * item_us;
+        if (has_split_tiles(su)) {
+            int64_t pieces, split_tiles;
+            split_pieces(su, pieces, split_tiles);
+            const double tile_bytes = (double)BM * 32 * t * 4;
+            cost += (double)(pieces + su.G - 1) / su.G * tile_bytes / 32.0e3 + 3.0 +
+                    (double)(pieces + split_tiles) * tile_bytes / 12.0e6;
+        }
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best.ks = su.G;
+            best.r = t;
         }
     }
-    if (oks > 16 || (oks != 0 && nb / oks < 2)) best.ks = (int)std::min<int64_t>(oks, nb);
     return best;
 }
 
 size_t gemm_partial_floats(const GemmLaunch &L, int64_t M, int64_t P) {
-    const size_t n = L.ks > 1 ? (size_t)L.ks * (size_t)P * (size_t)M : 0;
-    return (n + 63) / 64 * 64;  // keeps the bf16 X section 256-byte aligned
+    (void)M;
+    (void)P;
+    // two partial tiles per workgroup, rounded to 64 floats (keeps the bf16 X
+    // section after it 256-byte aligned)
+    const size_t n = (size_t)L.ks * 2 * BM * 32 * L.r;
+    return (n + 63) / 64 * 64;
 }
 
 size_t gemm_xb_floats(int64_t K, int64_t P) {
@@ -396,7 +540,7 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     p.row_bytes = (K / 256) * kBlockBytes;
     p.ks = L.ks;
     p.ws = ws.partials;
-    // workspace: [split partials][bf16 X, tokens padded]
+    // workspace: [partial tiles][bf16 X, tokens padded]
     __bf16 *xb = reinterpret_cast<__bf16 *>(ws.partials + gemm_partial_floats(L, M, P));
     p.Xb = xb;
     const int64_t n = P * K, n_pad = padded_tokens(P) * K;
@@ -405,19 +549,18 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)cgroups), dim3(256), 0, stream, X, xb, n,
                        n_pad);
     Q4K_HIP(hipGetLastError());
-    const int BN = 32 * L.r;
-    const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((P + BN - 1) / BN), (unsigned)L.ks);
-    if (grid.y > 65535 || grid.z > 65535)
-        return fail(Q4K_EUNSUPPORTED, "gemm: P or split count too large");
-    if (L.r == 8) hipLaunchKernelGGL(gemm_kernel<8>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(256), 0, stream, p);
+    const SKUnits su = sk_units(M, K, P, L.r, L.ks);
+    const int64_t tiles = su.U / su.nb;
+    if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: too many tiles");
+    if (L.r == 8) hipLaunchKernelGGL(gemm_kernel<8>, dim3((unsigned)su.G), dim3(256), 0, stream, p, su);
+    else hipLaunchKernelGGL(gemm_kernel<4>, dim3((unsigned)su.G), dim3(256), 0, stream, p, su);
     Q4K_HIP(hipGetLastError());
-    if (L.ks > 1) {
-        const int64_t m = P * M;
-        const int64_t groups = (m + 255) / 256;
-        if (groups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: output too large");
-        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)groups), dim3(256), 0, stream,
-                           (const float *)ws.partials, Y, m, L.ks);
+    if (has_split_tiles(su)) {  // implies G >= 2: there are G - 1 range boundaries
+        const dim3 fg((unsigned)(su.G - 1), (unsigned)(32 * L.r / FT));
+        if (L.r == 8)
+            hipLaunchKernelGGL(gemm_fixup_kernel<8>, fg, dim3(256), 0, stream, p, su);
+        else
+            hipLaunchKernelGGL(gemm_fixup_kernel<4>, fg, dim3(256), 0, stream, p, su);
         Q4K_HIP(hipGetLastError());
     }
     return Q4K_OK;

@@ -97,7 +97,7 @@ int launch_dequant(const uint8_t *w, float *out, int64_t M, int64_t K, hipStream
 
 // ---------------------------------------------------------------- GEMM
 struct GemmLaunch {
-    int ks;  // K splits across workgroups (split boundaries on whole super-blocks)
+    int ks;  // workgroups of the stream-K grid
     int r;   // 32-token groups per tile (tile = 256 W rows x 32r tokens)
 };
 GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P);
@@ -107,6 +107,6 @@ size_t gemm_xb_floats(int64_t K, int64_t P);
 size_t gemm_counters(int64_t M, int64_t P);
 int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
                 const GemmLaunch &L, const Workspace &ws, hipStream_t stream);
-void set_gemm_override(int token_groups, int ks);
+void set_gemm_override(int token_groups, int workgroups);
 
 }  // namespace q4k

@@ -122,8 +122,8 @@ def test_launch_shape_reports(lib):
         wk, groups = q4k.gemv_config(M, K, 1)
         units = -(-M // 64) * -(-(K // 256) // 4)
         assert wk == 4 and 1 <= groups <= units
-    tt, ks = q4k.gemm_config(5120, 17408, 256)
-    assert tt in (128, 256) and 1 <= ks <= 17408 // 256
+    tt, wg = q4k.gemm_config(5120, 17408, 256)
+    assert tt in (128, 256) and wg >= 1
 
 
 def test_tuning_knobs_validate(lib):
@@ -131,14 +131,14 @@ def test_tuning_knobs_validate(lib):
     assert lib.q4k_tune_gemv(8, 0) == -1
     assert lib.q4k_tune_gemv(4, -1) == -1
     assert lib.q4k_tune_gemm(0, -1) == -1
-    assert lib.q4k_tune_gemm(0, 65) == -1
+    assert lib.q4k_tune_gemm(0, 4097) == -1
     assert lib.q4k_tune_gemm(64, 0) == -1
     q4k.tune_gemm(256, 3)
     assert q4k.gemm_config(17408, 5120, 512) == (256, 3)
     q4k.tune_gemm(128, 0)
     assert q4k.gemm_config(17408, 5120, 512)[0] == 128
-    q4k.tune_gemm(0, 64)
-    assert q4k.gemm_config(17408, 5120, 512)[1] == 20        # capped at K/256 super-blocks
+    q4k.tune_gemm(256, 4096)
+    assert q4k.gemm_config(300, 512, 7) == (256, 4)          # capped at tiles x super-blocks
     q4k.tune_gemv(4, 300)
     assert q4k.gemv_config(17408, 5120) == (4, 300)
     q4k.tune_gemv(0, 5000)

@@ -216,24 +216,25 @@ def _check_gemm(Y, w, X, M, K, rows, toks, what):
         assert c >= COS_MIN, "%s token %d cosine %.9f" % (what, t, c)
 
 
-@pytest.mark.parametrize("tile,ks", [(0, 0), (128, 1), (128, 3), (256, 1), (256, 2)])
+@pytest.mark.parametrize("tile,wg", [(0, 0), (128, 1), (128, 3), (256, 1), (256, 2), (256, 7)])
 @pytest.mark.parametrize("M,K,P", [(300, 512, 1), (300, 512, 7), (128, 256, 128), (129, 768, 130),
                                    (520, 1024, 200), (64, 4096, 33), (257, 2048, 257),
                                    (256, 1280, 128)])
-def test_gemm_small(q4k, M, K, P, tile, ks):
-    """Ragged rows and tokens around both tile widths; one, two, odd and even
-    super-block counts per split (0: automatic)."""
+def test_gemm_small(q4k, M, K, P, tile, wg):
+    """Ragged rows and tokens around both tile widths; stream-K grids of one
+    workgroup (everything in one range), and a few workgroups whose ranges
+    cut tiles at odd super-block offsets (0: automatic)."""
     w, _ = _case(5, M + P, M, K)
     X = synth.activations(5, P, K, first=M)
-    note("gemm %dx%d P=%d tile=%d ks=%d" % (M, K, P, tile, ks))
+    note("gemm %dx%d P=%d tile=%d wg=%d" % (M, K, P, tile, wg))
     try:
-        q4k.tune_gemm(tile, ks)
+        q4k.tune_gemm(tile, wg)
         Y = down(q4k.gemm(up(w), up(X), M=M, K=K))
     finally:
         q4k.tune_gemm(0, 0)
     toks = np.arange(P)
     _check_gemm(Y, w, X, M, K, np.arange(M), toks,
-                "gemm %dx%d P=%d tile=%d ks=%d" % (M, K, P, tile, ks))
+                "gemm %dx%d P=%d tile=%d wg=%d" % (M, K, P, tile, wg))
 
 
 def _sample(n, rng, k=48, tile=128):
@@ -280,11 +281,12 @@ def test_gemm_split_k_variants_agree(q4k):
     rows, toks = _sample(M, rng, 24), _sample(P, rng, 8)
     try:
         outs = []
-        for tt, ks in ((128, 1), (128, 2), (128, 3), (128, 7), (256, 1), (256, 4), (256, 64)):
-            q4k.tune_gemm(tt, ks)
-            note("gemm tile=%d ks=%d" % (tt, ks))
+        for tt, wg in ((128, 1), (128, 37), (128, 256), (128, 511), (256, 1), (256, 5),
+                       (256, 256), (256, 1000)):
+            q4k.tune_gemm(tt, wg)
+            note("gemm tile=%d wg=%d" % (tt, wg))
             Y = down(q4k.gemm(wd, Xd, M=M, K=K))
-            _check_gemm(Y, w, X, M, K, rows, toks, "tile=%d ks=%d" % (tt, ks))
+            _check_gemm(Y, w, X, M, K, rows, toks, "tile=%d wg=%d" % (tt, wg))
             outs.append(Y)
         Y2 = down(q4k.gemm(wd, Xd, M=M, K=K))
         assert np.array_equal(bits(Y2), bits(outs[-1]))          # deterministic
