@@ -177,7 +177,8 @@ def main():
                                "frac_hbm": mlp_bytes[n] / kern[n] / 1e3 / HBM_PEAK_GBS}
                            for n in kern}
         out["gemv_mlp"]["kernel_sum_us"] = gpu_us
-        achieved = mlp_bytes["gate"] / kern["gate"] / 1e3
+        gate_alg = mlp_bytes["gate"] + 4 * (5120 + 17408)  # weights + x + y
+        achieved = gate_alg / kern["gate"] / 1e3
         traffic = None
         if os.path.exists(PROFILE_TRAFFIC):
             with open(PROFILE_TRAFFIC) as f:
@@ -186,10 +187,11 @@ def main():
                 traffic = tr.get("hbm_bytes_per_launch")
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "q4k_gemv on gate 17408x5120 (gemv_kernel<1,1,PLAIN>, one row tile "
-                                     "per workgroup, no reduce launch)",
+                           "kernel": "q4k_gemv on gate 17408x5120 (gemv_kernel<1,1,PLAIN>, one "
+                                     "workgroup per resident slot over contiguous unit ranges, cut "
+                                     "tiles finished in-kernel)",
                            "timing": "HIP events around bursts of back-to-back launches (kernel + gap)",
-                           "algorithmic_bytes_per_launch": mlp_bytes["gate"] + 4 * (5120 + 17408)}
+                           "algorithmic_bytes_per_launch": gate_alg}
         log("MLP GEMVs: step %.2f us wall, kernels %s" % (wall * 1e6, kern))
         del copies
         torch.cuda.empty_cache()
