@@ -8,6 +8,7 @@ dispatch from the FETCH_SIZE / WRITE_SIZE counters, scaled by the reading the
 same counter gives for a plain device copy of known size.
 
     python -m bit_block_quantized_gguf_amd.profiling trace DIR [--kernel SUBSTR] [--grid N]
+    python -m bit_block_quantized_gguf_amd.profiling calls DIR --start SUBSTR [--include SUBSTR]
     python -m bit_block_quantized_gguf_amd.profiling traffic --fetch DIR --write DIR \
         --kernel SUBSTR --grid N --calib-kernel SUBSTR --calib-bytes B \
         --algorithmic-bytes A --source-hash H --out FILE.json
@@ -44,6 +45,51 @@ def dispatches(directory: str, kernel: str = "", grid: int | None = None) -> lis
             rows.append({"name": name, "grid": g,
                          "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
     return rows
+
+
+def calls(directory: str, start: str, include: str = "") -> list[dict]:
+    """Group the dispatches (in time order) into library calls: a call begins
+    at a dispatch whose name contains `start` and takes the following
+    dispatches whose names contain `include` (others are skipped).  Returns,
+    per distinct (grid of the first dispatch, kernel sequence), the number of
+    calls and the median duration of each kernel position and of their sum."""
+    rows = []
+    with open(_csv(directory, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"],
+                         int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0),
+                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    groups: dict = {}
+    cur = None
+    for _, name, grid, ns in rows:
+        if start in name:
+            cur = {"grid": grid, "names": [_short(name)], "ns": [ns]}
+            key = None
+        elif cur is not None and include and include in name:
+            cur["names"].append(_short(name))
+            cur["ns"].append(ns)
+        else:
+            continue
+        # (re)file the call under its current kernel sequence
+        if key is not None:
+            groups[key].remove(cur)
+        key = (cur["grid"], tuple(cur["names"]))
+        groups.setdefault(key, []).append(cur)
+    out = []
+    for (grid, names), cs in groups.items():
+        if not cs:
+            continue
+        med = [statistics.median(c["ns"][i] for c in cs) / 1e3 for i in range(len(names))]
+        out.append({"grid": grid, "kernels": list(names), "calls": len(cs), "median_us": med,
+                    "median_sum_us": statistics.median(sum(c["ns"]) for c in cs) / 1e3})
+    return out
+
+
+def _short(name: str) -> str:
+    """Kernel name without the namespace and the parameter list."""
+    base = name.replace("(anonymous namespace)::", "").replace("q4k::", "").replace("void ", "")
+    return base.split("(")[0]
 
 
 def kernel_stats(directory: str) -> list[dict]:
@@ -94,6 +140,10 @@ def main(argv=None) -> int:
     t.add_argument("dir")
     t.add_argument("--kernel", default="")
     t.add_argument("--grid", type=int)
+    c = sub.add_parser("calls")
+    c.add_argument("dir")
+    c.add_argument("--start", required=True)
+    c.add_argument("--include", default="")
     tr = sub.add_parser("traffic")
     tr.add_argument("--fetch", required=True)
     tr.add_argument("--write", required=True)
@@ -116,6 +166,13 @@ def main(argv=None) -> int:
                 print("filter kernel=%r grid=%s: %d dispatches, mean %.2f us, median %.2f us"
                       % (a.kernel, a.grid, len(ns), statistics.fmean(ns) / 1e3,
                          statistics.median(ns) / 1e3))
+        return 0
+    if a.cmd == "calls":
+        for g in calls(a.dir, a.start, a.include):
+            print("first grid %9d  calls %4d  %s  sum %.1f us" % (
+                g["grid"], g["calls"],
+                "  ".join("%s %.1f us" % (n, u) for n, u in zip(g["kernels"], g["median_us"])),
+                g["median_sum_us"]))
         return 0
     res = traffic(a.fetch, a.write, a.kernel, a.grid, a.calib_kernel, a.calib_bytes)
     res.update({"kernel": a.kernel, "grid": a.grid, "algorithmic_bytes_per_launch":

@@ -68,3 +68,33 @@ def test_dispatch_filter(tmp_path):
         w.writerow(["other", 0, 10, 64])
     rows = profiling.dispatches(str(d), "gemv_kernel", 64)
     assert [r["ns"] for r in rows] == [1000, 3000]
+
+
+def test_calls_group_consecutive_dispatches(tmp_path):
+    """Dispatches are grouped into calls that start at the `start` kernel and
+    take the following `include` kernels; unrelated kernels in between are
+    skipped, and calls are keyed by the first grid and the kernel sequence."""
+    d = tmp_path / "c"
+    d.mkdir()
+    with open(d / "r_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size"])
+        # shape A, two calls (the second out of time order in the file)
+        w.writerow(["void q4k::(anonymous namespace)::to_bf16_kernel(float const*)", 0, 1000, 10])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<4>(x)", 1000, 5000, 7])
+        w.writerow(["copy", 5000, 5100, 3])                              # not included
+        w.writerow(["void q4k::(anonymous namespace)::gemm_fixup_kernel<4>(x)", 5100, 6100, 7])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<4>(x)", 11000, 17000, 7])
+        w.writerow(["void q4k::(anonymous namespace)::to_bf16_kernel(float const*)", 10000, 11000, 10])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_fixup_kernel<4>(x)", 17000, 19000, 7])
+        # shape B, one call without a fix-up
+        w.writerow(["void q4k::(anonymous namespace)::to_bf16_kernel(float const*)", 20000, 22000, 20])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<8>(x)", 22000, 30000, 7])
+    res = {g["grid"]: g for g in profiling.calls(str(d), "to_bf16_kernel", "gemm")}
+    a, b = res[10], res[20]
+    assert a["kernels"] == ["to_bf16_kernel", "gemm_kernel<4>", "gemm_fixup_kernel<4>"]
+    assert a["calls"] == 2
+    assert a["median_us"] == [1.0, 5.0, 1.5]
+    assert a["median_sum_us"] == 7.5
+    assert b["kernels"] == ["to_bf16_kernel", "gemm_kernel<8>"] and b["calls"] == 1
+    assert b["median_sum_us"] == 10.0
