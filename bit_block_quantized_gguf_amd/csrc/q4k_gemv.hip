@@ -19,8 +19,10 @@
 //    as an SGPR operand.  The wave index goes through readfirstlane so the
 //    compiler can prove those addresses wave-uniform.
 //  * Per weight the VALU work is one FMA taking the nibble as a binary16
-//    operand (v_fma_mix_f32), plus an AND and two byte permutes per four
-//    weights.  Per block the scale/min algebra is
+//    operand (v_fma_mix_f32), plus four ANDs and a shift per eight weights:
+//    one AND places two nibbles (of bytes 0 and 2, or of bytes 1 and 3 after
+//    the shift) straight into the two 16-bit halves of a dword.  Per block
+//    the scale/min algebra is
 //       y += d * sum_j sc_j * T_j  -  dmin * sum_j m_j * X_j
 //    with T_j = sum(q*x) and X_j = sum(x) over sub-block j; high nibbles are
 //    converted in place (16*q) and their partial sum carries the exact factor
@@ -70,10 +72,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-// Bytes 2k, 2k+1 of v (k = 0, 1) as the two 16-bit halves of a dword.
-__device__ __forceinline__ half2v byte_pair(uint32_t v, int k) {
-    return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, v, k ? 0x0C030C02u : 0x0C010C00u));
-}
 
 // acc[n] += sum over the block of w * x_n (factored form).
 //
@@ -114,24 +112,28 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
                 for (int c = 0; c < C; ++c) cl[n][c] = ch[n][c] = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
+                // Bytes 0 and 2 of the word sit in the low byte of each 16-bit
+                // half, bytes 1 and 3 after a shift by 8: one AND per nibble
+                // set places two nibbles straight into the halves (four ANDs
+                // and a shift per eight weights).
                 const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-                const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
-                const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
+                const uint32_t v8 = v >> 8;
+                const half2v l02 = __builtin_bit_cast(half2v, and_mask(v, 0x000F000Fu));   // q0, q2
+                const half2v l13 = __builtin_bit_cast(half2v, and_mask(v8, 0x000F000Fu));  // q1, q3
+                const half2v h02 = __builtin_bit_cast(half2v, and_mask(v, 0x00F000F0u));   // 16 q
+                const half2v h13 = __builtin_bit_cast(half2v, and_mask(v8, 0x00F000F0u));
                 cfloat *xl = as_const(xblk + 64 * g + 4 * i);
                 cfloat *xh = as_const(xblk + 64 * g + 32 + 4 * i);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const half2v ql = byte_pair(lo, k), qh = byte_pair(hi, k);
+                for (int e = 0; e < 4; ++e) {  // byte e of the word
+                    const int c = (4 * i + e) % C;
+                    const half2v ql = (e & 1) ? l13 : l02, qh = (e & 1) ? h13 : h02;
+                    const float wl = (e & 2) ? (float)ql.y : (float)ql.x;
+                    const float wh = (e & 2) ? (float)qh.y : (float)qh.x;
 #pragma unroll
-                    for (int e2 = 0; e2 < 2; ++e2) {
-                        const int c = (4 * i + 2 * k + e2) % C;
-                        const float wl = e2 ? (float)ql.y : (float)ql.x;
-                        const float wh = e2 ? (float)qh.y : (float)qh.x;
-#pragma unroll
-                        for (int n = 0; n < NV; ++n) {
-                            cl[n][c] = fmaf(wl, xl[n * xs + 2 * k + e2], cl[n][c]);
-                            ch[n][c] = fmaf(wh, xh[n * xs + 2 * k + e2], ch[n][c]);
-                        }
+                    for (int n = 0; n < NV; ++n) {
+                        cl[n][c] = fmaf(wl, xl[n * xs + e], cl[n][c]);
+                        ch[n][c] = fmaf(wh, xh[n * xs + e], ch[n][c]);
                     }
                 }
             }
