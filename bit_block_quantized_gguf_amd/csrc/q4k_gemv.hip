@@ -380,11 +380,14 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         const uint8_t *b1 = NMAT == 2 ? p.w1 + base : b0;
 #pragma unroll
         for (int i = 0; i < CH_THREAD; ++i) {
-            const int cr = crow[i], co = coff[i];
+            // chunks past the row's last block re-read the unit's first chunk
+            // (in range; blocks past the row end are never computed), so the
+            // loads need no branches
+            const int cr = crow[i], co = coff[i] < valid ? coff[i] : 0;
             const int r = NMAT == 2 ? (cr & 31) : cr;
             const uint32_t off = (uint32_t)min(r, rmax) * (uint32_t)p.row_bytes + (uint32_t)co;
             const uint8_t *src = (NMAT == 2 && cr >= 32) ? b1 : b0;
-            if (co < valid) reg[i] = ldg16(src + off);
+            reg[i] = ldg16(src + off);
         }
     };
     auto commit = [&]() {
