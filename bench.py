@@ -16,7 +16,8 @@ Also measured and reported in the same line:
     of Q4_K) replayed as one hipGraph per token: us/token vs the weight-read
     roofline 14,412,349,440 B / 8 TB/s;
   * prefill_gemm: bf16-MFMA GEMM for both MLP shapes at P = 256, 512, 1024
-    (TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak);
+    (TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak), and prefill_gemm_short
+    for short prompts, P = 16, 22, 27, 64;
   * gemv_batch: N = 1, 2, 4, 8, 16 vectors on the 17408x5120 weight;
   * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound);
   * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
@@ -43,6 +44,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 QK, BB = 256, 144
 METRIC = "Q4_K GEMV HBM GB/s (% peak); decode-stack µs/token; prefill GEMM TFLOP/s"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_mlp_17408x5120_traffic.json")
+SHORT_P = (16, 22, 27, 64)  # short-prompt prefill lengths timed next to the prefill configs
 GEMV_SOURCES = ["bit_block_quantized_gguf_amd/csrc/q4k_gemv.hip",
                 "bit_block_quantized_gguf_amd/csrc/q4k_device.hpp"]
 
@@ -256,7 +258,8 @@ def main():
         res = []
         for si, (M, K) in enumerate(wl.PREFILL_SHAPES):
             wd = upload(synth.q4k_weight(synth.key(5, si), M, K))
-            for P in wl.PREFILL_P:
+            # the prefill configs, then short prompts (22 and 27 tokens among them)
+            for P in tuple(wl.PREFILL_P) + SHORT_P:
                 X = upload(synth.activations(5, P, K))
                 Y = torch.empty((P, M), device=dev)
                 for _ in range(3):
@@ -277,7 +280,8 @@ def main():
                             "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
                             "tile_tokens_workgroups": list(q4k.gemm_config(M, K, P))})
                 del X, Y
-        out["prefill_gemm"] = res
+        out["prefill_gemm"] = [r for r in res if r["P"] not in SHORT_P]
+        out["prefill_gemm_short"] = [r for r in res if r["P"] in SHORT_P]
         log("gemm: %s" % [(r["M"], r["P"], round(r["TFLOPs"], 1)) for r in res])
         torch.cuda.empty_cache()
 

@@ -232,7 +232,7 @@ def tune_gemv(waves_per_group: int = 0, workgroups: int = 0) -> None:
 
 
 def tune_gemm(tile_tokens: int = 0, workgroups: int = 0) -> None:
-    """Force the GEMM tile width (0, 128 or 256 tokens) and workgroup count (0: automatic)."""
+    """Force the GEMM tile width (0, 32, 64, 128 or 256 tokens) and workgroup count (0: automatic)."""
     check(load().q4k_tune_gemm(tile_tokens, workgroups))
 
 

@@ -269,8 +269,9 @@ int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
 
 int q4k_tune_gemm(int32_t tile_tokens, int32_t workgroups) {
     clear_error();
-    if (tile_tokens != 0 && tile_tokens != 128 && tile_tokens != 256)
-        return fail(Q4K_EINVAL, "tile_tokens must be 0, 128 or 256");
+    if (tile_tokens != 0 && tile_tokens != 32 && tile_tokens != 64 && tile_tokens != 128 &&
+        tile_tokens != 256)
+        return fail(Q4K_EINVAL, "tile_tokens must be 0, 32, 64, 128 or 256");
     if (workgroups < 0 || workgroups > 4096)
         return fail(Q4K_EINVAL, "workgroups must be in 0..4096");
     set_gemm_override(tile_tokens / 32, workgroups);

@@ -10,7 +10,10 @@
 //    into a workspace whose token count is padded to the tile with zeros, so
 //    the main loop moves half the bytes, spends no VALU on conversion and
 //    needs no token clamping.
-//  * Workgroup tile: 256 W rows x (32 * T) tokens, four waves, one workgroup
+//  * Workgroup tile: 256 W rows x (32 * T) tokens, T = 1, 2, 4 or 8 (the
+//    narrow tiles serve short prompts: the dequantisation of a super-block
+//    costs the same at every width, the MFMA work shrinks with it), four
+//    waves, one workgroup
 //    per CU.  Wave w owns W rows 64w .. 64w+63 (two 32-row groups) for all
 //    tokens of the tile, so every W weight is dequantised exactly once per
 //    tile and every X fragment read from LDS feeds two MFMAs.  The 32 * T
@@ -62,7 +65,13 @@ typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int BM = 256;        // W rows per tile
 constexpr int KS = 128;        // columns per step (half a super-block)
-constexpr int TOK_PAD = 256;   // token padding of the bf16 X copy (the wider tile)
+constexpr int TOK_PAD = 256;   // token padding of the bf16 X copy (the widest tile)
+#ifndef GEMM_T1_US
+#define GEMM_T1_US 2.45
+#endif
+#ifndef GEMM_T2_US
+#define GEMM_T2_US 3.45
+#endif
 
 // (lo, hi) -> two bf16 (RNE) in one dword, lo in the low half: v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -486,10 +495,12 @@ GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P) {
     const int G = og > 0 ? og : device_cus();
     GemmLaunch best{G, 4};
     double best_cost = 1e300;
-    for (int t : {4, 8}) {
+    for (int t : {1, 2, 4, 8}) {
         if (ot != 0 && t != ot) continue;
         const SKUnits su = sk_units(M, K, P, t, G);
-        const double item_us = t == 8 ? 8.4 : 5.0;  // one super-block of one tile (measured)
+        // one super-block of one tile (measured): the dequantisation costs the
+        // same at every width, the MFMA work grows with it
+        const double item_us = t == 8 ? 8.4 : t == 4 ? 5.0 : t == 2 ? GEMM_T2_US : GEMM_T1_US;
         const int64_t per = (su.U + su.G - 1) / su.G;
         double cost = per * item_us;
         if (has_split_tiles(su)) {
@@ -552,15 +563,23 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     const SKUnits su = sk_units(M, K, P, L.r, L.ks);
     const int64_t tiles = su.U / su.nb;
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: too many tiles");
-    if (L.r == 8) hipLaunchKernelGGL(gemm_kernel<8>, dim3((unsigned)su.G), dim3(256), 0, stream, p, su);
-    else hipLaunchKernelGGL(gemm_kernel<4>, dim3((unsigned)su.G), dim3(256), 0, stream, p, su);
+    const dim3 gg((unsigned)su.G);
+    switch (L.r) {
+        case 8: hipLaunchKernelGGL(gemm_kernel<8>, gg, dim3(256), 0, stream, p, su); break;
+        case 4: hipLaunchKernelGGL(gemm_kernel<4>, gg, dim3(256), 0, stream, p, su); break;
+        case 2: hipLaunchKernelGGL(gemm_kernel<2>, gg, dim3(256), 0, stream, p, su); break;
+        case 1: hipLaunchKernelGGL(gemm_kernel<1>, gg, dim3(256), 0, stream, p, su); break;
+        default: return fail(Q4K_EINVAL, "gemm: tile of %d token groups", L.r);
+    }
     Q4K_HIP(hipGetLastError());
     if (has_split_tiles(su)) {  // implies G >= 2: there are G - 1 range boundaries
         const dim3 fg((unsigned)(su.G - 1), (unsigned)(32 * L.r / FT));
-        if (L.r == 8)
-            hipLaunchKernelGGL(gemm_fixup_kernel<8>, fg, dim3(256), 0, stream, p, su);
-        else
-            hipLaunchKernelGGL(gemm_fixup_kernel<4>, fg, dim3(256), 0, stream, p, su);
+        switch (L.r) {
+            case 8: hipLaunchKernelGGL(gemm_fixup_kernel<8>, fg, dim3(256), 0, stream, p, su); break;
+            case 4: hipLaunchKernelGGL(gemm_fixup_kernel<4>, fg, dim3(256), 0, stream, p, su); break;
+            case 2: hipLaunchKernelGGL(gemm_fixup_kernel<2>, fg, dim3(256), 0, stream, p, su); break;
+            default: hipLaunchKernelGGL(gemm_fixup_kernel<1>, fg, dim3(256), 0, stream, p, su); break;
+        }
         Q4K_HIP(hipGetLastError());
     }
     return Q4K_OK;

@@ -204,14 +204,14 @@ void q4k_decode_stack_destroy(q4k_stack *s);
 int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
                     int32_t *workgroups);
 
-/* Tile width (tokens per workgroup tile: 128 or 256) and workgroup count
+/* Tile width (tokens per workgroup tile: 32, 64, 128 or 256) and workgroup count
  * (the stream-K partition of the tile x super-block work) that q4k_gemm picks
  * for a shape. */
 int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32_t *workgroups);
 
 /* Force the GEMV workgroup count (workgroups in 1..2^20, capped at the
  * number of work units; waves_per_group must be 0 or 4), or the GEMM tile
- * width (tile_tokens 0, 128 or 256) and workgroup count (0..4096, capped at
+ * width (tile_tokens 0, 32, 64, 128 or 256) and workgroup count (0..4096, capped at
  * the number of tile x super-block work items); 0 restores the default of
  * that knob.  Process-wide and not synchronised with calls in flight: meant
  * for benchmark sweeps. */

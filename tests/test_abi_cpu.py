@@ -123,7 +123,7 @@ def test_launch_shape_reports(lib):
         units = -(-M // 64) * -(-(K // 256) // 4)
         assert wk == 4 and 1 <= groups <= units
     tt, wg = q4k.gemm_config(5120, 17408, 256)
-    assert tt in (128, 256) and wg >= 1
+    assert tt in (32, 64, 128, 256) and wg >= 1
 
 
 def test_tuning_knobs_validate(lib):
@@ -132,7 +132,11 @@ def test_tuning_knobs_validate(lib):
     assert lib.q4k_tune_gemv(4, -1) == -1
     assert lib.q4k_tune_gemm(0, -1) == -1
     assert lib.q4k_tune_gemm(0, 4097) == -1
-    assert lib.q4k_tune_gemm(64, 0) == -1
+    assert lib.q4k_tune_gemm(96, 0) == -1
+    q4k.tune_gemm(32, 0)
+    assert q4k.gemm_config(17408, 5120, 22)[0] == 32
+    q4k.tune_gemm(64, 0)
+    assert q4k.gemm_config(17408, 5120, 22)[0] == 64
     q4k.tune_gemm(256, 3)
     assert q4k.gemm_config(17408, 5120, 512) == (256, 3)
     q4k.tune_gemm(128, 0)

@@ -216,7 +216,8 @@ def _check_gemm(Y, w, X, M, K, rows, toks, what):
         assert c >= COS_MIN, "%s token %d cosine %.9f" % (what, t, c)
 
 
-@pytest.mark.parametrize("tile,wg", [(0, 0), (128, 1), (128, 3), (256, 1), (256, 2), (256, 7)])
+@pytest.mark.parametrize("tile,wg", [(0, 0), (32, 1), (32, 5), (64, 2), (64, 9), (128, 1), (128, 3),
+                                     (256, 1), (256, 2), (256, 7)])
 @pytest.mark.parametrize("M,K,P", [(300, 512, 1), (300, 512, 7), (128, 256, 128), (129, 768, 130),
                                    (520, 1024, 200), (64, 4096, 33), (257, 2048, 257),
                                    (256, 1280, 128)])
@@ -259,6 +260,22 @@ def test_gemm_prefill_sampled(q4k, shape, P):
     _check_gemm(Y, w, X, M, K, rows, toks, "prefill %dx%d P=%d" % (M, K, P))
 
 
+@pytest.mark.parametrize("P", [1, 16, 22, 27, 64])
+def test_gemm_short_prompt_sampled(q4k, P):
+    """Short prompts (the 22- and 27-token prompts among them) on the MLP
+    gate shape: narrow token tiles, every CU busy through stream-K, sampled
+    rows and every token."""
+    M, K = wl.PREFILL_SHAPES[0]
+    w = synth.q4k_weight(synth.key(5, 0), M, K)
+    X = synth.activations(5, P, K)
+    note("gemm short prompt %dx%d P=%d (tile %d)" % (M, K, P, q4k.gemm_config(M, K, P)[0]))
+    Y = down(q4k.gemm(up(w), up(X), M=M, K=K))
+    assert np.all(np.isfinite(Y))
+    rng = np.random.default_rng(P + 3)
+    rows = _sample(M, rng, 40)
+    _check_gemm(Y, w, X, M, K, rows, np.arange(P), "short prompt P=%d" % P)
+
+
 def test_gemm_bf16_exact_inputs(q4k):
     """E7-tiled weights (small integers) and x with <= 8 significant bits are
     exact in bf16, so only f32 accumulation error remains vs the exact sum."""
@@ -281,8 +298,8 @@ def test_gemm_split_k_variants_agree(q4k):
     rows, toks = _sample(M, rng, 24), _sample(P, rng, 8)
     try:
         outs = []
-        for tt, wg in ((128, 1), (128, 37), (128, 256), (128, 511), (256, 1), (256, 5),
-                       (256, 256), (256, 1000)):
+        for tt, wg in ((32, 1), (32, 256), (32, 1000), (64, 77), (64, 256), (128, 1), (128, 37),
+                       (128, 256), (128, 511), (256, 1), (256, 5), (256, 256), (256, 1000)):
             q4k.tune_gemm(tt, wg)
             note("gemm tile=%d wg=%d" % (tt, wg))
             Y = down(q4k.gemm(wd, Xd, M=M, K=K))
