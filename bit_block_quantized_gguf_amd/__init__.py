@@ -28,7 +28,8 @@ BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS = range(7)
 
 # Every symbol include/q4k.h declares (checked by the CPU test suite).
 EXPORTS = (
-    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
+    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_mlp", "q4k_gemv_batch",
+    "q4k_gemm",
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
     "q4k_tune_gemv", "q4k_tune_gemm", "q4k_release_workspaces",
@@ -82,6 +83,7 @@ def load(path: str | None = None):
     L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
     L.q4k_gemv_batch.argtypes = [p, p, p, i64, i64, i64, p]
     L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p]
+    L.q4k_mlp.argtypes = [p, p, p, i64, i64, p, p, ctypes.c_float, p, p, p, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
     L.q4k_decode_stack.argtypes = [p, p, p, p]
     L.q4k_decode_stack_buffer.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(i64)]
@@ -178,6 +180,37 @@ def gemv(w, x, y=None, M: int | None = None, K: int | None = None):
         y = torch.empty(M, dtype=torch.float32, device=w.device)
     _dev_tensor(y, torch.float32, "y")
     check(load().q4k_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    return y
+
+
+def mlp(w_gate, w_up, w_down, x, norm_w=None, eps: float = 1e-6, resid=None, y=None, act=None,
+        hidden: int | None = None, inter: int | None = None):
+    """y = resid + W_down (silu(W_gate n) * (W_up n)), n = x / rms(x) * (1 + norm_w).
+
+    w_gate, w_up: [inter, hidden/256*144] uint8; w_down: [hidden, inter/256*144].
+    norm_w and resid may be None (gain 1, no residual); act, if given, receives
+    the activation a = silu(W_gate n) * (W_up n)."""
+    torch = _torch()
+    if hidden is None:
+        inter, hidden = weight_shape(w_gate)
+    _weights(w_gate, inter, hidden)
+    _weights(w_up, inter, hidden)
+    _weights(w_down, hidden, inter)
+    _dev_tensor(x, torch.float32, "x")
+    if x.numel() != hidden:
+        raise ValueError("x must have hidden=%d elements" % hidden)
+    for name, v, n in (("norm_w", norm_w, hidden), ("resid", resid, hidden), ("act", act, inter)):
+        if v is not None:
+            _dev_tensor(v, torch.float32, name)
+            if v.numel() != n:
+                raise ValueError("%s must have %d elements" % (name, n))
+    if y is None:
+        y = torch.empty(hidden, dtype=torch.float32, device=x.device)
+    _dev_tensor(y, torch.float32, "y")
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    check(load().q4k_mlp(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), hidden, inter,
+                         x.data_ptr(), ptr(norm_w), float(eps), ptr(resid), y.data_ptr(),
+                         ptr(act), _stream()))
     return y
 
 

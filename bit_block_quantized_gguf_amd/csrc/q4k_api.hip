@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <string>
@@ -244,6 +246,76 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
                              gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P),
                              gemm_counters(M, P), &ws));
     return launch_gemm((const uint8_t *)w, X, Y, M, K, P, L, ws, (hipStream_t)stream);
+}
+
+int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hidden,
+            int64_t inter, const float *x, const float *norm_w, float eps, const float *resid,
+            float *y, float *act, void *stream) {
+    clear_error();
+    Q4K_TRY(check_mk(inter, hidden));  // gate and up: inter x hidden
+    Q4K_TRY(check_mk(hidden, inter));  // down: hidden x inter
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(Q4K_EINVAL, "eps must be finite and >= 0");
+    Q4K_TRY(check_ptr(w_gate, "w_gate"));
+    Q4K_TRY(check_ptr(w_up, "w_up"));
+    Q4K_TRY(check_ptr(w_down, "w_down"));
+    Q4K_TRY(check_ptr(x, "x"));
+    Q4K_TRY(check_ptr(y, "y"));
+    if (act) Q4K_TRY(check_ptr(act, "act"));
+    Q4K_TRY(check_device());
+    const hipStream_t st = (hipStream_t)stream;
+    const int epi_down = resid ? EPI_RESID : EPI_PLAIN;
+    const GemvLaunch Lg = choose_gemv_launch(inter, hidden, 1, 2, EPI_SWIGLU);
+    const GemvLaunch Ld = choose_gemv_launch(hidden, inter, 1, 1, epi_down);
+    auto round64 = [](size_t n) { return (n + 63) / 64 * 64; };
+    // workspace: [GEMV partials][x * (1 + w)][sums of squares of x][activation]
+    const size_t off_xg = round64(std::max(gemv_partial_floats(Lg, inter, 1, 2),
+                                           gemv_partial_floats(Ld, hidden, 1, 1)));
+    const size_t off_sq = off_xg + round64((size_t)hidden);
+    const size_t off_act = off_sq + round64((size_t)((hidden + 31) / 32));
+    const size_t total = off_act + (act ? 0 : round64((size_t)inter));
+    Workspace ws;
+    Q4K_TRY(stream_workspace(st, total, std::max(gemv_counters(inter), gemv_counters(hidden)),
+                             &ws));
+    float *xg = ws.partials + off_xg, *sq = ws.partials + off_sq;
+    float *a = act ? act : ws.partials + off_act;
+    Q4K_TRY(launch_norm_gain(x, norm_w, hidden, xg, sq, st));
+    // a = silu(W_gate n) * (W_up n), n = x / rms(x) * (1 + w): the gain goes on
+    // the input, the 1/rms on the outputs
+    GemvParams p = {};
+    p.w0 = (const uint8_t *)w_gate;
+    p.w1 = (const uint8_t *)w_up;
+    p.x = norm_w ? xg : x;
+    p.x_stride = hidden;
+    p.y = a;
+    p.y_stride = inter;
+    p.M = (int32_t)inter;
+    p.K = (int32_t)hidden;
+    p.nb = (int32_t)(hidden / 256);
+    p.row_bytes = (hidden / 256) * 144;
+    p.ks = Lg.ks;
+    p.ws = ws.partials;
+    p.cnt = ws.counters;
+    p.in_sq = sq;
+    p.in_sq_n = (int32_t)((hidden + 31) / 32);
+    p.in_len = (int32_t)hidden;
+    p.eps = eps;
+    Q4K_TRY(launch_gemv(p, 1, 2, EPI_SWIGLU, Lg, st));
+    // y = resid + W_down a (the activation is not normalised)
+    GemvParams q = {};
+    q.w0 = (const uint8_t *)w_down;
+    q.x = a;
+    q.x_stride = inter;
+    q.y = y;
+    q.y_stride = hidden;
+    q.M = (int32_t)hidden;
+    q.K = (int32_t)inter;
+    q.nb = (int32_t)(inter / 256);
+    q.row_bytes = (inter / 256) * 144;
+    q.ks = Ld.ks;
+    q.ws = ws.partials;
+    q.cnt = ws.counters;
+    q.resid = resid;
+    return launch_gemv(q, 1, 1, epi_down, Ld, st);
 }
 
 void q4k_release_workspaces(void) {

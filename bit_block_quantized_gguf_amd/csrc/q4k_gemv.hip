@@ -200,6 +200,7 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
 // Up to 1024 granules (K <= 32768) every lane issues its loads before adding
 // them (in the same order as the plain loop), so the latency is paid once.
 __device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
+    if (p.in_sq == nullptr) return 1.f;  // input taken as it is (no normalisation)
     float ss = 0.f;
     if (p.in_sq_n <= 16 * 64) {
         float v[16];
@@ -240,7 +241,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
             ok = lane < 32 && row < p.M;
             const float g = mine, v = other;
             val = g / (1.0f + expf(-g)) * v;
-            if (ok) {
+            if (ok && p.y_g) {
                 p.y_g[row] = g;
                 p.y_v[row] = v;
             }
@@ -252,6 +253,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
             else val = fmaf(tot[0], inv, p.resid[rowc]);
         }
         if (ok) p.y[row] = val;
+        if (!p.out_sq) return;
         // sums of squares per 32 output rows (lanes 0..31 and 32..63)
         float sq = ok ? val * val : 0.f;
         sq += __shfl_xor(sq, 16);
@@ -476,6 +478,25 @@ __global__ __launch_bounds__(64) void sumsq_kernel(const float *__restrict__ v, 
     if ((threadIdx.x & 31) == 0 && granule * 32 < n) out[granule] = s;
 }
 
+// xg[i] = x[i] * (1 + w[i]) (w null: xg not written) and the sums of squares
+// of x per 32 elements, one element per thread.
+__global__ __launch_bounds__(64) void norm_gain_kernel(const float *__restrict__ x,
+                                                       const float *__restrict__ w, int64_t n,
+                                                       float *__restrict__ xg,
+                                                       float *__restrict__ sq) {
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    const float a = i < n ? x[i] : 0.f;
+    if (w && i < n) xg[i] = a * (1.0f + w[i]);
+    float s = a * a;
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    const int64_t granule = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 5);
+    if ((threadIdx.x & 31) == 0 && granule * 32 < n) sq[granule] = s;
+}
+
 std::atomic<int> g_override_groups{0};
 
 // Resident workgroups of each kernel instance on a device (occupancy queries
@@ -595,6 +616,15 @@ int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch
     if (nmat == 1 && epi == EPI_RESID) return launch_t<1, 1, EPI_RESID>(p, L, stream);
     if (nmat == 2 && epi == EPI_SWIGLU) return launch_t<1, 2, EPI_SWIGLU>(p, L, stream);
     return fail(Q4K_EINVAL, "unsupported GEMV variant");
+}
+
+int launch_norm_gain(const float *x, const float *w, int64_t n, float *xg, float *sq,
+                     hipStream_t stream) {
+    const unsigned blocks = (unsigned)((n + 63) / 64);
+    if (!blocks) return Q4K_OK;
+    hipLaunchKernelGGL(norm_gain_kernel, dim3(blocks), dim3(64), 0, stream, x, w, n, xg, sq);
+    Q4K_HIP(hipGetLastError());
+    return Q4K_OK;
 }
 
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream) {

@@ -54,18 +54,19 @@ struct GemvParams {
     int64_t x_stride;
     float *y;               // [nv][M], vector stride y_stride floats
     int64_t y_stride;
-    float *y_g;             // EPI_SWIGLU: scaled gate output [M]
-    float *y_v;             // EPI_SWIGLU: scaled up output [M]
+    float *y_g;             // EPI_SWIGLU: scaled gate output [M] (null: not written)
+    float *y_v;             // EPI_SWIGLU: scaled up output [M] (null: not written)
     int32_t M, K, nb;       // nb = K / 256
     int64_t row_bytes;      // nb * 144
     int32_t ks;             // unused by the GEMV (the launch carries the grid)
     float *ws;              // partials of tiles split between workgroups [groups][2][nv][64]
     unsigned *cnt;          // per-tile arrival counters of split tiles (zero between launches)
     const float *in_sq;     // EPI_SCALE/RESID/SWIGLU: per-32-element sums of squares of x
+                            // (null: no 1/rms scaling)
     int32_t in_sq_n;        // number of partials to add (ceil(K/32))
     int32_t in_len;         // divisor of the mean (K)
     const float *resid;     // EPI_RESID: residual [M]
-    float *out_sq;          // EPI != PLAIN: per-32-row sums of squares of y
+    float *out_sq;          // EPI != PLAIN: per-32-row sums of squares of y (null: not written)
     float eps;
 };
 
@@ -88,6 +89,11 @@ int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch
 
 // Per-32-element sums of squares of v[0..n) (used to seed the stack).
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
+
+// xg = x * (1 + w) elementwise (skipped when w is null) and the per-32-element
+// sums of squares of x (the RMS of the un-gained input).
+int launch_norm_gain(const float *x, const float *w, int64_t n, float *xg, float *sq,
+                     hipStream_t stream);
 
 // Tuning override for benchmarks: workgroup count (0 = occupancy-based).
 void set_gemv_override(int groups);

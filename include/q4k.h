@@ -96,6 +96,29 @@ int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
 int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
 
 /*
+ * MLP block of one token (the model's SwiGLU feed-forward with its RMSNorm in
+ * the (1 + w) form, "Qwen3.6-27B on Apple M3 Pro — the llama.cpp parity bar",
+ * model description and the fak-native status list; the gate/up/down matmuls
+ * are the decode GEMVs of "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §2):
+ *   n = x / sqrt(mean(x^2) + eps) * (1 + norm_w)     (norm_w NULL: gain 1)
+ *   a = silu(W_gate n) * (W_up n),  silu(g) = g / (1 + e^-g)
+ *   y = resid + W_down a                              (resid NULL: 0)
+ * w_gate, w_up: Q4_K [inter][hidden]; w_down: Q4_K [hidden][inter]; hidden and
+ * inter positive multiples of 256.  x, norm_w, resid: f32 [hidden]; y: f32
+ * [hidden]; act: optional f32 [inter] that receives a (NULL: kept in the
+ * library's workspace).  Two GEMV launches (gate and up fused into one pass
+ * with the SwiGLU in its epilogue, then down with the residual add) after a
+ * small prologue that applies the gain.  y may alias x or resid (the down
+ * pass runs after gate|up has read x); act must not alias the other vectors.
+ * Each GEMV meets the q4k_gemv bound on its own inputs.  Errors:
+ * Q4K_ESHAPE for bad dims, Q4K_EINVAL for NULL w/x/y or eps < 0 or not
+ * finite, Q4K_EALIGN for w, x, y, act not 16-byte aligned.
+ */
+int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hidden,
+            int64_t inter, const float *x, const float *norm_w, float eps, const float *resid,
+            float *y, float *act, void *stream);
+
+/*
  * N-vector GEMV in one launch, weights read once:
  *   Y[n][i] = sum_k w_ik * X[n][k],  X f32 [N][K], Y f32 [N][M].
  * The batched witness of "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4b,

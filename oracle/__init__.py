@@ -70,6 +70,9 @@ def _load():
         L.oracle_rms.argtypes = [_p, _i64, ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
         L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_mlp.restype = ctypes.c_int
+        L.oracle_mlp.argtypes = [_p, _p, _p, _i64, _i64, _p, _p, ctypes.c_double, _p,
+                                 _p, _p, _p, _p, _p, _p, _p]
         L.oracle_stack.restype = ctypes.c_int
         L.oracle_stack.argtypes = [_p, _p, _p, ctypes.c_int32, _i64, ctypes.c_double, _p, _p, _p]
         L.oracle_set_threads.restype = None
@@ -205,6 +208,25 @@ def rms(v, eps: float = RMS_EPS) -> float:
 
 def silu(g: float) -> float:
     return float(_load().oracle_silu(float(g)))
+
+
+def mlp(wg, wu, wd, hidden: int, inter: int, x, norm_w=None, eps: float = RMS_EPS,
+        resid=None) -> dict:
+    """One MLP block (see q4k_oracle.c): returns g, u, a [inter], y [hidden]
+    and the sums of |w x| Sg, Su [inter], Sd [hidden], all float64."""
+    arrs = [_u8(wg), _u8(wu), _u8(wd)]
+    x = _f32(x)
+    nw = _f32(norm_w) if norm_w is not None else None
+    r = _f32(resid) if resid is not None else None
+    assert x.size == hidden and (nw is None or nw.size == hidden) and (r is None or r.size == hidden)
+    out = {k: np.empty(inter, np.float64) for k in ("g", "u", "a", "Sg", "Su")}
+    out.update({k: np.empty(hidden, np.float64) for k in ("y", "Sd")})
+    _check(_load().oracle_mlp(arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data,
+                              hidden, inter, x.ctypes.data,
+                              nw.ctypes.data if nw is not None else None, float(eps),
+                              r.ctypes.data if r is not None else None,
+                              *[out[k].ctypes.data for k in ("g", "u", "a", "y", "Sg", "Su", "Sd")]))
+    return out
 
 
 def stack(mats, shapes, n_layers: int, hidden: int, h0, eps: float = RMS_EPS,

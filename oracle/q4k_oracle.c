@@ -256,6 +256,51 @@ static int gemv_rmsn(const uint8_t *w, int64_t M, int64_t K, const double *v, do
     return rc;
 }
 
+/* One MLP block of a token: the model's SwiGLU feed-forward with its RMSNorm
+ * in the (1 + w) form ("Qwen3.6-27B on Apple M3 Pro — the llama.cpp parity
+ * bar": the model description lists hidden 5120, intermediate 17408 with
+ * SwiGLU and rms_norm_eps 1e-6; the fak-native status list names the
+ * (1 + w) RMSNorm):
+ *   n = x / rms(x) * (1 + nw)          (nw NULL: gain 1)
+ *   g = W_gate n,  u = W_up n,  a = silu(g) * u
+ *   y = r + W_down a                   (r NULL: no residual)
+ * Everything in double.  Any of the outputs may be NULL; Sg, Su, Sd are the
+ * sums of |w_ik n_k| (|w_ik a_k| for down) of the three matmuls. */
+int oracle_mlp(const uint8_t *wg, const uint8_t *wu, const uint8_t *wd, int64_t hidden,
+               int64_t inter, const float *x, const float *nw, double eps, const float *r,
+               double *g_out, double *u_out, double *a_out, double *y_out, double *Sg,
+               double *Su, double *Sd) {
+    if (check_shape(inter, hidden) || check_shape(hidden, inter) || !x || eps < 0.0) return -2;
+    double *n = (double *)malloc(sizeof(double) * (size_t)hidden);
+    double *g = (double *)malloc(sizeof(double) * (size_t)inter);
+    double *u = (double *)malloc(sizeof(double) * (size_t)inter);
+    double *a = (double *)malloc(sizeof(double) * (size_t)inter);
+    double *y = (double *)malloc(sizeof(double) * (size_t)hidden);
+    int rc = (n && g && u && a && y) ? 0 : -4;
+    if (!rc) {
+        for (int64_t k = 0; k < hidden; ++k) n[k] = (double)x[k];
+        const double rm = oracle_rms(n, hidden, eps);
+        for (int64_t k = 0; k < hidden; ++k)
+            n[k] = n[k] / rm * (nw ? 1.0 + (double)nw[k] : 1.0);
+        rc = oracle_gemv_rows_d(wg, n, inter, hidden, NULL, 0, g, Sg);
+    }
+    if (!rc) rc = oracle_gemv_rows_d(wu, n, inter, hidden, NULL, 0, u, Su);
+    if (!rc) {
+        for (int64_t i = 0; i < inter; ++i) a[i] = oracle_silu(g[i]) * u[i];
+        rc = oracle_gemv_rows_d(wd, a, hidden, inter, NULL, 0, y, Sd);
+    }
+    if (!rc) {
+        if (r)
+            for (int64_t j = 0; j < hidden; ++j) y[j] += (double)r[j];
+        if (g_out) memcpy(g_out, g, sizeof(double) * (size_t)inter);
+        if (u_out) memcpy(u_out, u, sizeof(double) * (size_t)inter);
+        if (a_out) memcpy(a_out, a, sizeof(double) * (size_t)inter);
+        if (y_out) memcpy(y_out, y, sizeof(double) * (size_t)hidden);
+    }
+    free(n); free(g); free(u); free(a); free(y);
+    return rc;
+}
+
 /* The per-token chain of projection and MLP matmuls, with every matmul input
  * RMS-normalised (no gain) and the stand-in mixer taking the first mix_out.K
  * outputs of mix_in:

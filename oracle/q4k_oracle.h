@@ -60,6 +60,16 @@ double oracle_rms(const double *v, int64_t n, double eps);
 /* SiLU: g / (1 + exp(-g)). */
 double oracle_silu(double g);
 
+/* One MLP block: n = x / rms(x) * (1 + nw) (nw NULL: gain 1), a = silu(W_gate n)
+ * * (W_up n), y = r + W_down a (r NULL: 0).  wg, wu: [inter][hidden];
+ * wd: [hidden][inter].  Outputs double, each may be NULL: g, u, a [inter],
+ * y [hidden], and the sums of |w x| of the three matmuls Sg, Su [inter],
+ * Sd [hidden]. */
+int oracle_mlp(const uint8_t *wg, const uint8_t *wu, const uint8_t *wd, int64_t hidden,
+               int64_t inter, const float *x, const float *nw, double eps, const float *r,
+               double *g_out, double *u_out, double *a_out, double *y_out, double *Sg,
+               double *Su, double *Sd);
+
 /* Decode matmul chain.  mats holds 5*n_layers + 1 matrices in the order
  * (mix_in, mix_out, gate, up, down) per layer, then lm_head; Ms/Ks their
  * shapes.  h0 is f32 [hidden]; logits (double) gets lm_head's M outputs.

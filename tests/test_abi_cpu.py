@@ -73,6 +73,23 @@ def test_null_and_alignment_errors(lib):
     assert b"P must be" in lib.q4k_last_error()
 
 
+def test_mlp_validation(lib):
+    """q4k_mlp checks shapes, pointers, alignment and eps before any device
+    work (hidden and inter must be positive multiples of 256)."""
+    f = ctypes.c_float
+    ok = lambda **kw: dict(dict(wg=P, wu=P, wd=P, H=512, I=768, x=P, nw=None, eps=f(1e-6),
+                                r=None, y=P, act=None), **kw)
+    call = lambda a: lib.q4k_mlp(a["wg"], a["wu"], a["wd"], a["H"], a["I"], a["x"], a["nw"],
+                                 a["eps"], a["r"], a["y"], a["act"], None)
+    for kw, code in (({"H": 500}, -2), ({"I": 0}, -2), ({"I": 100}, -2), ({"H": -256}, -2),
+                     ({"wg": None}, -1), ({"wu": None}, -1), ({"wd": None}, -1),
+                     ({"x": None}, -1), ({"y": None}, -1), ({"eps": f(-1.0)}, -1),
+                     ({"eps": f(float("nan"))}, -1), ({"eps": f(float("inf"))}, -1),
+                     ({"x": P + 4}, -3), ({"act": P + 8}, -3), ({"wd": P + 2}, -3)):
+        assert call(ok(**kw)) == code, kw
+        assert lib.q4k_last_error()
+
+
 def test_zero_sizes_are_noops(lib):
     # nothing is enqueued and no device is touched
     assert lib.q4k_gemv(None, None, None, 0, 256, None) == 0

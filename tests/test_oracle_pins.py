@@ -365,6 +365,98 @@ def test_rms_and_silu_closed_forms():
         assert abs((oracle.silu(g) - oracle.silu(-g)) - g) < 1e-15 * (1 + g)
 
 
+# ---------------------------------------------------------------- MLP block
+
+def _worked_rows(n_rows, shift):
+    """A [n_rows][256] Q4_K matrix (one super-block per row) whose row i is
+    hand-worked block (i + shift) mod len(WORKED), and its known values."""
+    blocks = [np.asarray(it["block"], np.uint8) for it in WORKED]
+    vals = [[float(v) for v, _ in it["expect"]] for it in WORKED]
+    idx = [(i + shift) % len(WORKED) for i in range(n_rows)]
+    return np.stack([blocks[j] for j in idx]), [vals[j] for j in idx]
+
+
+def _silu(v: float) -> float:
+    # e^-v overflows past 709.78: the quotient is then v / inf = -0
+    return v / (1.0 + math.exp(-v)) if -v < 709.0 else v / math.inf
+
+
+@pytest.mark.parametrize("k,c", [(0, 1.0), (37, 1.0), (200, 0.75), (255, 2.5)])
+def test_mlp_one_hot_closed_form(k, c):
+    """x = e_k, eps = 0, gain (1 + w) = c everywhere, hidden = inter = 256:
+    rms(e_k) = 1/16 exactly, so n = 16 c e_k and the gate and up outputs are
+    16 c times column k of the hand-worked rows.  a = silu(g) * u, and
+    y = r + W_down a as an exactly rounded sum (math.fsum) over the known
+    down-row values: pins the normalisation, the gain, which product takes the
+    SiLU, the down matrix orientation and the residual."""
+    H = I = 256
+    wg, vg = _worked_rows(I, 0)
+    wu, vu = _worked_rows(I, 3)
+    wd, vd = _worked_rows(H, 5)
+    x = np.zeros(H, np.float32)
+    x[k] = 1.0
+    nw = np.full(H, c - 1.0, np.float32)
+    r = np.linspace(-2, 2, H).astype(np.float32)
+    out = oracle.mlp(wg, wu, wd, H, I, x, nw, 0.0, r)
+    g = [16.0 * c * vg[i][k] for i in range(I)]
+    u = [16.0 * c * vu[i][k] for i in range(I)]
+    a = [_silu(g[i]) * u[i] for i in range(I)]
+    for i in range(I):
+        assert out["g"][i] == g[i] and out["u"][i] == u[i]
+        assert abs(out["a"][i] - a[i]) <= 1e-15 * abs(a[i])
+    for j in range(H):
+        yj = float(r[j]) + math.fsum(vd[j][i] * a[i] for i in range(I))
+        scale = float(abs(r[j])) + math.fsum(abs(vd[j][i] * a[i]) for i in range(I))
+        assert abs(out["y"][j] - yj) <= 1e-13 * (scale + 1.0), j
+
+
+def test_mlp_zero_input_and_zero_gain_give_the_residual():
+    """x = 0 normalises to 0 (rms = sqrt(eps)), and a gain of 1 + w = 0 zeroes
+    n: either way a = silu(0) * 0 = 0 and y is exactly the residual."""
+    H, I = 512, 768
+    wg = synth.q4k_weight(synth.key(9, 901), I, H)
+    wu = synth.q4k_weight(synth.key(9, 902), I, H)
+    wd = synth.q4k_weight(synth.key(9, 903), H, I)
+    r = synth.normal(synth.key(9, 904), H)
+    out = oracle.mlp(wg, wu, wd, H, I, np.zeros(H, np.float32), None, 1e-6, r)
+    assert np.all(out["a"] == 0.0) and np.array_equal(out["y"], r.astype(np.float64))
+    x = synth.normal(synth.key(9, 905), H)
+    out = oracle.mlp(wg, wu, wd, H, I, x, np.full(H, -1.0, np.float32), 1e-6, r)
+    assert np.all(out["a"] == 0.0) and np.array_equal(out["y"], r.astype(np.float64))
+    out = oracle.mlp(wg, wu, wd, H, I, x, None, 1e-6, None)
+    assert np.all(out["y"] != 0.0)     # no residual: y is the MLP output itself
+
+
+def test_mlp_scale_invariance_without_eps():
+    """With eps = 0, RMSNorm(4x) = RMSNorm(x) exactly (4 is a power of two, so
+    the mean, the square root and the division all scale exactly): every
+    output is bit-identical."""
+    H, I = 512, 768
+    wg = synth.q4k_weight(synth.key(9, 911), I, H)
+    wu = synth.q4k_weight(synth.key(9, 912), I, H)
+    wd = synth.q4k_weight(synth.key(9, 913), H, I)
+    x = synth.normal(synth.key(9, 914), H)
+    nw = (0.1 * synth.normal(synth.key(9, 915), H)).astype(np.float32)
+    a = oracle.mlp(wg, wu, wd, H, I, x, nw, 0.0, None)
+    b = oracle.mlp(wg, wu, wd, H, I, (4 * x).astype(np.float32), nw, 0.0, None)
+    for key in ("g", "u", "a", "y"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_mlp_eps_enters_the_rms():
+    """x = e_k with eps = 1/256: rms = sqrt(1/256 + 1/256) = sqrt(2)/16, so
+    the gate output is 16/sqrt(2) times the hand-worked column value."""
+    H = I = 256
+    wg, vg = _worked_rows(I, 1)
+    wu, _ = _worked_rows(I, 2)
+    wd, _ = _worked_rows(H, 4)
+    x = np.zeros(H, np.float32)
+    x[9] = 1.0
+    out = oracle.mlp(wg, wu, wd, H, I, x, None, 1.0 / 256, None)
+    for i in range(I):
+        assert abs(out["g"][i] - 16.0 / math.sqrt(2.0) * vg[i][9]) <= 1e-15 * (1 + abs(out["g"][i]))
+
+
 def _tiny_stack(n_layers, hidden=512, mix_in=768, mix_k=512, inter=768, vocab=256, cfg=9):
     mats, shapes = [], []
     t = 500
