@@ -20,6 +20,8 @@ Also measured and reported in the same line:
     for short prompts, P = 16, 22, 27, 64;
   * gemv_batch: N = 1, 2, 4, 8, 16 vectors on the 17408x5120 weight;
   * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound);
+  * mlp_block: the same MLP block through q4k_mlp (RMSNorm gain, gate|up
+    fused with the SwiGLU on device, down with the residual add);
   * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
     launch over its HIP-event duration, against 8 TB/s;
   * cpu_baseline: the CPU oracle (double precision, all host cores) on the
@@ -195,6 +197,33 @@ def main():
                            "timing": "HIP events around bursts of back-to-back launches (kernel + gap)",
                            "algorithmic_bytes_per_launch": gate_alg}
         log("MLP GEMVs: step %.2f us wall, kernels %s" % (wall * 1e6, kern))
+        # The same block through q4k_mlp: RMSNorm gain prologue, gate|up in one
+        # pass with the SwiGLU on device, down with the residual add (bursts
+        # of back-to-back calls on the cold copies, as above).
+        gain = upload((0.2 * synth.normal(synth.key(2, 50), wl.HIDDEN)).astype(np.float32))
+        y_mlp = torch.empty(wl.HIDDEN, device=dev)
+        for i in range(args.warmup):
+            c = i % args.copies
+            q4k.mlp(copies["gate"][c], copies["up"][c], copies["down"][c], xd, gain, 1e-6, xd, y_mlp)
+        torch.cuda.synchronize()
+        mlp_us = []
+        for rep in range(3):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for i in range(args.steps):
+                c = i % args.copies
+                q4k.mlp(copies["gate"][c], copies["up"][c], copies["down"][c], xd, gain, 1e-6, xd,
+                        y_mlp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mlp_us.append(e0.elapsed_time(e1) * 1e3 / args.steps)
+        t_mlp = float(np.mean(mlp_us))
+        out["mlp_block"] = {"us_mean": t_mlp, "us_median": float(np.median(mlp_us)),
+                            "GBps": step_bytes / t_mlp / 1e3,
+                            "frac_hbm": step_bytes / t_mlp / 1e3 / HBM_PEAK_GBS,
+                            "three_gemvs_us": gpu_us,
+                            "call": "q4k_mlp: (1+w) RMSNorm prologue, gate|up SwiGLU GEMV, down GEMV + residual"}
+        log("q4k_mlp: %.2f us per block (three GEMVs: %.2f us)" % (t_mlp, gpu_us))
         del copies
         torch.cuda.empty_cache()
 
