@@ -70,6 +70,12 @@ def _load():
         L.oracle_rms.argtypes = [_p, _i64, ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
         L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_dequant_q8_0_block.restype = None
+        L.oracle_dequant_q8_0_block.argtypes = [_p, _p]
+        L.oracle_dequant_q8_0.restype = ctypes.c_int
+        L.oracle_dequant_q8_0.argtypes = [_p, _i64, _i64, _p]
+        L.oracle_gemv_q8_0_rows_d.restype = ctypes.c_int
+        L.oracle_gemv_q8_0_rows_d.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
         L.oracle_mlp.restype = ctypes.c_int
         L.oracle_mlp.argtypes = [_p, _p, _p, _i64, _i64, _p, _p, ctypes.c_double, _p,
                                  _p, _p, _p, _p, _p, _p, _p]
@@ -208,6 +214,29 @@ def rms(v, eps: float = RMS_EPS) -> float:
 
 def silu(g: float) -> float:
     return float(_load().oracle_silu(float(g)))
+
+
+def dequant_q8_0(w, M: int, K: int) -> np.ndarray:
+    """Q8_0 matrix [M, K/32*34] -> f32 [M, K]."""
+    w = _u8(w)
+    out = np.empty((M, K), np.float32)
+    _check(_load().oracle_dequant_q8_0(w.ctypes.data, M, K, out.ctypes.data))
+    return out
+
+
+def gemv_q8_0(w, x, M: int, K: int, rows=None) -> tuple[np.ndarray, np.ndarray]:
+    """(y, S) in float64 for a Q8_0 matrix: y = W x, S = sum |w x| per row."""
+    w = _u8(w)
+    x = np.asarray(x)
+    xd = np.ascontiguousarray(x if x.dtype == np.float64 else x.astype(np.float32), np.float64)
+    assert xd.size == K
+    r, nr = _rows(rows)
+    n = nr if r is not None else M
+    y, S = np.empty(n, np.float64), np.empty(n, np.float64)
+    _check(_load().oracle_gemv_q8_0_rows_d(w.ctypes.data, xd.ctypes.data, M, K,
+                                           r.ctypes.data if r is not None else None, nr,
+                                           y.ctypes.data, S.ctypes.data))
+    return y, S
 
 
 def mlp(wg, wu, wd, hidden: int, inter: int, x, norm_w=None, eps: float = RMS_EPS,

@@ -236,6 +236,57 @@ int oracle_gemm_sub(const uint8_t *w, const float *X, int64_t M, int64_t K, int6
     return fail ? -4 : 0;
 }
 
+/* ---------------------------------------------------------------- Q8_0
+ * The other GGUF block type the pages use (the lm_head matmul in Q8, "Mac
+ * Qwen3.6-27B Metal Q4_K perf diagnosis", §2 decode profile; the GGUF->Q8
+ * path of "Qwen3.6-27B on Apple M3 Pro — the llama.cpp parity bar").  Layout
+ * per the public GGUF convention: 34 bytes per 32 weights, a binary16 scale d
+ * (little-endian) followed by 32 two's-complement int8 quants; w_i = d * q_i.
+ * The product of an 11-bit and an 8-bit significand is exact in f32. */
+static int check_shape_q8(int64_t M, int64_t K) {
+    return (M < 0 || K <= 0 || K % 32 != 0) ? -2 : 0;
+}
+
+void oracle_dequant_q8_0_block(const uint8_t *b, float out[32]) {
+    const double d = oracle_half_to_double((uint16_t)(b[0] | (b[1] << 8)));
+    for (int i = 0; i < 32; ++i) out[i] = (float)(d * (double)(int8_t)b[2 + i]);
+}
+
+int oracle_dequant_q8_0(const uint8_t *w, int64_t M, int64_t K, float *out) {
+    if (check_shape_q8(M, K)) return -2;
+    const int64_t nb = K / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; ++r)
+        for (int64_t j = 0; j < nb; ++j)
+            oracle_dequant_q8_0_block(w + (r * nb + j) * 34, out + r * K + j * 32);
+    return 0;
+}
+
+/* y[r] = sum_k w_rk x_k in double, and S[r] = sum_k |w_rk x_k| (either may
+ * be NULL), for the listed rows (rows NULL: all M). */
+int oracle_gemv_q8_0_rows_d(const uint8_t *w, const double *x, int64_t M, int64_t K,
+                            const int64_t *rows, int64_t nrows, double *y, double *S) {
+    if (check_shape_q8(M, K)) return -2;
+    const int64_t nb = K / 32, n = rows ? nrows : M;
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t r = rows ? rows[t] : t;
+        double acc = 0.0, sab = 0.0;
+        float v[32];
+        for (int64_t j = 0; j < nb; ++j) {
+            oracle_dequant_q8_0_block(w + (r * nb + j) * 34, v);
+            for (int i = 0; i < 32; ++i) {
+                const double p = (double)v[i] * x[j * 32 + i];
+                acc += p;
+                sab += fabs(p);
+            }
+        }
+        if (y) y[t] = acc;
+        if (S) S[t] = sab;
+    }
+    return 0;
+}
+
 double oracle_rms(const double *v, int64_t n, double eps) {
     double ss = 0.0;
     for (int64_t i = 0; i < n; ++i) ss += v[i] * v[i];

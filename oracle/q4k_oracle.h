@@ -54,6 +54,12 @@ int oracle_gemm_sub(const uint8_t *w, const float *X, int64_t M, int64_t K, int6
                     const int64_t *rows, int64_t nrows, const int64_t *toks, int64_t ntok,
                     int32_t bf16_inputs, double *Y, double *S);
 
+/* Q8_0 (34 bytes per 32 weights: binary16 d, 32 int8 q; w = d*q). */
+void oracle_dequant_q8_0_block(const uint8_t *b, float out[32]);
+int oracle_dequant_q8_0(const uint8_t *w, int64_t M, int64_t K, float *out);
+int oracle_gemv_q8_0_rows_d(const uint8_t *w, const double *x, int64_t M, int64_t K,
+                            const int64_t *rows, int64_t nrows, double *y, double *S);
+
 /* Root mean square with epsilon: sqrt(mean(v^2) + eps). */
 double oracle_rms(const double *v, int64_t n, double eps);
 

@@ -53,6 +53,9 @@ def _load():
         lib.synth_q4k_blocks.restype = ctypes.c_int
         lib.synth_q4k_blocks.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                          ctypes.c_void_p, ctypes.c_double, ctypes.c_double]
+        lib.synth_q8_0_blocks.restype = ctypes.c_int
+        lib.synth_q8_0_blocks.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_void_p, ctypes.c_double, ctypes.c_double]
         lib.synth_normal_f32.restype = None
         lib.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         lib.synth_bytes.restype = None
@@ -92,6 +95,23 @@ def q4k_weight(k: int, M: int, K: int, lo: float = D_LO, hi: float = D_HI,
         rc = _load().synth_q4k_blocks(k, row0 * nb, M * nb, out.ctypes.data, lo, hi)
         if rc != 0:
             raise ValueError("d/dmin range outside binary16 normals")
+    return out
+
+
+Q8_QK, Q8_BLOCK_BYTES = 32, 34
+
+
+def q8_0_weight(k: int, M: int, K: int, lo: float = D_LO, hi: float = D_HI) -> np.ndarray:
+    """A random Q8_0 matrix with K columns: uint8 [M, K/32*34], row-major, each
+    row K/32 consecutive 34-byte blocks (binary16 d, then 32 int8 quants)."""
+    if K % Q8_QK:
+        raise ValueError("K must be a multiple of 32")
+    nb = K // Q8_QK
+    out = np.empty((M, nb * Q8_BLOCK_BYTES), dtype=np.uint8)
+    if M:
+        rc = _load().synth_q8_0_blocks(k, 0, M * nb, out.ctypes.data, lo, hi)
+        if rc != 0:
+            raise ValueError("d range outside binary16 normals")
     return out
 
 

@@ -22,6 +22,8 @@
  * Uniform bytes give uniform 6-bit scales/mins and uniform nibbles under any
  * bijective packing, so the distribution does not depend on the layout.
  *
+ * Q8_0 block stream: see synth_q8_0_blocks.
+ *
  * Normal activations: Box–Muller (G. E. P. Box, M. E. Muller, 1958) on the
  * word pair (2i, 2i+1), computed in double and rounded once to f32.
  */
@@ -82,6 +84,28 @@ int synth_q4k_blocks(uint64_t key, uint64_t block0, uint64_t nblocks,
         for (int j = 0; j < 16; ++j) {
             uint64_t w = sm64_word(key, base + 4 + (uint64_t)j);
             memcpy(p + 16 + 8 * j, &w, 8);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Q8_0 block stream (34 bytes per block, 5 words per block):
+ *   word 5b+0 -> d : U(lo, hi) in double, rounded to IEEE binary16 (RNE)
+ *   words 5b+1 .. 5b+4 -> the 32 quant bytes (uniform over all 256 values). */
+int synth_q8_0_blocks(uint64_t key, uint64_t block0, uint64_t nblocks,
+                      uint8_t *out, double lo, double hi) {
+    int bad = 0;
+    #pragma omp parallel for schedule(static) reduction(|:bad)
+    for (int64_t bi = 0; bi < (int64_t)nblocks; ++bi) {
+        uint64_t b = block0 + (uint64_t)bi;
+        uint8_t *p = out + (uint64_t)bi * 34u;
+        uint64_t base = b * 5u;
+        uint16_t hd = half_bits_rne(lo + (hi - lo) * u01(sm64_word(key, base + 0)));
+        if (hd == 0xFFFF) bad = 1;
+        p[0] = (uint8_t)(hd & 0xFF); p[1] = (uint8_t)(hd >> 8);
+        for (int j = 0; j < 4; ++j) {
+            uint64_t w = sm64_word(key, base + 1 + (uint64_t)j);
+            memcpy(p + 2 + 8 * j, &w, 8);
         }
     }
     return bad ? -1 : 0;

@@ -524,3 +524,91 @@ def test_thread_count_does_not_change_bits():
     oracle.set_threads(4)
     y4, _ = oracle.gemv(w, x, M, K)
     assert np.array_equal(y1, y4)
+
+
+# ---------------------------------------------------------------- Q8_0
+
+def _q8_fixture():
+    """The hand-worked Q8_0 blocks of tests/golden/q8_0_blocks.txt."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "q8_0_blocks.txt")
+    out = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        bid, dhex, qs, exp = [f.strip() for f in line.split("|")]
+        if qs == "ramp":
+            q = [i - 16 for i in range(32)]
+        elif qs == "alt":
+            q = [127 if i % 2 == 0 else -128 for i in range(32)]
+        else:
+            q = [int(v) for v in qs.split()]
+        d = int(dhex, 16)
+        blk = np.array([d & 0xFF, d >> 8] + [v & 0xFF for v in q], np.uint8)
+        out.append((bid, blk, exp.split()))
+    return out
+
+
+@pytest.mark.parametrize("item", _q8_fixture(), ids=lambda it: it[0])
+def test_q8_0_worked_blocks(item):
+    """d is the first (little-endian) binary16, the quants are two's-complement
+    bytes, w = d * q with the sign of zero kept."""
+    bid, blk, exp = item
+    got = oracle.dequant_q8_0(blk[None, :], 1, 32)[0]
+    assert len(exp) == 32
+    for i, e in enumerate(exp):
+        want = np.float32(-0.0) if e == "-0" else np.float32(float(e))
+        assert _f32_bits(got[i]) == _f32_bits(want), (bid, i, got[i], e)
+
+
+def test_q8_0_dequant_vs_numpy_decoding():
+    """Random blocks: numpy's own binary16 and int8 decoding of the same bytes,
+    multiplied in double and rounded once, agree bit for bit."""
+    w = synth.q8_0_weight(synth.key(9, 930), 37, 1024)
+    blocks = w.reshape(-1, 34)
+    d = blocks[:, :2].copy().view(np.float16).astype(np.float64)
+    q = blocks[:, 2:].view(np.int8).astype(np.float64)
+    ref = (d * q).astype(np.float32).reshape(37, 1024)
+    got = oracle.dequant_q8_0(w, 37, 1024)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_q8_0_gemv_closed_forms():
+    """Zero x gives exact zeros; a one-hot x returns the dequantised column; a
+    row of blocks repeated k times with x = 1 sums to k times the block sum."""
+    M, K = 40, 512
+    w = synth.q8_0_weight(synth.key(9, 931), M, K)
+    y, S = oracle.gemv_q8_0(w, np.zeros(K, np.float32), M, K)
+    assert np.all(y == 0.0) and np.all(S == 0.0)
+    deq = oracle.dequant_q8_0(w, M, K)
+    for k in (0, 31, 32, 100, 511):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y, _ = oracle.gemv_q8_0(w, x, M, K)
+        assert np.array_equal(y, deq[:, k].astype(np.float64))
+    _, blk, _ = _q8_fixture()[0]              # Q1: weights -16 .. 15
+    tiled = np.tile(blk, 16)[None, :]         # 16 blocks = 512 weights
+    y, _ = oracle.gemv_q8_0(tiled, np.ones(512, np.float32), 1, 512)
+    assert y[0] == 16 * sum(range(-16, 16))
+
+
+@pytest.mark.parametrize("M,K", [(3, 32), (2, 96)])
+def test_q8_0_gemv_bruteforce_exact_rationals(M, K):
+    """Tiny matrices: the exact rational sum (Fractions from the raw bytes) is
+    within the double rounding of the oracle's result."""
+    w = synth.q8_0_weight(synth.key(9, 932 + K), M, K)
+    x = synth.normal(synth.key(9, 933), K)
+    y, _ = oracle.gemv_q8_0(w, x, M, K)
+    for r in range(M):
+        acc = Fraction(0)
+        for j in range(K // 32):
+            b = w[r, 34 * j:34 * (j + 1)]
+            h = int(b[0]) | (int(b[1]) << 8)
+            e, m, s = (h >> 10) & 31, h & 1023, -1 if h & 0x8000 else 1
+            d = s * (Fraction(m, 1024) * Fraction(2) ** -14 if e == 0 else
+                     Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15))
+            for i in range(32):
+                q = int(b[2 + i]) - 256 if b[2 + i] >= 128 else int(b[2 + i])
+                acc += d * q * Fraction(float(x[32 * j + i]))
+        assert abs(Fraction(y[r]) - acc) <= Fraction(1, 2 ** 40) * (1 + abs(acc))
