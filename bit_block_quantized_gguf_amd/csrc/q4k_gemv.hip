@@ -478,6 +478,161 @@ __global__ __launch_bounds__(64) void sumsq_kernel(const float *__restrict__ v, 
     if ((threadIdx.x & 31) == 0 && granule * 32 < n) out[granule] = s;
 }
 
+// ---------------------------------------------------------------------------
+// Q8_0 GEMV (one vector).  Q8_0 stores 32 weights in 34 bytes: a binary16
+// scale d, then 32 two's-complement int8 quants; w = d * q (public GGUF
+// convention; the pages run the lm_head matmul in Q8, "Mac Qwen3.6-27B Metal
+// Q4_K perf diagnosis", §2 decode profile).  Same skeleton as the Q4_K
+// kernel: a unit is 64 rows x 16 blocks (one 544-byte run per row), copied to
+// LDS in address order (rows padded to 560 bytes) with the next unit's loads
+// in flight; wave w then takes blocks 4w .. 4w+3 of every row, one row per
+// lane.  Per dword of quants, an XOR with 0x80 per byte makes u = q + 128
+// (0..255), and one AND (of the dword, or of it shifted by 8) places two
+// bytes into the 16-bit halves, where binary16 reads u as the subnormal
+// u * 2^-24: one v_fma_mix_f32 per weight.  Per block, sum(q x) =
+// 2^24 * sum(u x) - 128 * sum(x); the block sums of x come from one 16-byte
+// load per lane and a 3-step butterfly.
+constexpr int Q8_BB = 34;                      // bytes per block
+constexpr int Q8_UNIT_BLOCKS = 16;             // blocks per row per unit
+constexpr int Q8_SEG = Q8_UNIT_BLOCKS * Q8_BB;  // 544-byte row run
+constexpr int Q8_SEGP = Q8_SEG + 16;           // LDS row stride
+constexpr int Q8_CH_ROW = Q8_SEG / 16;         // 34 chunks per row
+constexpr int Q8_CH_UNIT = 64 * Q8_CH_ROW;     // 2176 chunks per unit
+constexpr int Q8_CH_THREAD = (Q8_CH_UNIT + 64 * WK - 1) / (64 * WK);  // 9 (the last for half the threads)
+static_assert(Q8_SEG % 16 == 0 && Q8_SEGP % 16 == 0, "16-byte chunks");
+
+// sum over a block's 32 quants of u * x (in units of 2^-24), u = q + 128;
+// q8 holds the 8 quant dwords, x the block's 32 activations.
+__device__ __forceinline__ float q8_block_dot(const uint32_t (&q8)[8], cfloat *x) {
+    float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t u = q8[i] ^ 0x80808080u;
+        const half2v u02 = __builtin_bit_cast(half2v, and_mask(u, 0x00FF00FFu));       // u0, u2
+        const half2v u13 = __builtin_bit_cast(half2v, and_mask(u >> 8, 0x00FF00FFu));  // u1, u3
+        c0 = fmaf((float)u02.x, x[4 * i + 0], c0);
+        c1 = fmaf((float)u13.x, x[4 * i + 1], c1);
+        c0 = fmaf((float)u02.y, x[4 * i + 2], c0);
+        c1 = fmaf((float)u13.y, x[4 * i + 3], c1);
+    }
+    return c0 + c1;
+}
+
+__global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, const Units un) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * Q8_SEGP];
+    __shared__ float red[WK][1][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x;
+    const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
+
+    int crow[Q8_CH_THREAD], coff[Q8_CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < Q8_CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;  // past Q8_CH_UNIT only in the last slot (waves 2, 3)
+        crow[i] = q / Q8_CH_ROW;
+        coff[i] = 16 * (q - crow[i] * Q8_CH_ROW);
+    }
+    uint4 reg[Q8_CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < Q8_CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    auto fetch = [&](int t, int k) {
+        const int j0 = k * Q8_UNIT_BLOCKS;
+        const int valid = min(Q8_UNIT_BLOCKS, p.nb - j0) * Q8_BB;  // bytes of this row run
+        const int rmax = min(63, p.M - 1 - t * 64);
+        const uint8_t *b0 = p.w0 + (int64_t)t * 64 * p.row_bytes + (int64_t)j0 * Q8_BB;
+#pragma unroll
+        for (int i = 0; i < Q8_CH_THREAD; ++i) {
+            if (i * 64 * WK + 64 * wave >= Q8_CH_UNIT) continue;  // wave-uniform
+            const int co = coff[i] < valid ? coff[i] : 0;
+            const uint32_t off = (uint32_t)min(crow[i], rmax) * (uint32_t)p.row_bytes + (uint32_t)co;
+            reg[i] = ldg16(b0 + off);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < Q8_CH_THREAD; ++i) {
+            if (i * 64 * WK + 64 * wave >= Q8_CH_UNIT) continue;
+            *reinterpret_cast<uint4 *>(&stage[crow[i] * Q8_SEGP + coff[i]]) = reg[i];
+        }
+    };
+
+    float acc = 0.f;
+    int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);
+    fetch(t, k);
+    commit();
+    __syncthreads();
+    bool seg_first = k == 0;
+    for (int64_t u = ua; u < ub; ++u) {
+        const int j = k * Q8_UNIT_BLOCKS + 4 * wave;  // this wave's first block
+        const bool active = j < p.nb;                // nb is a multiple of 8: all 4 or none
+        const bool last_of_tile = k + 1 == un.upt;
+        const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
+        // block sums of x first (lanes 8b .. 8b+7 hold block b's 32 values),
+        // then the next unit's loads
+        float4 xq = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (active && lane < 32) xq = *reinterpret_cast<const float4 *>(p.x + 32 * (int64_t)j + 4 * lane);
+        const bool more = u + 1 < ub;
+        if (more) fetch(tn, kn);
+        if (active) {
+            const uint8_t *lp = &stage[lane * Q8_SEGP + wave * 4 * Q8_BB];
+            uint32_t D[34];
+#pragma unroll
+            for (int i = 0; i < 17; ++i) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(lp + 8 * i);
+                D[2 * i] = v.x;
+                D[2 * i + 1] = v.y;
+            }
+            float s = (xq.x + xq.y) + (xq.z + xq.w);
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 4);
+            cfloat *xb = as_const(p.x + 32 * (int64_t)j);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                // block b starts at byte 34 b: d in its first two bytes, the
+                // quants after them (2 bytes into a dword for even b)
+                const int w0 = (34 * b) >> 2;
+                const uint32_t dbits = (b & 1) ? (D[w0] >> 16) : (D[w0] & 0xFFFFu);
+                uint32_t q8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    q8[i] = (b & 1) ? D[w0 + 1 + i]
+                                    : __builtin_amdgcn_alignbyte(D[w0 + 1 + i], D[w0 + i], 2);
+                const float T = q8_block_dot(q8, xb + 32 * b);
+                const float X = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * b));
+                const float d = __half2float(__ushort_as_half((unsigned short)dbits));
+                acc = fmaf(d, fmaf(T, 16777216.0f, -128.0f * X), acc);
+            }
+        }
+        const bool seg_end = !more || last_of_tile;
+        if (seg_end) {
+            red[wave][0][lane] = acc;
+            acc = 0.f;
+        }
+        __syncthreads();
+        if (seg_end && wave == 0) {
+            float tot[1] = {red[0][0][lane]};
+#pragma unroll
+            for (int w = 1; w < WK; ++w) tot[0] += red[w][0][lane];
+            if (seg_first && last_of_tile)
+                epilogue<1, 1, EPI_PLAIN>(p, t * 64, lane, tot, 1.f);
+            else
+                finish_split_tile<1, 1, EPI_PLAIN>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot,
+                                                   1.f);
+        }
+        if (seg_end) seg_first = true;
+        t = tn;
+        k = kn;
+        if (more) commit();
+        __syncthreads();
+    }
+}
+
 // xg[i] = x[i] * (1 + w[i]) (w null: xg not written) and the sums of squares
 // of x per 32 elements, one element per thread.
 __global__ __launch_bounds__(64) void norm_gain_kernel(const float *__restrict__ x,
@@ -616,6 +771,35 @@ int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch
     if (nmat == 1 && epi == EPI_RESID) return launch_t<1, 1, EPI_RESID>(p, L, stream);
     if (nmat == 2 && epi == EPI_SWIGLU) return launch_t<1, 2, EPI_SWIGLU>(p, L, stream);
     return fail(Q4K_EINVAL, "unsupported GEMV variant");
+}
+
+GemvLaunch choose_gemv_q8_launch(int64_t M, int64_t K) {
+    GemvLaunch L;
+    L.wk = WK;
+    const int64_t units = ((M + 63) / 64) * ((K / 32 + Q8_UNIT_BLOCKS - 1) / Q8_UNIT_BLOCKS);
+    int G = g_override_groups.load(), res = 0, cus = 0;
+    if (G <= 0) {
+        if (resident_groups((const void *)gemv_q8_kernel, &res, &cus) == Q4K_OK) G = res;
+        else {
+            clear_error();
+            G = 1024;
+        }
+    }
+    L.ks = (int)std::max<int64_t>(1, std::min<int64_t>(G, units));
+    return L;
+}
+
+int launch_gemv_q8(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
+    const int64_t tiles = (p.M + 63) / 64;
+    Units un;
+    un.upt = (p.nb + Q8_UNIT_BLOCKS - 1) / Q8_UNIT_BLOCKS;
+    un.U = tiles * un.upt;
+    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
+    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
+    hipLaunchKernelGGL(gemv_q8_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
+    Q4K_HIP(hipGetLastError());
+    return Q4K_OK;
 }
 
 int launch_norm_gain(const float *x, const float *w, int64_t n, float *xg, float *sq,

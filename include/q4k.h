@@ -96,6 +96,18 @@ int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
 int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
 
 /*
+ * Q8_0 GEMV: y[i] = sum_k w_ik * x[k] for a Q8_0 matrix (public GGUF layout:
+ * 34 bytes per 32 weights, a little-endian binary16 scale d then 32
+ * two's-complement int8 quants, w = d * q; rows of K / 32 consecutive
+ * blocks).  The pages run the lm_head matmul in Q8 ("Mac Qwen3.6-27B Metal
+ * Q4_K perf diagnosis", §2 decode profile).  K must be a positive multiple
+ * of 256 (so row runs stay 16-byte aligned), x f32 [K], y f32 [M]; w, x, y
+ * 16-byte aligned.  f32 accumulation within the q4k_gemv bound.  Same error
+ * codes as q4k_gemv.
+ */
+int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+
+/*
  * MLP block of one token (the model's SwiGLU feed-forward with its RMSNorm in
  * the (1 + w) form, "Qwen3.6-27B on Apple M3 Pro — the llama.cpp parity bar",
  * model description and the fak-native status list; the gate/up/down matmuls
