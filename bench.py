@@ -22,6 +22,7 @@ Also measured and reported in the same line:
   * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound);
   * mlp_block: the same MLP block through q4k_mlp (RMSNorm gain, gate|up
     fused with the SwiGLU on device, down with the residual add);
+  * gemv_q8_0_lm_head: the lm_head matmul in Q8_0 (248320x5120, 1.35 GB);
   * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
     launch over its HIP-event duration, against 8 TB/s;
   * cpu_baseline: the CPU oracle (double precision, all host cores) on the
@@ -72,7 +73,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="gemv,batch,small,gemm,stack,cpu",
+    ap.add_argument("--sections", default="gemv,batch,small,q8,gemm,stack,cpu",
                     help="comma list of gemv,batch,small,gemm,stack,cpu (and copy: the "
                          "256 MiB device copy that calibrates the PMC traffic counters)")
     ap.add_argument("--copies", type=int, default=4, help="cold-rotation copies per MLP matrix")
@@ -281,6 +282,35 @@ def main():
                 ts.append(e0.elapsed_time(e1) * 1e3)
             res.append({"M": M, "K": K, "us_median": float(np.median(ts)), "bytes": wbytes(M, K)})
         out["gemv_small"] = res
+
+    # ------------------------------------------------------------ Q8_0 GEMV
+    if "q8" in sections:
+        # the lm_head matmul in Q8_0 (vocab x hidden, 1.35 GB: larger than the
+        # Infinity Cache, so every launch streams from HBM)
+        M, K = wl.VOCAB, wl.HIDDEN
+        log("generating the %dx%d Q8_0 lm_head" % (M, K))
+        wq = upload(synth.q8_0_weight(synth.key(7, 1), M, K))
+        xq = upload(synth.activations(7, 1, K)[0])
+        yq = torch.empty(M, device=dev)
+        for _ in range(3):
+            q4k.gemv_q8_0(wq, xq, yq)
+        torch.cuda.synchronize()
+        reps = []
+        for rep in range(3):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(10):
+                q4k.gemv_q8_0(wq, xq, yq)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) * 1e3 / 10)
+        qb = M * (K // 32) * 34 + 4 * (M + K)
+        t = float(np.mean(reps))
+        out["gemv_q8_0_lm_head"] = {"M": M, "K": K, "us": t, "bytes": qb, "GBps": qb / t / 1e3,
+                                    "frac_hbm": qb / t / 1e3 / HBM_PEAK_GBS}
+        log("q8_0 lm_head: %.1f us, %.0f GB/s" % (t, qb / t / 1e3))
+        del wq
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ prefill GEMM
     if "gemm" in sections:
