@@ -17,7 +17,9 @@
 //    per lane.  All lanes need the same 256 activations at the same time:
 //    they arrive by scalar loads (constant address space) and enter every FMA
 //    as an SGPR operand.  The wave index goes through readfirstlane so the
-//    compiler can prove those addresses wave-uniform.
+//    compiler can prove those addresses wave-uniform.  For one and two
+//    vectors the scalar loads are software-pipelined one stage (two or one
+//    quant words) ahead of the FMAs that use them.
 //  * Per weight the VALU work is one FMA taking the nibble as a binary16
 //    operand (v_fma_mix_f32), plus four ANDs and a shift per eight weights:
 //    one AND places two nibbles (of bytes 0 and 2, or of bytes 1 and 3 after
@@ -73,22 +75,163 @@ __device__ __forceinline__ float wave_sum(float v) {
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 
-// acc[n] += sum over the block of w * x_n (factored form).
-//
-// A nibble value c (0..15, or 16q for a high nibble kept in place) sitting in
-// a 16-bit half is, read as binary16, the subnormal c * 2^-24 exactly, and
-// v_fma_mix_f32 takes such a half as an operand.  So each weight costs one
-// FMA (no byte-to-float conversion): the sums T_j carry the exact factor
-// 2^-24, removed at the end by a power-of-two scaling (exact, so the sums
-// equal the unscaled ones unless a product falls below the f32 normal range).
+// Activations of one pipeline stage of block_dot_mix: for each vector, the
+// 4*SW values of the low-nibble sub-block and the 4*SW matching values of the
+// high-nibble sub-block that SW quant words multiply.
+template <int NV, int SW>
+struct XStage {
+    float l[NV][4 * SW], h[NV][4 * SW];
+};
+
+// Stage st of a block covers words 1 + 2g + ..., i.e. quant words
+// i = SW*(st % (8/SW)) ... of group g = st / (8/SW); its activations are
+// x[64g + 4i + e] (low nibbles) and x[64g + 32 + 4i + e] (high nibbles).
+template <int NV, int SW>
+__device__ __forceinline__ void load_stage(XStage<NV, SW> &s, cfloat *xb, int64_t xs, int st) {
+    constexpr int SPG = 8 / SW;  // stages per group
+    // An offset the optimiser cannot see through (always 0) pins the loads
+    // after this point: without it they are hoisted to the block start and
+    // their values spilled.
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const int o = 64 * (st / SPG) + 4 * SW * (st % SPG) + z;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < 4 * SW; ++e) {
+            s.l[n][e] = xb[n * xs + o + e];
+            s.h[n][e] = xb[n * xs + o + 32 + e];
+        }
+}
+
+// One quant word (8 weights) of a stage: four ANDs and a shift place the
+// nibbles into binary16 halves (q[0..1]: bytes 0 and 2, q[2..3]: bytes 1 and
+// 3, low nibbles then 16 x high nibbles); then one v_fma_mix_f32 per weight
+// into two chains per sub-block (even and odd bytes).
+struct WordQ {
+    half2v l02, l13, h02, h13;
+};
+
+__device__ __forceinline__ WordQ word_unpack(uint32_t v) {
+    const uint32_t v8 = v >> 8;
+    WordQ q;
+    q.l02 = __builtin_bit_cast(half2v, and_mask(v, 0x000F000Fu));   // q0, q2
+    q.l13 = __builtin_bit_cast(half2v, and_mask(v8, 0x000F000Fu));  // q1, q3
+    q.h02 = __builtin_bit_cast(half2v, and_mask(v, 0x00F000F0u));   // 16 q
+    q.h13 = __builtin_bit_cast(half2v, and_mask(v8, 0x00F000F0u));
+    return q;
+}
+
+// byte e of word w of the stage
+template <int NV, int SW>
+__device__ __forceinline__ void byte_fma(const WordQ &q, const XStage<NV, SW> &s, int w, int e,
+                                         float (&cl)[NV][2], float (&ch)[NV][2]) {
+    const int c = e & 1;
+    const half2v ql = c ? q.l13 : q.l02, qh = c ? q.h13 : q.h02;
+    const float wl = (e & 2) ? (float)ql.y : (float)ql.x;
+    const float wh = (e & 2) ? (float)qh.y : (float)qh.x;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        cl[n][c] = fmaf(wl, s.l[n][4 * w + e], cl[n][c]);
+        ch[n][c] = fmaf(wh, s.h[n][4 * w + e], ch[n][c]);
+    }
+}
+
+// block_dot for one or two vectors.  A nibble value c (0..15, or 16q for a
+// high nibble kept in place) sitting in a 16-bit half is, read as binary16,
+// the subnormal c * 2^-24 exactly, and v_fma_mix_f32 takes such a half as an
+// operand: each weight costs one FMA and no byte-to-float conversion.  The
+// sums carry the exact factor 2^-24, removed at the end by a power-of-two
+// scaling (exact unless a product falls below the f32 normal range).
+// The activations are software-pipelined through SGPRs: the scalar loads of stage st+1 are issued
+// right after the first word of stage st has consumed its (already waited)
+// operands, so each wait for scalar data covers loads issued one stage
+// earlier.  Scalar loads complete out of order, so every wait is a full
+// lgkmcnt(0); the order wait -> issue next -> compute keeps exactly one stage
+// in flight.
+template <int NV>
+__device__ __forceinline__ void block_dot_mix(const uint4 (&b)[9], const float *xblk, int64_t xs,
+                                              const float4 (&xq)[NV], float (&acc)[NV]) {
+    constexpr int SW = NV == 1 ? 2 : 1;  // quant words per stage
+    constexpr int SPG = 8 / SW;          // stages per group
+    constexpr int NST = 4 * SPG;         // stages per block
+    const float d = half_lo(b[0].x);
+    const float dmin = half_hi(b[0].x);
+    const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
+    cfloat *xc = as_const(xblk);
+    float A_lo[NV], A_hi[NV], B[NV];
+    float cl[NV][2], ch[NV][2];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        A_lo[n] = A_hi[n] = B[n] = 0.f;
+        cl[n][0] = cl[n][1] = ch[n][0] = ch[n][1] = 0.f;
+    }
+    XStage<NV, SW> xs_a, xs_b;
+    load_stage<NV, SW>(xs_a, xc, xs, 0);
+    auto stage = [&](int st, const XStage<NV, SW> &cur, XStage<NV, SW> &nxt) {
+        const int g = st / SPG;
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+            const int i = SW * (st % SPG) + w;  // word of the group
+            const WordQ q = word_unpack(word_of(b[1 + 2 * g + (i >> 2)], i & 3));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                byte_fma<NV, SW>(q, cur, w, e, cl, ch);
+                if (w == 0 && e == 3) {
+                    // The stage's first word has waited for its activations.
+                    // The chains pass through an empty volatile asm, so the
+                    // next stage's loads are issued only now and the rest of
+                    // the stage covers their latency.  (Issuing them after the
+                    // first FMA instead measured 2-3% slower.)
+#pragma unroll
+                    for (int n = 0; n < NV; ++n)
+                        asm volatile("" : "+v"(cl[n][0]), "+v"(cl[n][1]), "+v"(ch[n][0]),
+                                     "+v"(ch[n][1]));
+                    if (st + 1 < NST) load_stage<NV, SW>(nxt, xc, xs, st + 1);
+                }
+            }
+        }
+        if (st % SPG == SPG - 1) {  // group complete
+            const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                A_lo[n] = fmaf(sl, cl[n][0] + cl[n][1], A_lo[n]);
+                A_hi[n] = fmaf(sh, ch[n][0] + ch[n][1], A_hi[n]);
+                cl[n][0] = cl[n][1] = ch[n][0] = ch[n][1] = 0.f;
+            }
+        }
+    };
+#pragma unroll
+    for (int st = 0; st < NST; st += 2) {
+        stage(st, xs_a, xs_b);
+        stage(st + 1, xs_b, xs_a);
+    }
+    constexpr float kScale = 16777216.0f;  // 2^24 removes the binary16 subnormal scale
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        float s = (xq[n].x + xq[n].y) + (xq[n].z + xq[n].w);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+#pragma unroll
+        for (int sb = 0; sb < 8; ++sb)
+            B[n] = fmaf(min_of(sc, sb),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
+        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f * kScale, A_lo[n] * kScale), -dmin * B[n]);
+    }
+}
+
+// acc[n] += sum over the block of w * x_n (factored form).  For three or
+// more vectors one byte-to-float conversion per weight is shared by NV FMAs
+// (the binary16 operand trick of block_dot_mix would cost a register pair per
+// weight instead); one and two vectors go to block_dot_mix.
 template <int NV>
 __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk, int64_t xs,
                                           const float4 (&xq)[NV], float (&acc)[NV]) {
-    // Up to two vectors the nibbles go through v_fma_mix_f32; with more, one
-    // conversion per weight is shared by NV FMAs and the extra registers of
-    // the byte permutes cost more than they save.
-    constexpr bool MIX = NV <= 2;
-    constexpr float kScale = MIX ? 16777216.0f : 1.0f;  // 2^24 removes the binary16 subnormal scale
+    if constexpr (NV <= 2) {
+        block_dot_mix<NV>(b, xblk, xs, xq, acc);
+        return;
+    }
     const float d = half_lo(b[0].x);
     const float dmin = half_hi(b[0].x);
     const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
@@ -100,78 +243,28 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
         float tl[NV], th[NV];
 #pragma unroll
         for (int n = 0; n < NV; ++n) tl[n] = th[n] = 0.f;
-        if constexpr (MIX) {
-            // Low and high nibbles of each word in one pass, each sum spread
-            // over C chains (weight e of the sub-block into chain e mod C), so
-            // neighbouring FMAs do not wait on each other's results.
-            constexpr int C = 2;
-            float cl[NV][C], ch[NV][C];
 #pragma unroll
-            for (int n = 0; n < NV; ++n)
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+            const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
 #pragma unroll
-                for (int c = 0; c < C; ++c) cl[n][c] = ch[n][c] = 0.f;
+            for (int bb = 0; bb < 4; ++bb) {
+                const float q = ubyte(lo, bb);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // Bytes 0 and 2 of the word sit in the low byte of each 16-bit
-                // half, bytes 1 and 3 after a shift by 8: one AND per nibble
-                // set places two nibbles straight into the halves (four ANDs
-                // and a shift per eight weights).
-                const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-                const uint32_t v8 = v >> 8;
-                const half2v l02 = __builtin_bit_cast(half2v, and_mask(v, 0x000F000Fu));   // q0, q2
-                const half2v l13 = __builtin_bit_cast(half2v, and_mask(v8, 0x000F000Fu));  // q1, q3
-                const half2v h02 = __builtin_bit_cast(half2v, and_mask(v, 0x00F000F0u));   // 16 q
-                const half2v h13 = __builtin_bit_cast(half2v, and_mask(v8, 0x00F000F0u));
-                cfloat *xl = as_const(xblk + 64 * g + 4 * i);
-                cfloat *xh = as_const(xblk + 64 * g + 32 + 4 * i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {  // byte e of the word
-                    const int c = (4 * i + e) % C;
-                    const half2v ql = (e & 1) ? l13 : l02, qh = (e & 1) ? h13 : h02;
-                    const float wl = (e & 2) ? (float)ql.y : (float)ql.x;
-                    const float wh = (e & 2) ? (float)qh.y : (float)qh.x;
-#pragma unroll
-                    for (int n = 0; n < NV; ++n) {
-                        cl[n][c] = fmaf(wl, xl[n * xs + e], cl[n][c]);
-                        ch[n][c] = fmaf(wh, xh[n * xs + e], ch[n][c]);
-                    }
-                }
+                for (int n = 0; n < NV; ++n)
+                    tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
             }
+        }
 #pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                float a = cl[n][0], bs = ch[n][0];
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
+            const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
 #pragma unroll
-                for (int c = 1; c < C; ++c) {
-                    a += cl[n][c];
-                    bs += ch[n][c];
-                }
-                tl[n] = a;
-                th[n] = bs;
-            }
-        } else {
+            for (int bb = 0; bb < 4; ++bb) {
+                const float q = ubyte(hi, bb);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-                const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const float q = ubyte(lo, bb);
-#pragma unroll
-                    for (int n = 0; n < NV; ++n)
-                        tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-                const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const float q = ubyte(hi, bb);
-#pragma unroll
-                    for (int n = 0; n < NV; ++n)
-                        th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
-                }
+                for (int n = 0; n < NV; ++n)
+                    th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
             }
         }
         const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
@@ -192,7 +285,7 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
         for (int sb = 0; sb < 8; ++sb)
             B[n] = fmaf(min_of(sc, sb),
                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
-        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f * kScale, A_lo[n] * kScale), -dmin * B[n]);
+        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f, A_lo[n]), -dmin * B[n]);
     }
 }
 
@@ -682,11 +775,12 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
     return ((M + rows - 1) / rows) * ((K / 256 + WK - 1) / WK);
 }
 
-// Workgroup count: every resident slot (three workgroups per CU for one
-// vector), each taking a contiguous range of units; tiles cut by a range
-// boundary are finished in-kernel by their last contributor.  Measured
-// against one 64-row tile per workgroup (no cut tiles): 19.1 against 20.3 us
-// on the 17408 x 5120 matrix.
+// Workgroup count: every resident slot, at most two workgroups per CU, each
+// taking a contiguous range of units; tiles cut by a range boundary are
+// finished in-kernel by their last contributor.  On the 50 MB MLP matrices
+// two workgroups per CU measured 16.8-17.1 us against 17.8-19.1 us at three
+// and 18.3-20.0 us at four; one tile per workgroup (no cut tiles) was slower
+// still.
 template <int NV, int NMAT, int EPI>
 int groups_for(int64_t M, int64_t K, int *G) {
     int res = 0, cus = 0;
@@ -695,7 +789,7 @@ int groups_for(int64_t M, int64_t K, int *G) {
     if (o <= 0) {
         int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res, &cus);
         if (rc) return rc;
-        g = res;
+        g = std::min(res, 2 * cus);
     }
     *G = (int)std::max<int64_t>(1, std::min<int64_t>(g, units_of(M, K, NMAT)));
     return Q4K_OK;
