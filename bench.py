@@ -241,15 +241,18 @@ def main():
             for i in range(3):
                 q4k.gemv_batch(ws[i % ncop], X, Y)
             torch.cuda.synchronize()
-            pairs = []
-            for i in range(max(10, args.steps)):
+            # bursts of back-to-back launches on the cold copies, one event
+            # pair per burst (as for the MLP GEMVs above)
+            nrep = max(10, args.steps)
+            ts = []
+            for rep in range(3):
                 e0, e1 = ev(), ev()
                 e0.record(stream)
-                q4k.gemv_batch(ws[i % ncop], X, Y)
+                for i in range(nrep):
+                    q4k.gemv_batch(ws[i % ncop], X, Y)
                 e1.record(stream)
-                pairs.append((e0, e1))
-            torch.cuda.synchronize()
-            ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / nrep)
             t = float(np.mean(ts))
             roof_us = max(wbytes(M, K) / HBM_PEAK_GBS / 1e3, 2.0 * M * K * N / 157.3e12 * 1e6)
             res.append({"N": N, "us": t, "us_per_vector": t / N,
