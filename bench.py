@@ -19,7 +19,9 @@ Also measured and reported in the same line:
     (TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak), and prefill_gemm_short
     for short prompts, P = 16, 22, 27, 64;
   * gemv_batch: N = 1, 2, 4, 8, 16 vectors on the 17408x5120 weight;
-  * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound);
+  * gemv_small: the 512x1024 and 1024x512 GEMVs (latency-bound): per call
+    from an idle queue, and per call inside a replayed hipGraph next to a
+    one-kernel fill (the launch floor);
   * mlp_block: the same MLP block through q4k_mlp (RMSNorm gain, gate|up
     fused with the SwiGLU on device, down with the residual add);
   * gemv_q8_0_lm_head: the lm_head matmul in Q8_0 (248320x5120, 1.35 GB);
@@ -283,7 +285,37 @@ def main():
                 e1.record(stream)
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) * 1e3)
-            res.append({"M": M, "K": K, "us_median": float(np.median(ts)), "bytes": wbytes(M, K)})
+            # The per-call figure above includes the launch from an idle
+            # queue.  The kernel's own latency: NG back-to-back calls
+            # captured in one hipGraph, replayed; next to it the same for a
+            # one-kernel torch fill of y (the launch floor).
+            NG, R = 50, 10
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(stream)
+            with torch.cuda.stream(s2):
+                for _ in range(3):
+                    q4k.gemv(wd, xs, y)
+                    y.fill_(0.0)
+            torch.cuda.synchronize()
+            per_graph = {}
+            for name, fn in (("gemv", lambda: q4k.gemv(wd, xs, y)), ("fill", lambda: y.fill_(0.0))):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s2):
+                    for _ in range(NG):
+                        fn()
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for _ in range(R):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per_graph[name] = e0.elapsed_time(e1) * 1e3 / (R * NG)
+                del g
+            res.append({"M": M, "K": K, "us_median": float(np.median(ts)),
+                        "us_in_graph": per_graph["gemv"], "floor_fill_us_in_graph": per_graph["fill"],
+                        "bytes": wbytes(M, K)})
         out["gemv_small"] = res
 
     # ------------------------------------------------------------ Q8_0 GEMV
