@@ -76,6 +76,12 @@ def _load():
         L.oracle_dequant_q8_0.argtypes = [_p, _i64, _i64, _p]
         L.oracle_gemv_q8_0_rows_d.restype = ctypes.c_int
         L.oracle_gemv_q8_0_rows_d.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.oracle_dequant_q6_k_block.restype = None
+        L.oracle_dequant_q6_k_block.argtypes = [_p, _p]
+        L.oracle_dequant_q6_k.restype = ctypes.c_int
+        L.oracle_dequant_q6_k.argtypes = [_p, _i64, _i64, _p]
+        L.oracle_gemv_q6_k_rows_d.restype = ctypes.c_int
+        L.oracle_gemv_q6_k_rows_d.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
         L.oracle_mlp.restype = ctypes.c_int
         L.oracle_mlp.argtypes = [_p, _p, _p, _i64, _i64, _p, _p, ctypes.c_double, _p,
                                  _p, _p, _p, _p, _p, _p, _p]
@@ -234,6 +240,29 @@ def gemv_q8_0(w, x, M: int, K: int, rows=None) -> tuple[np.ndarray, np.ndarray]:
     n = nr if r is not None else M
     y, S = np.empty(n, np.float64), np.empty(n, np.float64)
     _check(_load().oracle_gemv_q8_0_rows_d(w.ctypes.data, xd.ctypes.data, M, K,
+                                           r.ctypes.data if r is not None else None, nr,
+                                           y.ctypes.data, S.ctypes.data))
+    return y, S
+
+
+def dequant_q6_k(w, M: int, K: int) -> np.ndarray:
+    """Q6_K matrix [M, K/256*210] -> f32 [M, K] (exact)."""
+    w = _u8(w)
+    out = np.empty((M, K), np.float32)
+    _check(_load().oracle_dequant_q6_k(w.ctypes.data, M, K, out.ctypes.data))
+    return out
+
+
+def gemv_q6_k(w, x, M: int, K: int, rows=None) -> tuple[np.ndarray, np.ndarray]:
+    """(y, S) in float64 for a Q6_K matrix: y = W x, S = sum |w x| per row."""
+    w = _u8(w)
+    x = np.asarray(x)
+    xd = np.ascontiguousarray(x if x.dtype == np.float64 else x.astype(np.float32), np.float64)
+    assert xd.size == K
+    r, nr = _rows(rows)
+    n = nr if r is not None else M
+    y, S = np.empty(n, np.float64), np.empty(n, np.float64)
+    _check(_load().oracle_gemv_q6_k_rows_d(w.ctypes.data, xd.ctypes.data, M, K,
                                            r.ctypes.data if r is not None else None, nr,
                                            y.ctypes.data, S.ctypes.data))
     return y, S

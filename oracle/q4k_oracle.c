@@ -287,6 +287,79 @@ int oracle_gemv_q8_0_rows_d(const uint8_t *w, const double *x, int64_t M, int64_
     return 0;
 }
 
+/* ---------------------------------------------------------------- Q6_K
+ * The six-bit GGUF k-quant that q4_k_m files use next to Q4_K for some
+ * tensors (the pages run the Qwen3.6-27B q4_k_m file: "Mac Qwen3.6-27B Metal
+ * Q4_K perf diagnosis", §1).  Layout per the public GGUF convention, 210
+ * bytes per 256 weights:
+ *   bytes   0..127  ql: the low four bits of the quants
+ *   bytes 128..191  qh: the high two bits
+ *   bytes 192..207  sixteen two's-complement int8 scales, one per 16
+ *                   consecutive weights
+ *   bytes 208..209  d, binary16 (little-endian)
+ * Write weight k as 128h + 32c + l (h in 0..1, c in 0..3, l in 0..31).  Its
+ * low four bits are the low nibble (c = 0, 1) or the high nibble (c = 2, 3)
+ * of ql[64h + 32(c mod 2) + l]; its high two bits are bits 2c and 2c+1 of
+ * qh[32h + l].  With q_k in 0..63 the value is
+ *   w_k = d * (sc[k / 16] * (q_k - 32)),
+ * the integer product taken first.  It has at most 12 significant bits and d
+ * at most 11, so w_k is exact in f32 (no rounding in any order; the stated
+ * order fixes only the sign of a zero). */
+static int check_shape_q6(int64_t M, int64_t K) {
+    return (M < 0 || K <= 0 || K % 256 != 0) ? -2 : 0;
+}
+
+static int q6_quant(const uint8_t *b, int k) {
+    const int h = k / 128, c = (k % 128) / 32, l = k % 32;
+    const int lo_byte = b[64 * h + 32 * (c % 2) + l];
+    const int lo = c < 2 ? (lo_byte & 15) : (lo_byte >> 4);
+    const int hi = (b[128 + 32 * h + l] >> (2 * c)) & 3;
+    return lo | (hi << 4);
+}
+
+void oracle_dequant_q6_k_block(const uint8_t *b, float out[256]) {
+    const double d = oracle_half_to_double((uint16_t)(b[208] | (b[209] << 8)));
+    for (int k = 0; k < 256; ++k) {
+        const int sc = (int8_t)b[192 + k / 16];
+        out[k] = (float)(d * (double)(sc * (q6_quant(b, k) - 32)));
+    }
+}
+
+int oracle_dequant_q6_k(const uint8_t *w, int64_t M, int64_t K, float *out) {
+    if (check_shape_q6(M, K)) return -2;
+    const int64_t nb = K / 256;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; ++r)
+        for (int64_t j = 0; j < nb; ++j)
+            oracle_dequant_q6_k_block(w + (r * nb + j) * 210, out + r * K + j * 256);
+    return 0;
+}
+
+/* y[r] = sum_k w_rk x_k in double, and S[r] = sum_k |w_rk x_k| (either may
+ * be NULL), for the listed rows (rows NULL: all M). */
+int oracle_gemv_q6_k_rows_d(const uint8_t *w, const double *x, int64_t M, int64_t K,
+                            const int64_t *rows, int64_t nrows, double *y, double *S) {
+    if (check_shape_q6(M, K)) return -2;
+    const int64_t nb = K / 256, n = rows ? nrows : M;
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t r = rows ? rows[t] : t;
+        double acc = 0.0, sab = 0.0;
+        float v[256];
+        for (int64_t j = 0; j < nb; ++j) {
+            oracle_dequant_q6_k_block(w + (r * nb + j) * 210, v);
+            for (int i = 0; i < 256; ++i) {
+                const double p = (double)v[i] * x[j * 256 + i];
+                acc += p;
+                sab += fabs(p);
+            }
+        }
+        if (y) y[t] = acc;
+        if (S) S[t] = sab;
+    }
+    return 0;
+}
+
 double oracle_rms(const double *v, int64_t n, double eps) {
     double ss = 0.0;
     for (int64_t i = 0; i < n; ++i) ss += v[i] * v[i];

@@ -60,6 +60,13 @@ int oracle_dequant_q8_0(const uint8_t *w, int64_t M, int64_t K, float *out);
 int oracle_gemv_q8_0_rows_d(const uint8_t *w, const double *x, int64_t M, int64_t K,
                             const int64_t *rows, int64_t nrows, double *y, double *S);
 
+/* Q6_K (210 bytes per 256 weights: ql[128], qh[64], int8 sc[16], binary16 d;
+ * w = d * (sc * (q - 32)), q six bits). */
+void oracle_dequant_q6_k_block(const uint8_t *b, float out[256]);
+int oracle_dequant_q6_k(const uint8_t *w, int64_t M, int64_t K, float *out);
+int oracle_gemv_q6_k_rows_d(const uint8_t *w, const double *x, int64_t M, int64_t K,
+                            const int64_t *rows, int64_t nrows, double *y, double *S);
+
 /* Root mean square with epsilon: sqrt(mean(v^2) + eps). */
 double oracle_rms(const double *v, int64_t n, double eps);
 

@@ -53,6 +53,9 @@ def _load():
         lib.synth_q4k_blocks.restype = ctypes.c_int
         lib.synth_q4k_blocks.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                          ctypes.c_void_p, ctypes.c_double, ctypes.c_double]
+        lib.synth_q6_k_blocks.restype = ctypes.c_int
+        lib.synth_q6_k_blocks.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                          ctypes.c_void_p, ctypes.c_double, ctypes.c_double]
         lib.synth_q8_0_blocks.restype = ctypes.c_int
         lib.synth_q8_0_blocks.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                           ctypes.c_void_p, ctypes.c_double, ctypes.c_double]
@@ -110,6 +113,24 @@ def q8_0_weight(k: int, M: int, K: int, lo: float = D_LO, hi: float = D_HI) -> n
     out = np.empty((M, nb * Q8_BLOCK_BYTES), dtype=np.uint8)
     if M:
         rc = _load().synth_q8_0_blocks(k, 0, M * nb, out.ctypes.data, lo, hi)
+        if rc != 0:
+            raise ValueError("d range outside binary16 normals")
+    return out
+
+
+Q6_QK, Q6_BLOCK_BYTES = 256, 210
+
+
+def q6_k_weight(k: int, M: int, K: int, lo: float = D_LO, hi: float = D_HI) -> np.ndarray:
+    """A random Q6_K matrix with K columns: uint8 [M, K/256*210], row-major, each
+    row K/256 consecutive 210-byte blocks (quant low bits, quant high bits,
+    sixteen int8 scales, binary16 d; all bytes uniform except d ~ U(lo, hi))."""
+    if K % Q6_QK:
+        raise ValueError("K must be a multiple of 256")
+    nb = K // Q6_QK
+    out = np.empty((M, nb * Q6_BLOCK_BYTES), dtype=np.uint8)
+    if M:
+        rc = _load().synth_q6_k_blocks(k, 0, M * nb, out.ctypes.data, lo, hi)
         if rc != 0:
             raise ValueError("d range outside binary16 normals")
     return out

@@ -23,6 +23,7 @@
  * bijective packing, so the distribution does not depend on the layout.
  *
  * Q8_0 block stream: see synth_q8_0_blocks.
+ * Q6_K block stream: see synth_q6_k_blocks.
  *
  * Normal activations: Box–Muller (G. E. P. Box, M. E. Muller, 1958) on the
  * word pair (2i, 2i+1), computed in double and rounded once to f32.
@@ -112,6 +113,30 @@ int synth_q8_0_blocks(uint64_t key, uint64_t block0, uint64_t nblocks,
 }
 
 /* n standard-normal f32 values from the stream keyed by `key`. */
+/* Q6_K block stream: per block b, word 27b gives d = U(lo, hi) rounded to
+ * binary16 (stored in the last two bytes), and words 27b+1 .. 27b+26 give
+ * the 208 bytes before it (quant low bits, quant high bits and the sixteen
+ * int8 scales, all uniform), eight bytes per word, the last word's final
+ * six bytes unused. */
+int synth_q6_k_blocks(uint64_t key, uint64_t block0, uint64_t nblocks,
+                      uint8_t *out, double lo, double hi) {
+    int bad = 0;
+    #pragma omp parallel for schedule(static) reduction(|:bad)
+    for (int64_t bi = 0; bi < (int64_t)nblocks; ++bi) {
+        uint64_t b = block0 + (uint64_t)bi;
+        uint8_t *p = out + (uint64_t)bi * 210u;
+        uint64_t base = b * 27u;
+        uint16_t hd = half_bits_rne(lo + (hi - lo) * u01(sm64_word(key, base + 0)));
+        if (hd == 0xFFFF) bad = 1;
+        for (int j = 0; j < 26; ++j) {
+            uint64_t w = sm64_word(key, base + 1 + (uint64_t)j);
+            memcpy(p + 8 * j, &w, 8);
+        }
+        p[208] = (uint8_t)(hd & 0xFF); p[209] = (uint8_t)(hd >> 8);
+    }
+    return bad ? -1 : 0;
+}
+
 void synth_normal_f32(uint64_t key, uint64_t n, float *out) {
     uint64_t pairs = (n + 1) / 2;
     #pragma omp parallel for schedule(static)

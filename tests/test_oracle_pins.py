@@ -612,3 +612,123 @@ def test_q8_0_gemv_bruteforce_exact_rationals(M, K):
                 q = int(b[2 + i]) - 256 if b[2 + i] >= 128 else int(b[2 + i])
                 acc += d * q * Fraction(float(x[32 * j + i]))
         assert abs(Fraction(y[r]) - acc) <= Fraction(1, 2 ** 40) * (1 + abs(acc))
+
+
+# ---------------------------------------------------------------- Q6_K
+
+def _q6_fixture():
+    """The hand-worked Q6_K blocks of tests/golden/q6_k_blocks.txt."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "q6_k_blocks.txt")
+    out = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        bid, dhex, ql, qh, sc, exp = [f.strip() for f in line.split("|")]
+        if ql == "ramp4":
+            qlb = [(i % 16) | ((15 - i % 16) << 4) for i in range(128)]
+        else:
+            qlb = [int(ql, 16)] * 128
+        qhb = [int(qh, 16)] * 64
+        if sc == "idx1":
+            scv = [g + 1 for g in range(16)]
+        elif sc == "alt":
+            scv = [-1 if g % 2 == 0 else 2 for g in range(16)]
+        else:
+            scv = [int(sc)] * 16
+        d = int(dhex, 16)
+        blk = np.array(qlb + qhb + [v & 0xFF for v in scv] + [d & 0xFF, d >> 8], np.uint8)
+        assert blk.size == 210
+        kind, *vals = exp.split()
+        if kind == "all":
+            want = vals * 256
+        elif kind == "groups":
+            want = [v for v in vals for _ in range(16)]
+        else:
+            want = vals * 2
+        assert len(want) == 256, bid
+        out.append((bid, blk, want))
+    return out
+
+
+@pytest.mark.parametrize("item", _q6_fixture(), ids=lambda it: it[0])
+def test_q6_k_worked_blocks(item):
+    """Scale per 16 weights, nibble order (low nibbles of ql for the first two
+    32-weight quarters of each half, high nibbles for the last two), qh bit
+    pairs 2c, 2c+1, d last and little-endian, subnormal d, negative d and
+    scales, and the sign of zero of d * (sc * (q - 32))."""
+    bid, blk, exp = item
+    got = oracle.dequant_q6_k(blk[None, :], 1, 256)[0]
+    for i, e in enumerate(exp):
+        want = np.float32(-0.0) if e == "-0" else np.float32(float(e))
+        assert _f32_bits(got[i]) == _f32_bits(want), (bid, i, got[i], e)
+
+
+def test_q6_k_dequant_vs_numpy_decoding():
+    """Random blocks decoded a second way: numpy's binary16 and int8 views and
+    array-wide bit slicing of the same bytes, multiplied in double, agree with
+    the oracle bit for bit (every value is exact in f32)."""
+    M, K = 23, 1024
+    w = synth.q6_k_weight(synth.key(9, 940), M, K)
+    blocks = w.reshape(-1, 210)
+    ql, qh = blocks[:, :128].astype(np.int64), blocks[:, 128:192].astype(np.int64)
+    sc = blocks[:, 192:208].view(np.int8).astype(np.int64)
+    d = blocks[:, 208:210].copy().view(np.float16).astype(np.float64)[:, 0]
+    q = np.empty((blocks.shape[0], 256), np.int64)
+    for h in range(2):
+        for c in range(4):
+            src = ql[:, 64 * h + 32 * (c % 2): 64 * h + 32 * (c % 2) + 32]
+            low = (src & 15) if c < 2 else (src >> 4)
+            high = (qh[:, 32 * h: 32 * h + 32] >> (2 * c)) & 3
+            q[:, 128 * h + 32 * c: 128 * h + 32 * c + 32] = low | (high << 4)
+    ints = np.repeat(sc, 16, axis=1) * (q - 32)
+    ref = (d[:, None] * ints.astype(np.float64)).astype(np.float32).reshape(M, K)
+    got = oracle.dequant_q6_k(w, M, K)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(ref.astype(np.float64), d[:, None].repeat(256, 1).reshape(M, K) *
+                          ints.reshape(M, K))   # no rounding anywhere
+
+
+def test_q6_k_gemv_closed_forms():
+    """Zero x gives exact zeros; a one-hot x returns the dequantised column;
+    the all-63 block (K2: w = 31) tiled k times with x = 1 sums to 256 k 31."""
+    M, K = 40, 1024
+    w = synth.q6_k_weight(synth.key(9, 941), M, K)
+    y, S = oracle.gemv_q6_k(w, np.zeros(K, np.float32), M, K)
+    assert np.all(y == 0.0) and np.all(S == 0.0)
+    deq = oracle.dequant_q6_k(w, M, K)
+    for k in (0, 15, 16, 127, 128, 255, 256, 1023):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y, _ = oracle.gemv_q6_k(w, x, M, K)
+        assert np.array_equal(y, deq[:, k].astype(np.float64))
+    blk = [b for b in _q6_fixture() if b[0] == "K2"][0][1]
+    tiled = np.tile(blk, 4)[None, :]
+    y, _ = oracle.gemv_q6_k(tiled, np.ones(1024, np.float32), 1, 1024)
+    assert y[0] == 4 * 256 * 31
+
+
+@pytest.mark.parametrize("M,K", [(2, 256), (1, 512)])
+def test_q6_k_gemv_bruteforce_exact_rationals(M, K):
+    """Tiny matrices: the exact rational sum, decoded from the raw bytes with
+    Python integers, is within the double rounding of the oracle's result."""
+    w = synth.q6_k_weight(synth.key(9, 942 + K), M, K)
+    x = synth.normal(synth.key(9, 943), K)
+    y, _ = oracle.gemv_q6_k(w, x, M, K)
+    for r in range(M):
+        acc = Fraction(0)
+        for j in range(K // 256):
+            b = [int(v) for v in w[r, 210 * j:210 * (j + 1)]]
+            h16 = b[208] | (b[209] << 8)
+            e, m, s = (h16 >> 10) & 31, h16 & 1023, -1 if h16 & 0x8000 else 1
+            d = s * (Fraction(m, 1024) * Fraction(2) ** -14 if e == 0 else
+                     Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15))
+            for k in range(256):
+                h, c, l = k // 128, (k % 128) // 32, k % 32
+                lo = b[64 * h + 32 * (c % 2) + l]
+                lo = lo & 15 if c < 2 else lo >> 4
+                hi = (b[128 + 32 * h + l] >> (2 * c)) & 3
+                sc = b[192 + k // 16] - 256 if b[192 + k // 16] >= 128 else b[192 + k // 16]
+                acc += d * sc * ((lo | (hi << 4)) - 32) * Fraction(float(x[256 * j + k]))
+        assert abs(Fraction(y[r]) - acc) <= Fraction(1, 2 ** 40) * (1 + abs(acc))

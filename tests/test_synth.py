@@ -62,3 +62,23 @@ def test_normals_moments_and_determinism():
     x = synth.normal(synth.key(1, synth.ACT_BASE), 200001)
     assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
     assert np.array_equal(x[:1000], synth.normal(synth.key(1, synth.ACT_BASE), 1000))
+
+
+def test_q6_k_blocks_counter_layout_and_ranges():
+    """Block b of a Q6_K stream is word 27b (d) and words 27b+1 .. 27b+26
+    (the 208 bytes before d, little-endian); d is a normal binary16 in
+    [1e-4, 1e-3] and the other bytes look uniform."""
+    k = synth.key(2, 7)
+    w = synth.q6_k_weight(k, 3, 512)                 # 6 blocks
+    blocks = w.reshape(-1, 210)
+    for b in range(blocks.shape[0]):
+        body = b"".join(synth.word(k, 27 * b + 1 + j).to_bytes(8, "little") for j in range(26))
+        assert bytes(blocks[b, :208]) == body[:208]
+    big = synth.q6_k_weight(synth.key(2, 8), 128, 4096).reshape(-1, 210)
+    h = big[:, 208].astype(np.uint16) | (big[:, 209].astype(np.uint16) << 8)
+    v = h.view(np.float16).astype(np.float64)
+    assert v.min() >= 1e-4 * (1 - 2 ** -11) and v.max() <= 1e-3 * (1 + 2 ** -11)
+    counts = np.bincount(big[:, :208].ravel(), minlength=256)
+    exp = big[:, :208].size / 256
+    assert ((counts - exp) ** 2 / exp).sum() < 400
+    assert np.array_equal(synth.q6_k_weight(synth.key(2, 8), 128, 4096).reshape(-1, 210), big)
