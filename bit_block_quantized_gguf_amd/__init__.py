@@ -28,7 +28,8 @@ BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS = range(7)
 
 # Every symbol include/q4k.h declares (checked by the CPU test suite).
 EXPORTS = (
-    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_gemv_q8_0", "q4k_mlp",
+    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_gemv_q8_0", "q4k_gemv_q6_k",
+    "q4k_mlp",
     "q4k_gemv_batch",
     "q4k_gemm",
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
@@ -86,6 +87,7 @@ def load(path: str | None = None):
     L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p]
     L.q4k_mlp.argtypes = [p, p, p, i64, i64, p, p, ctypes.c_float, p, p, p, p]
     L.q4k_gemv_q8_0.argtypes = [p, p, p, i64, i64, p]
+    L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
     L.q4k_decode_stack.argtypes = [p, p, p, p]
     L.q4k_decode_stack_buffer.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(i64)]
@@ -207,6 +209,31 @@ def gemv_q8_0(w, x, y=None, M: int | None = None, K: int | None = None):
         y = torch.empty(M, dtype=torch.float32, device=w.device)
     _dev_tensor(y, torch.float32, "y")
     check(load().q4k_gemv_q8_0(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    return y
+
+
+Q6_BLOCK_BYTES = 210
+
+
+def gemv_q6_k(w, x, y=None, M: int | None = None, K: int | None = None):
+    """y = W x for a Q6_K weight [M, K/256*210] uint8 (K a multiple of 1024)."""
+    torch = _torch()
+    if M is None:
+        M, rb = w.shape
+        if rb % Q6_BLOCK_BYTES:
+            raise ValueError("row length is not a whole number of 210-byte blocks")
+        K = rb // Q6_BLOCK_BYTES * 256
+    _dev_tensor(w, torch.uint8, "w")
+    if w.numel() != M * (K // 256) * Q6_BLOCK_BYTES:
+        raise ValueError("w holds %d bytes, a %dx%d Q6_K matrix needs %d"
+                         % (w.numel(), M, K, M * (K // 256) * Q6_BLOCK_BYTES))
+    _dev_tensor(x, torch.float32, "x")
+    if x.numel() != K:
+        raise ValueError("x must have K=%d elements" % K)
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=w.device)
+    _dev_tensor(y, torch.float32, "y")
+    check(load().q4k_gemv_q6_k(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
     return y
 
 

@@ -248,6 +248,36 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
     return launch_gemm((const uint8_t *)w, X, Y, M, K, P, L, ws, (hipStream_t)stream);
 }
 
+int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream) {
+    clear_error();
+    Q4K_TRY(check_mk(M, K));
+    if (K % 1024 != 0)
+        return fail(Q4K_ESHAPE, "q4k_gemv_q6_k: K must be a multiple of 1024 (K=%lld)", (long long)K);
+    if (M == 0) return Q4K_OK;
+    Q4K_TRY(check_ptr(w, "w"));
+    Q4K_TRY(check_ptr(x, "x"));
+    Q4K_TRY(check_ptr(y, "y"));
+    Q4K_TRY(check_device());
+    const GemvLaunch L = choose_gemv_q6_launch(M, K);
+    Workspace ws;
+    Q4K_TRY(stream_workspace((hipStream_t)stream, gemv_partial_floats(L, M, 1, 1),
+                             gemv_counters(M), &ws));
+    GemvParams p = {};
+    p.w0 = (const uint8_t *)w;
+    p.x = x;
+    p.x_stride = K;
+    p.y = y;
+    p.y_stride = M;
+    p.M = (int32_t)M;
+    p.K = (int32_t)K;
+    p.nb = (int32_t)(K / 256);
+    p.row_bytes = (K / 256) * 210;
+    p.ks = L.ks;
+    p.ws = ws.partials;
+    p.cnt = ws.counters;
+    return launch_gemv_q6(p, L, (hipStream_t)stream);
+}
+
 int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));

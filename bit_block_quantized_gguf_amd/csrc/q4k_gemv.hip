@@ -726,6 +726,168 @@ __global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, co
     }
 }
 
+// ---------------------------------------------------------------------------
+// Q6_K GEMV (one vector).  Q6_K stores 256 weights in 210 bytes (public GGUF
+// convention; the six-bit k-quant that q4_k_m files carry next to Q4_K):
+// ql[128] (low four bits of the quants), qh[64] (high two bits), sixteen
+// int8 scales (one per 16 weights), then a binary16 d.  Weight
+// k = 128h + 32c + l takes the low (c < 2) or high (c >= 2) nibble of
+// ql[64h + 32(c mod 2) + l] and bits 2c, 2c+1 of qh[32h + l]; with q in 0..63,
+// w = d * sc[k/16] * (q - 32).  Per block the kernel forms
+//    d * (sum_g sc_g * T_g  -  32 * sum_g sc_g * X_g)
+// with T_g = sum(q x) and X_g = sum(x) over the 16 weights of group g.
+//
+// Same skeleton as the Q4_K kernel: a unit is 64 rows x 4 blocks (one
+// 840-byte run per row) and wave w takes block w of every row, one row per
+// lane, activations through SGPRs.  A row of K/256 blocks is 8-byte aligned
+// when K is a multiple of 1024 (the entry point requires it), so the unit is
+// copied in 8-byte chunks; LDS rows are padded to 844 bytes (211 dwords, an
+// odd count, so the row-strided dword reads below are conflict-free).  Odd
+// blocks start 2 bytes into a dword: a wave reads the 54 aligned dwords
+// covering its block and realigns them with one v_alignbit_b32 each.
+constexpr int Q6_BB = 210;                       // bytes per block
+constexpr int Q6_SEG = WK * Q6_BB;               // 840-byte row run
+constexpr int Q6_SEGP = Q6_SEG + 4;              // LDS row stride (211 dwords)
+constexpr int Q6_CH_ROW = Q6_SEG / 8;            // 105 eight-byte chunks per row
+constexpr int Q6_CH_UNIT = 64 * Q6_CH_ROW;       // 6720 chunks per unit
+constexpr int Q6_CH_THREAD = (Q6_CH_UNIT + 64 * WK - 1) / (64 * WK);  // 27 (the last for wave 0 only)
+static_assert(Q6_SEG % 8 == 0 && Q6_SEGP % 4 == 0 && (Q6_SEGP / 4) % 2 == 1, "Q6_K staging");
+static_assert(Q6_CH_UNIT - (Q6_CH_THREAD - 1) * 64 * WK == 64, "last copy slot = wave 0");
+
+__global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, const Units un) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * Q6_SEGP];
+    __shared__ float red[WK][1][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x;
+    const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
+
+    int crow[Q6_CH_THREAD], coff[Q6_CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < Q6_CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;  // past Q6_CH_UNIT only in the last slot (waves 1..3)
+        crow[i] = q / Q6_CH_ROW;
+        coff[i] = 8 * (q - crow[i] * Q6_CH_ROW);
+    }
+    uint2 reg[Q6_CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < Q6_CH_THREAD; ++i) reg[i] = make_uint2(0u, 0u);
+    // every unit is whole: K/256 is a multiple of 4
+    auto fetch = [&](int t, int k) {
+        const int rmax = min(63, p.M - 1 - t * 64);
+        const uint8_t *b0 = p.w0 + (int64_t)t * 64 * p.row_bytes + (int64_t)k * Q6_SEG;
+#pragma unroll
+        for (int i = 0; i < Q6_CH_THREAD; ++i) {
+            if (i * 64 * WK + 64 * wave >= Q6_CH_UNIT) continue;  // wave-uniform
+            const uint32_t off =
+                (uint32_t)min(crow[i], rmax) * (uint32_t)p.row_bytes + (uint32_t)coff[i];
+            reg[i] = *reinterpret_cast<const uint2 *>(b0 + off);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < Q6_CH_THREAD; ++i) {
+            if (i * 64 * WK + 64 * wave >= Q6_CH_UNIT) continue;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&stage[crow[i] * Q6_SEGP + coff[i]]);
+            dst[0] = reg[i].x;  // 4-byte aligned only (odd rows): two dword stores
+            dst[1] = reg[i].y;
+        }
+    };
+
+    float acc = 0.f;
+    int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);
+    fetch(t, k);
+    commit();
+    __syncthreads();
+    bool seg_first = k == 0;
+    for (int64_t u = ua; u < ub; ++u) {
+        const int j = k * WK + wave;  // this wave's block
+        const bool last_of_tile = k + 1 == un.upt;
+        const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
+        // group sums of x first (lanes 4g .. 4g+3 hold group g's 16 values),
+        // then the next unit's loads
+        const float4 xq = *reinterpret_cast<const float4 *>(p.x + 256 * (int64_t)j + 4 * lane);
+        const bool more = u + 1 < ub;
+        if (more) fetch(tn, kn);
+        {
+            const int off = wave * Q6_BB;  // block start inside the row run
+            const uint32_t *lp =
+                reinterpret_cast<const uint32_t *>(&stage[lane * Q6_SEGP + (off & ~3)]);
+            const int sh = (off & 3) * 8;  // 0 or 16
+            uint32_t B[53];
+            {
+                uint32_t D[54];
+#pragma unroll
+                for (int i = 0; i < 54; ++i) D[i] = lp[i];
+#pragma unroll
+                for (int i = 0; i < 53; ++i) B[i] = __builtin_amdgcn_alignbit(D[i + 1], D[i], sh);
+            }
+            float s = (xq.x + xq.y) + (xq.z + xq.w);
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            cfloat *xb = as_const(p.x + 256 * (int64_t)j);
+            float A = 0.f, Bs = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {  // group 8h + 2c + half
+                        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+                        for (int i = 4 * half; i < 4 * half + 4; ++i) {
+                            const uint32_t QL = B[16 * h + 8 * (c & 1) + i];
+                            const uint32_t QH = B[32 + 8 * h + i];
+                            const uint32_t lo = (c < 2 ? QL : QL >> 4) & 0x0F0F0F0Fu;
+                            const uint32_t hi = (c < 1 ? QH << 4 : c < 2 ? QH << 2 : c < 3 ? QH : QH >> 2) &
+                                                0x30303030u;
+                            uint32_t q4 = lo | hi;  // four six-bit quants, one per byte
+                            asm("" : "+v"(q4));     // keeps one byte conversion per weight
+                            const int kx = 128 * h + 32 * c + 4 * i;
+                            t0 = fmaf(ubyte(q4, 0), xb[kx + 0], t0);
+                            t1 = fmaf(ubyte(q4, 1), xb[kx + 1], t1);
+                            t0 = fmaf(ubyte(q4, 2), xb[kx + 2], t0);
+                            t1 = fmaf(ubyte(q4, 3), xb[kx + 3], t1);
+                        }
+                        const int grp = 8 * h + 2 * c + half;
+                        const float scg =
+                            (float)(int8_t)((B[48 + (grp >> 2)] >> (8 * (grp & 3))) & 0xFFu);
+                        A = fmaf(scg, t0 + t1, A);
+                        Bs = fmaf(scg,
+                                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 4 * grp)),
+                                  Bs);
+                    }
+            const float d = __half2float(__ushort_as_half((unsigned short)(B[52] & 0xFFFFu)));
+            acc = fmaf(d, fmaf(-32.0f, Bs, A), acc);
+        }
+        const bool seg_end = !more || last_of_tile;
+        if (seg_end) {
+            red[wave][0][lane] = acc;
+            acc = 0.f;
+        }
+        __syncthreads();
+        if (seg_end && wave == 0) {
+            float tot[1] = {red[0][0][lane]};
+#pragma unroll
+            for (int w = 1; w < WK; ++w) tot[0] += red[w][0][lane];
+            if (seg_first && last_of_tile)
+                epilogue<1, 1, EPI_PLAIN>(p, t * 64, lane, tot, 1.f);
+            else
+                finish_split_tile<1, 1, EPI_PLAIN>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot,
+                                                   1.f);
+        }
+        if (seg_end) seg_first = true;
+        t = tn;
+        k = kn;
+        if (more) commit();
+        __syncthreads();
+    }
+}
+
 // xg[i] = x[i] * (1 + w[i]) (w null: xg not written) and the sums of squares
 // of x per 32 elements, one element per thread.
 __global__ __launch_bounds__(64) void norm_gain_kernel(const float *__restrict__ x,
@@ -892,6 +1054,37 @@ int launch_gemv_q8(const GemvParams &p, const GemvLaunch &L, hipStream_t stream)
     un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL(gemv_q8_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
+    Q4K_HIP(hipGetLastError());
+    return Q4K_OK;
+}
+
+GemvLaunch choose_gemv_q6_launch(int64_t M, int64_t K) {
+    GemvLaunch L;
+    L.wk = WK;
+    const int64_t units = ((M + 63) / 64) * (K / 256 / WK);
+    int G = g_override_groups.load(), res = 0, cus = 0;
+    if (G <= 0) {
+        if (resident_groups((const void *)gemv_q6_kernel, &res, &cus) == Q4K_OK)
+            G = std::min(res, 2 * cus);
+        else {
+            clear_error();
+            G = 512;
+        }
+    }
+    L.ks = (int)std::max<int64_t>(1, std::min<int64_t>(G, units));
+    return L;
+}
+
+int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
+    const int64_t tiles = (p.M + 63) / 64;
+    if (p.nb % WK != 0) return fail(Q4K_ESHAPE, "gemv_q6_k: K must be a multiple of 1024");
+    Units un;
+    un.upt = p.nb / WK;
+    un.U = tiles * un.upt;
+    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
+    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
+    hipLaunchKernelGGL(gemv_q6_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }

@@ -92,6 +92,11 @@ int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch
 GemvLaunch choose_gemv_q8_launch(int64_t M, int64_t K);
 int launch_gemv_q8(const GemvParams &p, const GemvLaunch &L, hipStream_t stream);
 
+// Q6_K GEMV (one vector, plain output): launch shape and launch.  p.nb is the
+// number of 256-weight blocks per row (a multiple of 4), p.row_bytes nb * 210.
+GemvLaunch choose_gemv_q6_launch(int64_t M, int64_t K);
+int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream);
+
 // Per-32-element sums of squares of v[0..n) (used to seed the stack).
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
 

@@ -108,6 +108,21 @@ int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void
 int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
 
 /*
+ * Q6_K GEMV: y[i] = sum_k w_ik * x[k] for a Q6_K matrix (public GGUF layout,
+ * the six-bit k-quant that q4_k_m files carry next to Q4_K; the pages run the
+ * Qwen3.6-27B q4_k_m file, "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §1):
+ * 210 bytes per 256 weights, ql[128] (low four bits of the quants), qh[64]
+ * (high two bits), sixteen int8 scales (one per 16 weights), then a
+ * little-endian binary16 d; w = d * sc * (q - 32) with q in 0..63; rows of
+ * K / 256 consecutive blocks.  K must be a positive multiple of 1024 (rows
+ * of a multiple of four blocks, so row runs stay 8-byte aligned; every
+ * Qwen3.6-27B shape qualifies), otherwise Q4K_ESHAPE.  x f32 [K], y f32 [M];
+ * w, x, y 16-byte aligned.  f32 accumulation within the q4k_gemv bound.
+ * Other error codes as q4k_gemv.
+ */
+int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+
+/*
  * MLP block of one token (the model's SwiGLU feed-forward with its RMSNorm in
  * the (1 + w) form, "Qwen3.6-27B on Apple M3 Pro — the llama.cpp parity bar",
  * model description and the fak-native status list; the gate/up/down matmuls
