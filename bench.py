@@ -25,6 +25,7 @@ Also measured and reported in the same line:
   * mlp_block: the same MLP block through q4k_mlp (RMSNorm gain, gate|up
     fused with the SwiGLU on device, down with the residual add);
   * gemv_q8_0_lm_head: the lm_head matmul in Q8_0 (248320x5120, 1.35 GB);
+  * gemv_q6_k_mlp: Q6_K GEMVs on the two MLP shapes (73 MB each, cold);
   * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
     launch over its HIP-event duration, against 8 TB/s;
   * cpu_baseline: the CPU oracle (double precision, all host cores) on the
@@ -75,7 +76,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="gemv,batch,small,q8,gemm,stack,cpu",
+    ap.add_argument("--sections", default="gemv,batch,small,q8,q6,gemm,stack,cpu",
                     help="comma list of gemv,batch,small,gemm,stack,cpu (and copy: the "
                          "256 MiB device copy that calibrates the PMC traffic counters)")
     ap.add_argument("--copies", type=int, default=4, help="cold-rotation copies per MLP matrix")
@@ -346,6 +347,37 @@ def main():
         log("q8_0 lm_head: %.1f us, %.0f GB/s" % (t, qb / t / 1e3))
         del wq
         torch.cuda.empty_cache()
+
+    if "q6" in sections:
+        # Q6_K, the other k-quant of q4_k_m files, on the two MLP shapes (73 MB
+        # each; 4 copies each in rotation, 585 MB, above the Infinity Cache)
+        res = []
+        for si, (name, M, K) in enumerate((("17408x5120", wl.INTER, wl.HIDDEN),
+                                           ("5120x17408", wl.HIDDEN, wl.INTER))):
+            hw = synth.q6_k_weight(synth.key(8, 100 + si), M, K)
+            wc = [upload(hw) for _ in range(4)]
+            x6 = upload(synth.activations(8, 1, K)[0])
+            y6 = torch.empty(M, device=dev)
+            for i in range(3):
+                q4k.gemv_q6_k(wc[i % 4], x6, y6)
+            torch.cuda.synchronize()
+            reps = []
+            for rep in range(3):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                for i in range(args.steps):
+                    q4k.gemv_q6_k(wc[i % 4], x6, y6)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                reps.append(e0.elapsed_time(e1) * 1e3 / args.steps)
+            qb = hw.size + 4 * (M + K)
+            t = float(np.mean(reps))
+            res.append({"shape": name, "M": M, "K": K, "us": t, "bytes": qb, "GBps": qb / t / 1e3,
+                        "frac_hbm": qb / t / 1e3 / HBM_PEAK_GBS})
+            log("q6_k %s: %.1f us, %.0f GB/s" % (name, t, qb / t / 1e3))
+            del wc
+            torch.cuda.empty_cache()
+        out["gemv_q6_k_mlp"] = res
 
     # ------------------------------------------------------------ prefill GEMM
     if "gemm" in sections:
