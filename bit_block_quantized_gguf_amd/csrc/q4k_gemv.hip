@@ -83,9 +83,11 @@ struct XStage {
     float l[NV][4 * SW], h[NV][4 * SW];
 };
 
-// Stage st of a block covers words 1 + 2g + ..., i.e. quant words
-// i = SW*(st % (8/SW)) ... of group g = st / (8/SW); its activations are
-// x[64g + 4i + e] (low nibbles) and x[64g + 32 + 4i + e] (high nibbles).
+// Stage st of a block covers the SW quant words i = SW*(st mod 8/SW) ..
+// +SW-1 of 32-byte group g = st / (8/SW) (word i of group g is dword i mod 4
+// of the block's 16-byte chunk 1 + 2g + i/4); its activations are
+// x[64g + 4i + e] (low nibbles) and x[64g + 32 + 4i + e] (high nibbles),
+// e = 0..3.
 template <int NV, int SW>
 __device__ __forceinline__ void load_stage(XStage<NV, SW> &s, cfloat *xb, int64_t xs, int st) {
     constexpr int SPG = 8 / SW;  // stages per group
@@ -105,9 +107,10 @@ __device__ __forceinline__ void load_stage(XStage<NV, SW> &s, cfloat *xb, int64_
 }
 
 // One quant word (8 weights) of a stage: four ANDs and a shift place the
-// nibbles into binary16 halves (q[0..1]: bytes 0 and 2, q[2..3]: bytes 1 and
-// 3, low nibbles then 16 x high nibbles); then one v_fma_mix_f32 per weight
-// into two chains per sub-block (even and odd bytes).
+// nibbles into binary16 halves (l02 / l13: the low nibbles of bytes 0, 2 and
+// 1, 3; h02 / h13: the high nibbles, kept in place as 16 q); byte_fma then
+// spends one v_fma_mix_f32 per weight, into two chains per sub-block (even
+// and odd bytes).
 struct WordQ {
     half2v l02, l13, h02, h13;
 };

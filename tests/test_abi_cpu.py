@@ -178,3 +178,23 @@ def test_product_path_has_no_oracle_or_fallback():
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text, f
                 assert "q4k_oracle" not in text, f
+
+
+@pytest.mark.parametrize("M,K,code", [(-1, 1024, -2), (4, 0, -2), (4, 256, -2), (4, 512, -2),
+                                      (4, 1280, -2), (4, 1000, -2), (1 << 31, 1024, -6)])
+def test_gemv_q6_k_shape_errors(lib, M, K, code):
+    """K must be a positive multiple of 1024 (rows of a multiple of four
+    210-byte blocks); checked before the pointers and the device."""
+    assert lib.q4k_gemv_q6_k(None, None, None, M, K, None) == code
+    assert lib.q4k_last_error()
+
+
+def test_gemv_q6_k_pointer_errors_and_zero_rows(lib):
+    assert lib.q4k_gemv_q6_k(None, P, P, 4, 1024, None) == -1
+    assert lib.q4k_gemv_q6_k(P, None, P, 4, 1024, None) == -1
+    assert lib.q4k_gemv_q6_k(P, P, None, 4, 1024, None) == -1
+    assert lib.q4k_gemv_q6_k(P + 8, P, P, 4, 1024, None) == -3
+    assert lib.q4k_gemv_q6_k(P, P + 4, P, 4, 1024, None) == -3
+    assert lib.q4k_gemv_q6_k(P, P, P + 12, 4, 1024, None) == -3
+    assert lib.q4k_gemv_q6_k(None, None, None, 0, 2048, None) == 0
+    assert lib.q4k_last_error() == b""
