@@ -940,14 +940,14 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
     return ((M + rows - 1) / rows) * ((K / 256 + WK - 1) / WK);
 }
 
-// Workgroup count: every resident slot, at most two workgroups per CU (three
-// from 16 units per CU up), each taking a contiguous range of units; tiles
-// cut by a range boundary are finished in-kernel by their last contributor.
-// On the 50 MB MLP matrices (5.3 units per CU) two workgroups per CU measured
-// 16.7-17.2 us against 17.8-19.1 us at three and 18.3-20.0 us at four, and
-// every count from 384 to 640 workgroups was slower than 512; one tile per
-// workgroup (no cut tiles) was slower still.  On the 715 MB lm_head
-// (76 units per CU) three per CU took 145 us against 166 us at two.
+// Workgroup count: every resident slot, at most two workgroups per CU, each
+// taking a contiguous range of units; tiles cut by a range boundary are
+// finished in-kernel by their last contributor.  On the 50 MB MLP matrices
+// two workgroups per CU measured 16.6-17.2 us against 17.8-19.1 us at three
+// and 18.3-20.0 us at four, and every count from 384 to 640 workgroups was
+// slower than 512; on the 715 MB lm_head two per CU took 134.6 us against
+// 138.0 at three and 152.7 at four (interleaved runs).  One tile per
+// workgroup (no cut tiles) was slower still.
 template <int NV, int NMAT, int EPI>
 int groups_for(int64_t M, int64_t K, int *G) {
     int res = 0, cus = 0;
@@ -956,8 +956,7 @@ int groups_for(int64_t M, int64_t K, int *G) {
     if (o <= 0) {
         int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res, &cus);
         if (rc) return rc;
-        const int per_cu = units_of(M, K, NMAT) >= 16 * (int64_t)cus ? 3 : 2;
-        g = std::min(res, per_cu * cus);
+        g = std::min(res, 2 * cus);
     }
     *G = (int)std::max<int64_t>(1, std::min<int64_t>(g, units_of(M, K, NMAT)));
     return Q4K_OK;
@@ -1041,8 +1040,9 @@ GemvLaunch choose_gemv_q8_launch(int64_t M, int64_t K) {
     const int64_t units = ((M + 63) / 64) * ((K / 32 + Q8_UNIT_BLOCKS - 1) / Q8_UNIT_BLOCKS);
     int G = g_override_groups.load(), res = 0, cus = 0;
     if (G <= 0) {
-        // at most three workgroups per CU: on the 1.35 GB lm_head 243.7 us
-        // against 249.7 us at four and 268.8 us at every resident slot
+        // at most three workgroups per CU: on the 1.35 GB lm_head 241.6 us
+        // against 256.2 at two, 249.3 at four and 278.5 at five (every
+        // resident slot), interleaved runs
         if (resident_groups((const void *)gemv_q8_kernel, &res, &cus) == Q4K_OK)
             G = std::min(res, 3 * cus);
         else {
