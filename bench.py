@@ -50,7 +50,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 QK, BB = 256, 144
 METRIC = "Q4_K GEMV HBM GB/s (% peak); decode-stack µs/token; prefill GEMM TFLOP/s"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_mlp_17408x5120_traffic.json")
-SHORT_P = (16, 22, 27, 64)  # short-prompt prefill lengths timed next to the prefill configs
+SHORT_P = (16, 22, 27, 64)
+SETTLE_MS = 50  # untimed steady-state run before every timed region  # short-prompt prefill lengths timed next to the prefill configs
 GEMV_SOURCES = ["bit_block_quantized_gguf_amd/csrc/q4k_gemv.hip",
                 "bit_block_quantized_gguf_amd/csrc/q4k_device.hpp"]
 
@@ -108,7 +109,24 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    def settle(fn, ms=SETTLE_MS):
+        """Untimed: call fn(i) for i = 0, 1, ... until `ms` of wall time have
+        passed (synchronising every few calls).  The weights of each section
+        are generated on the host first, during which the GPU idles; the
+        first milliseconds of work after that run slower than the steady
+        state (clocks, first touches of fresh allocations)."""
+        t_end = time.perf_counter() + ms / 1e3
+        i = 0
+        while True:
+            for _ in range(4):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                break
+
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "settle_ms_before_each_timed_region": SETTLE_MS,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic (seeded SplitMix64 Q4_K blocks, N(0,1) f32 activations)"}
     props = torch.cuda.get_device_properties(0)
@@ -144,7 +162,7 @@ def main():
 
         for i in range(args.warmup):
             step(i)
-        torch.cuda.synchronize()
+        settle(step)
         # wall-clock step timing (no per-kernel events inside)
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -209,7 +227,8 @@ def main():
         for i in range(args.warmup):
             c = i % args.copies
             q4k.mlp(copies["gate"][c], copies["up"][c], copies["down"][c], xd, gain, 1e-6, xd, y_mlp)
-        torch.cuda.synchronize()
+        settle(lambda i: q4k.mlp(copies["gate"][i % args.copies], copies["up"][i % args.copies],
+                                 copies["down"][i % args.copies], xd, gain, 1e-6, xd, y_mlp))
         mlp_us = []
         for rep in range(3):
             e0, e1 = ev(), ev()
@@ -243,7 +262,7 @@ def main():
             Y = torch.empty((N, M), device=dev)
             for i in range(3):
                 q4k.gemv_batch(ws[i % ncop], X, Y)
-            torch.cuda.synchronize()
+            settle(lambda i: q4k.gemv_batch(ws[i % ncop], X, Y))
             # bursts of back-to-back launches on the cold copies, one event
             # pair per burst (as for the MLP GEMVs above)
             nrep = max(10, args.steps)
@@ -277,7 +296,7 @@ def main():
             y = torch.empty(M, device=dev)
             for _ in range(5):
                 q4k.gemv(wd, xs, y)
-            torch.cuda.synchronize()
+            settle(lambda i: q4k.gemv(wd, xs, y))
             ts = []
             for _ in range(50):
                 e0, e1 = ev(), ev()
@@ -330,7 +349,7 @@ def main():
         yq = torch.empty(M, device=dev)
         for _ in range(3):
             q4k.gemv_q8_0(wq, xq, yq)
-        torch.cuda.synchronize()
+        settle(lambda i: q4k.gemv_q8_0(wq, xq, yq))
         reps = []
         for rep in range(3):
             e0, e1 = ev(), ev()
@@ -360,7 +379,7 @@ def main():
             y6 = torch.empty(M, device=dev)
             for i in range(3):
                 q4k.gemv_q6_k(wc[i % 4], x6, y6)
-            torch.cuda.synchronize()
+            settle(lambda i: q4k.gemv_q6_k(wc[i % 4], x6, y6))
             reps = []
             for rep in range(3):
                 e0, e1 = ev(), ev()
@@ -390,7 +409,7 @@ def main():
                 Y = torch.empty((P, M), device=dev)
                 for _ in range(3):
                     q4k.gemm(wd, X, Y)
-                torch.cuda.synchronize()
+                settle(lambda i: q4k.gemm(wd, X, Y))
                 pairs = []
                 for _ in range(max(10, args.steps // 2)):
                     e0, e1 = ev(), ev()
@@ -438,7 +457,7 @@ def main():
         logits = torch.empty(wl.VOCAB, device=dev)
         for _ in range(3):
             stk(h0, logits)
-        torch.cuda.synchronize()
+        settle(lambda i: stk(h0, logits))
         pairs = []
         t0 = time.perf_counter()
         for _ in range(args.stack_tokens):
