@@ -364,9 +364,33 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
     }
 }
 
-// Unit bookkeeping shared by the main and the reduce kernel.  The divisions
-// run in 32 bits when the products fit (64-bit division is a long scalar
-// sequence on this ISA).
+// 64-bit forms of the range arithmetic below.  They are only reached when
+// (U + 1) * G does not fit in 32 bits, which at two workgroups per CU takes
+// more weight bytes than the device holds, so they use a one-bit-per-step
+// restoring division: a few scalar instructions of code instead of the long
+// inlined sequence a 64-bit '/' expands to (which grew every kernel to
+// 40 KB, most of it copies of that sequence).
+__device__ __forceinline__ uint64_t udiv64_compact(uint64_t n, uint64_t d) {
+    uint64_t q = 0, r = 0;
+#pragma unroll 1
+    for (int i = 63; i >= 0; --i) {
+        r = (r << 1) | ((n >> i) & 1u);
+        if (r >= d) {
+            r -= d;
+            q |= (uint64_t)1 << i;
+        }
+    }
+    return q;
+}
+__device__ __forceinline__ int64_t range_begin64(int g, int64_t U, int G) {
+    return (int64_t)udiv64_compact((uint64_t)g * (uint64_t)U, (uint64_t)G);
+}
+__device__ __forceinline__ int range_owner64(int64_t u, int64_t U, int G) {
+    return (int)udiv64_compact((uint64_t)(u + 1) * (uint64_t)G + (uint64_t)U - 1, (uint64_t)U) - 1;
+}
+
+// Unit bookkeeping shared by the GEMV kernels.  The divisions run in 32 bits
+// when the products fit.
 struct Units {
     int upt;      // units per row tile = ceil(nb / 4)
     int64_t U;    // total units = tiles * upt
@@ -374,13 +398,13 @@ struct Units {
     bool small;   // (U + 1) * G < 2^32
     __device__ __forceinline__ int64_t begin(int g) const {
         if (small) return (int64_t)((uint32_t)g * (uint32_t)U / (uint32_t)G);
-        return (int64_t)g * U / G;
+        return range_begin64(g, U, G);
     }
     // workgroup whose range contains unit u
     __device__ __forceinline__ int owner(int64_t u) const {
         if (small)
             return (int)(((uint32_t)(u + 1) * (uint32_t)G + (uint32_t)U - 1) / (uint32_t)U) - 1;
-        return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
+        return range_owner64(u, U, G);
     }
 };
 
@@ -412,6 +436,10 @@ __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Uni
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != (unsigned)(gl - gf)) return;  // not the last contributor
     if (lane == 0) __hip_atomic_store(&p.cnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Contributor g2 stored its partial in slot 0 when tile t is its first
+    // tile.  Every contributor after gf starts inside tile t; gf does when its
+    // range starts exactly at the tile's first unit.
+    const int slot_gf = un.begin(gf) < (int64_t)t * un.upt ? 1 : 0;
     float sum[NV];
 #pragma unroll
     for (int n = 0; n < NV; ++n) sum[n] = 0.f;
@@ -421,9 +449,7 @@ __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Uni
         for (int c = 0; c < CH; ++c) {
             const int g2 = c0 + c;
             if (g2 <= gl) {
-                const int64_t bg = un.begin(g2);
-                const int ft = un.small ? (int)((uint32_t)bg / (uint32_t)un.upt) : (int)(bg / un.upt);
-                const int sl = t == ft ? 0 : 1;
+                const int sl = g2 == gf ? slot_gf : 0;
 #pragma unroll
                 for (int n = 0; n < NV; ++n)
                     part[c][n] = __hip_atomic_load(&p.ws[(((int64_t)g2 * 2 + sl) * NV + n) * 64 + lane],
