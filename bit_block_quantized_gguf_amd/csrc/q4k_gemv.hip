@@ -764,7 +764,10 @@ __global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, co
 // ql[64h + 32(c mod 2) + l] and bits 2c, 2c+1 of qh[32h + l]; with q in 0..63,
 // w = d * sc[k/16] * (q - 32).  Per block the kernel forms
 //    d * (sum_g sc_g * T_g  -  32 * sum_g sc_g * X_g)
-// with T_g = sum(q x) and X_g = sum(x) over the 16 weights of group g.
+// with T_g = sum(q x) and X_g = sum(x) over the 16 weights of group g.  As
+// in the Q4_K kernel, a quant (at most 63) sitting in a 16-bit half is the
+// binary16 subnormal q * 2^-24, so each weight costs one v_fma_mix_f32; the
+// T_g carry that exact factor, removed once per block.
 //
 // Same skeleton as the Q4_K kernel: a unit is 64 rows x 4 blocks (one
 // 840-byte run per row) and wave w takes block w of every row, one row per
@@ -874,13 +877,15 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
                             const uint32_t lo = (c < 2 ? QL : QL >> 4) & 0x0F0F0F0Fu;
                             const uint32_t hi = (c < 1 ? QH << 4 : c < 2 ? QH << 2 : c < 3 ? QH : QH >> 2) &
                                                 0x30303030u;
-                            uint32_t q4 = lo | hi;  // four six-bit quants, one per byte
-                            asm("" : "+v"(q4));     // keeps one byte conversion per weight
+                            const uint32_t q4 = lo | hi;  // four six-bit quants, one per byte
+                            // bytes 0, 2 and 1, 3 into binary16 halves: q * 2^-24 exactly
+                            const half2v q02 = __builtin_bit_cast(half2v, and_mask(q4, 0x00FF00FFu));
+                            const half2v q13 = __builtin_bit_cast(half2v, and_mask(q4 >> 8, 0x00FF00FFu));
                             const int kx = 128 * h + 32 * c + 4 * i;
-                            t0 = fmaf(ubyte(q4, 0), xb[kx + 0], t0);
-                            t1 = fmaf(ubyte(q4, 1), xb[kx + 1], t1);
-                            t0 = fmaf(ubyte(q4, 2), xb[kx + 2], t0);
-                            t1 = fmaf(ubyte(q4, 3), xb[kx + 3], t1);
+                            t0 = fmaf((float)q02.x, xb[kx + 0], t0);
+                            t1 = fmaf((float)q13.x, xb[kx + 1], t1);
+                            t0 = fmaf((float)q02.y, xb[kx + 2], t0);
+                            t1 = fmaf((float)q13.y, xb[kx + 3], t1);
                         }
                         const int grp = 8 * h + 2 * c + half;
                         const float scg =
@@ -891,7 +896,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
                                   Bs);
                     }
             const float d = __half2float(__ushort_as_half((unsigned short)(B[52] & 0xFFFFu)));
-            acc = fmaf(d, fmaf(-32.0f, Bs, A), acc);
+            // A carries the exact factor 2^-24 of the binary16 quants
+            acc = fmaf(d, fmaf(-32.0f, Bs, A * 16777216.0f), acc);
         }
         const bool seg_end = !more || last_of_tile;
         if (seg_end) {
