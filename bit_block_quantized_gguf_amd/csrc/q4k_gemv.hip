@@ -492,16 +492,33 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
     uint4 reg[CH_THREAD];
 #pragma unroll
     for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    // An interior unit (all rows of its tile below M, all WK blocks inside the
+    // row) loads every chunk at an offset that does not depend on the unit:
+    // computed once here, so its loads cost no vector instructions.
+    uint32_t ofull[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) {
+        const int r = NMAT == 2 ? (crow[i] & 31) : crow[i];
+        ofull[i] = (uint32_t)r * (uint32_t)p.row_bytes + (uint32_t)coff[i];
+    }
     // Loads of unit u: a uniform tile base (SGPRs) plus a 32-bit lane offset;
     // rows past M are clamped to the last row (their results are not stored).
     // Unit u = t * upt + k is passed as (t, k): no 64-bit division in the loop.
     auto fetch = [&](int t, int k) {
         const int j0 = k * WK;
-        const int valid = min(WK, p.nb - j0) * kBlockBytes;  // bytes per row segment
-        const int rmax = min(ROWS - 1, p.M - 1 - t * ROWS);
         const int64_t base = (int64_t)t * ROWS * p.row_bytes + (int64_t)j0 * kBlockBytes;
         const uint8_t *b0 = p.w0 + base;
         const uint8_t *b1 = NMAT == 2 ? p.w1 + base : b0;
+        if ((t + 1) * ROWS <= p.M && j0 + WK <= p.nb) {  // wave-uniform
+#pragma unroll
+            for (int i = 0; i < CH_THREAD; ++i) {
+                const uint8_t *src = (NMAT == 2 && crow[i] >= 32) ? b1 : b0;
+                reg[i] = ldg16(src + ofull[i]);
+            }
+            return;
+        }
+        const int valid = min(WK, p.nb - j0) * kBlockBytes;  // bytes per row segment
+        const int rmax = min(ROWS - 1, p.M - 1 - t * ROWS);
 #pragma unroll
         for (int i = 0; i < CH_THREAD; ++i) {
             // chunks past the row's last block re-read the unit's first chunk
