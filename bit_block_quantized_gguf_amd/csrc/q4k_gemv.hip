@@ -494,12 +494,18 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
     for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
     // An interior unit (all rows of its tile below M, all WK blocks inside the
     // row) loads every chunk at an offset that does not depend on the unit:
-    // computed once here, so its loads cost no vector instructions.
-    uint32_t ofull[CH_THREAD];
+    // computed once here, so its loads cost no vector instructions.  Only in
+    // the plain-output kernels up to eight vectors: at sixteen the nine extra
+    // registers spill to scratch, and the decode stack's fused-epilogue
+    // variants measured 0.8% slower with them (same-process A/B).
+    constexpr bool kFast = NV <= 8 && EPI == EPI_PLAIN;
+    uint32_t ofull[kFast ? CH_THREAD : 1];
+    if constexpr (kFast) {
 #pragma unroll
-    for (int i = 0; i < CH_THREAD; ++i) {
-        const int r = NMAT == 2 ? (crow[i] & 31) : crow[i];
-        ofull[i] = (uint32_t)r * (uint32_t)p.row_bytes + (uint32_t)coff[i];
+        for (int i = 0; i < CH_THREAD; ++i) {
+            const int r = NMAT == 2 ? (crow[i] & 31) : crow[i];
+            ofull[i] = (uint32_t)r * (uint32_t)p.row_bytes + (uint32_t)coff[i];
+        }
     }
     // Loads of unit u: a uniform tile base (SGPRs) plus a 32-bit lane offset;
     // rows past M are clamped to the last row (their results are not stored).
@@ -509,13 +515,15 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         const int64_t base = (int64_t)t * ROWS * p.row_bytes + (int64_t)j0 * kBlockBytes;
         const uint8_t *b0 = p.w0 + base;
         const uint8_t *b1 = NMAT == 2 ? p.w1 + base : b0;
-        if ((t + 1) * ROWS <= p.M && j0 + WK <= p.nb) {  // wave-uniform
+        if constexpr (kFast) {
+            if ((t + 1) * ROWS <= p.M && j0 + WK <= p.nb) {  // wave-uniform
 #pragma unroll
-            for (int i = 0; i < CH_THREAD; ++i) {
-                const uint8_t *src = (NMAT == 2 && crow[i] >= 32) ? b1 : b0;
-                reg[i] = ldg16(src + ofull[i]);
+                for (int i = 0; i < CH_THREAD; ++i) {
+                    const uint8_t *src = (NMAT == 2 && crow[i] >= 32) ? b1 : b0;
+                    reg[i] = ldg16(src + ofull[i]);
+                }
+                return;
             }
-            return;
         }
         const int valid = min(WK, p.nb - j0) * kBlockBytes;  // bytes per row segment
         const int rmax = min(ROWS - 1, p.M - 1 - t * ROWS);
