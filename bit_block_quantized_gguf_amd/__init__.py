@@ -28,14 +28,13 @@ BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS = range(7)
 
 # Every symbol include/q4k.h declares (checked by the CPU test suite).
 EXPORTS = (
-    "q4k_last_error", "q4k_version", "q4k_dequant", "q4k_gemv", "q4k_gemv_q8_0", "q4k_gemv_q6_k",
-    "q4k_mlp",
-    "q4k_gemv_batch",
-    "q4k_gemm",
+    "q4k_last_error", "q4k_version", "q4k_workspace_size", "q4k_dequant", "q4k_gemv",
+    "q4k_gemv_q8_0", "q4k_gemv_q6_k", "q4k_mlp", "q4k_gemv_batch", "q4k_gemm",
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
-    "q4k_tune_gemv", "q4k_tune_gemm", "q4k_release_workspaces",
+    "q4k_tune_gemv", "q4k_tune_gemm",
 )
+OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP = range(6)
 
 _lib = None
 
@@ -81,13 +80,15 @@ def load(path: str | None = None):
     L.q4k_last_error.restype = ctypes.c_char_p
     L.q4k_last_error.argtypes = []
     L.q4k_version.restype = ctypes.c_int
+    sz = ctypes.c_size_t
+    L.q4k_workspace_size.argtypes = [i32, i64, i64, i64, ctypes.POINTER(sz)]
     L.q4k_dequant.argtypes = [p, p, i64, i64, p]
-    L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
-    L.q4k_gemv_batch.argtypes = [p, p, p, i64, i64, i64, p]
-    L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p]
-    L.q4k_mlp.argtypes = [p, p, p, i64, i64, p, p, ctypes.c_float, p, p, p, p]
-    L.q4k_gemv_q8_0.argtypes = [p, p, p, i64, i64, p]
-    L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p]
+    L.q4k_gemv.argtypes = [p, p, p, i64, i64, p, sz, p]
+    L.q4k_gemv_batch.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
+    L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
+    L.q4k_mlp.argtypes = [p, p, p, i64, i64, p, p, ctypes.c_float, p, p, p, p, sz, p]
+    L.q4k_gemv_q8_0.argtypes = [p, p, p, i64, i64, p, sz, p]
+    L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p, sz, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
     L.q4k_decode_stack.argtypes = [p, p, p, p]
     L.q4k_decode_stack_buffer.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(i64)]
@@ -98,9 +99,8 @@ def load(path: str | None = None):
     L.q4k_gemm_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.q4k_tune_gemv.argtypes = [i32, i32]
     L.q4k_tune_gemm.argtypes = [i32, i32]
-    L.q4k_release_workspaces.argtypes = []
-    L.q4k_release_workspaces.restype = None
-    for name in ("q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
+    for name in ("q4k_workspace_size", "q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm",
+                 "q4k_mlp", "q4k_gemv_q8_0", "q4k_gemv_q6_k",
                  "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
                  "q4k_decode_stack_nodes", "q4k_gemv_config", "q4k_gemm_config",
                  "q4k_tune_gemv", "q4k_tune_gemm"):
@@ -124,28 +124,45 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _dev_tensor(t, dtype, name):
+def _tensor(t, dtype, name, numel=None):
+    """Check a tensor argument's type, dtype, element count and layout (an
+    undersized output would make a kernel write past it).  Device placement is
+    checked separately, after every argument's size (_on_gpu)."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements, the call needs %d" % (name, t.numel(), numel))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t
 
 
-def _weights(w, M, K):
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+
+
+def _dev_tensor(t, dtype, name):
+    _tensor(t, dtype, name)
+    _on_gpu(**{name: t})
+    return t
+
+
+def _weights(w, M, K, block_bytes=BLOCK_BYTES, block_weights=QK, fmt="Q4_K"):
     torch = _torch()
-    _dev_tensor(w, torch.uint8, "w")
     if K % QK:
         raise ValueError("K must be a multiple of 256")
-    if w.numel() != M * (K // QK) * BLOCK_BYTES:
-        raise ValueError("w holds %d bytes, a %dx%d Q4_K matrix needs %d"
-                         % (w.numel(), M, K, M * (K // QK) * BLOCK_BYTES))
-    return w
+    need = M * (K // block_weights) * block_bytes
+    if not isinstance(w, torch.Tensor):
+        raise TypeError("w must be a torch.Tensor")
+    if w.numel() != need:
+        raise ValueError("w holds %d bytes, a %dx%d %s matrix needs %d"
+                         % (w.numel(), M, K, fmt, need))
+    return _tensor(w, torch.uint8, "w")
 
 
 def weight_shape(w) -> tuple[int, int]:
@@ -160,6 +177,64 @@ def version() -> int:
     return int(load().q4k_version())
 
 
+# ---------------------------------------------------------------- workspaces
+
+_ws_need: dict = {}
+
+
+def workspace_size(op: int, M: int, K: int, N: int = 0) -> int:
+    """Bytes of workspace that call `op` (OP_GEMV, ...) needs for the shape
+    (memoised per shape; the tuning knobs clear the memo)."""
+    key = (op, M, K, N)
+    n = _ws_need.get(key)
+    if n is None:
+        c = ctypes.c_size_t()
+        check(load().q4k_workspace_size(op, M, K, N, ctypes.byref(c)))
+        n = _ws_need[key] = c.value
+    return n
+
+
+class Workspace:
+    """Caller-owned device scratch for the calls that need one: zero-filled
+    once here; every call leaves it valid for the next (see include/q4k.h).
+    Calls that may run at the same time need distinct workspaces."""
+
+    def __init__(self, nbytes: int, device=None):
+        torch = _torch()
+        n = max(256, (int(nbytes) + 255) // 256 * 256)
+        self.tensor = torch.zeros(n, dtype=torch.uint8,
+                                  device=device if device is not None else "cuda")
+        if self.tensor.data_ptr() % 256:
+            raise RuntimeError("workspace allocation is not 256-byte aligned")
+        self.nbytes = n
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+
+# Default workspaces, one growing chain per (device, stream).  A buffer is
+# never released once made: a HIP graph that captured a call keeps using the
+# buffer that call was given.
+_ws_cache: dict = {}
+
+
+def _ws(op, M, K, N, ws):
+    need = workspace_size(op, M, K, N)
+    if ws is not None:
+        if not isinstance(ws, Workspace):
+            raise TypeError("ws must be a Workspace")
+        return ws
+    torch = _torch()
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    chain = _ws_cache.setdefault(key, [])
+    if not chain or chain[-1].nbytes < need:
+        chain.append(Workspace(need))
+    return chain[-1]
+
+
+# ---------------------------------------------------------------- calls
+
 def dequant(w, M: int | None = None, K: int | None = None, out=None):
     torch = _torch()
     if M is None:
@@ -167,30 +242,32 @@ def dequant(w, M: int | None = None, K: int | None = None, out=None):
     _weights(w, M, K)
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=w.device)
-    _dev_tensor(out, torch.float32, "out")
+    _tensor(out, torch.float32, "out", M * K)
+    _on_gpu(w=w, out=out)
     check(load().q4k_dequant(w.data_ptr(), out.data_ptr(), M, K, _stream()))
     return out
 
 
-def gemv(w, x, y=None, M: int | None = None, K: int | None = None):
+def gemv(w, x, y=None, M: int | None = None, K: int | None = None, ws=None):
     torch = _torch()
     if M is None:
         M, K = weight_shape(w)
     _weights(w, M, K)
-    _dev_tensor(x, torch.float32, "x")
-    if x.numel() != K:
-        raise ValueError("x must have K=%d elements" % K)
+    _tensor(x, torch.float32, "x", K)
     if y is None:
         y = torch.empty(M, dtype=torch.float32, device=w.device)
-    _dev_tensor(y, torch.float32, "y")
-    check(load().q4k_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    _tensor(y, torch.float32, "y", M)
+    _on_gpu(w=w, x=x, y=y)
+    ws = _ws(OP_GEMV, M, K, 1, ws)
+    check(load().q4k_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, ws.ptr, ws.nbytes,
+                          _stream()))
     return y
 
 
 Q8_BLOCK_BYTES = 34
 
 
-def gemv_q8_0(w, x, y=None, M: int | None = None, K: int | None = None):
+def gemv_q8_0(w, x, y=None, M: int | None = None, K: int | None = None, ws=None):
     """y = W x for a Q8_0 weight [M, K/32*34] uint8 (K a multiple of 256)."""
     torch = _torch()
     if M is None:
@@ -198,24 +275,22 @@ def gemv_q8_0(w, x, y=None, M: int | None = None, K: int | None = None):
         if rb % Q8_BLOCK_BYTES:
             raise ValueError("row length is not a whole number of 34-byte blocks")
         K = rb // Q8_BLOCK_BYTES * 32
-    _dev_tensor(w, torch.uint8, "w")
-    if w.numel() != M * (K // 32) * Q8_BLOCK_BYTES:
-        raise ValueError("w holds %d bytes, a %dx%d Q8_0 matrix needs %d"
-                         % (w.numel(), M, K, M * (K // 32) * Q8_BLOCK_BYTES))
-    _dev_tensor(x, torch.float32, "x")
-    if x.numel() != K:
-        raise ValueError("x must have K=%d elements" % K)
+    _weights(w, M, K, Q8_BLOCK_BYTES, 32, "Q8_0")
+    _tensor(x, torch.float32, "x", K)
     if y is None:
         y = torch.empty(M, dtype=torch.float32, device=w.device)
-    _dev_tensor(y, torch.float32, "y")
-    check(load().q4k_gemv_q8_0(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    _tensor(y, torch.float32, "y", M)
+    _on_gpu(w=w, x=x, y=y)
+    ws = _ws(OP_GEMV_Q8_0, M, K, 1, ws)
+    check(load().q4k_gemv_q8_0(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, ws.ptr,
+                               ws.nbytes, _stream()))
     return y
 
 
 Q6_BLOCK_BYTES = 210
 
 
-def gemv_q6_k(w, x, y=None, M: int | None = None, K: int | None = None):
+def gemv_q6_k(w, x, y=None, M: int | None = None, K: int | None = None, ws=None):
     """y = W x for a Q6_K weight [M, K/256*210] uint8 (K a multiple of 1024)."""
     torch = _torch()
     if M is None:
@@ -223,22 +298,20 @@ def gemv_q6_k(w, x, y=None, M: int | None = None, K: int | None = None):
         if rb % Q6_BLOCK_BYTES:
             raise ValueError("row length is not a whole number of 210-byte blocks")
         K = rb // Q6_BLOCK_BYTES * 256
-    _dev_tensor(w, torch.uint8, "w")
-    if w.numel() != M * (K // 256) * Q6_BLOCK_BYTES:
-        raise ValueError("w holds %d bytes, a %dx%d Q6_K matrix needs %d"
-                         % (w.numel(), M, K, M * (K // 256) * Q6_BLOCK_BYTES))
-    _dev_tensor(x, torch.float32, "x")
-    if x.numel() != K:
-        raise ValueError("x must have K=%d elements" % K)
+    _weights(w, M, K, Q6_BLOCK_BYTES, 256, "Q6_K")
+    _tensor(x, torch.float32, "x", K)
     if y is None:
         y = torch.empty(M, dtype=torch.float32, device=w.device)
-    _dev_tensor(y, torch.float32, "y")
-    check(load().q4k_gemv_q6_k(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
+    _tensor(y, torch.float32, "y", M)
+    _on_gpu(w=w, x=x, y=y)
+    ws = _ws(OP_GEMV_Q6_K, M, K, 1, ws)
+    check(load().q4k_gemv_q6_k(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, ws.ptr,
+                               ws.nbytes, _stream()))
     return y
 
 
 def mlp(w_gate, w_up, w_down, x, norm_w=None, eps: float = 1e-6, resid=None, y=None, act=None,
-        hidden: int | None = None, inter: int | None = None):
+        hidden: int | None = None, inter: int | None = None, ws=None):
     """y = resid + W_down (silu(W_gate n) * (W_up n)), n = x / rms(x) * (1 + norm_w).
 
     w_gate, w_up: [inter, hidden/256*144] uint8; w_down: [hidden, inter/256*144].
@@ -250,53 +323,57 @@ def mlp(w_gate, w_up, w_down, x, norm_w=None, eps: float = 1e-6, resid=None, y=N
     _weights(w_gate, inter, hidden)
     _weights(w_up, inter, hidden)
     _weights(w_down, hidden, inter)
-    _dev_tensor(x, torch.float32, "x")
-    if x.numel() != hidden:
-        raise ValueError("x must have hidden=%d elements" % hidden)
+    _tensor(x, torch.float32, "x", hidden)
     for name, v, n in (("norm_w", norm_w, hidden), ("resid", resid, hidden), ("act", act, inter)):
         if v is not None:
-            _dev_tensor(v, torch.float32, name)
-            if v.numel() != n:
-                raise ValueError("%s must have %d elements" % (name, n))
+            _tensor(v, torch.float32, name, n)
     if y is None:
         y = torch.empty(hidden, dtype=torch.float32, device=x.device)
-    _dev_tensor(y, torch.float32, "y")
+    _tensor(y, torch.float32, "y", hidden)
+    _on_gpu(w_gate=w_gate, w_up=w_up, w_down=w_down, x=x, norm_w=norm_w, resid=resid, act=act, y=y)
+    ws = _ws(OP_MLP, inter, hidden, 0, ws)
     ptr = lambda t: t.data_ptr() if t is not None else None
     check(load().q4k_mlp(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), hidden, inter,
                          x.data_ptr(), ptr(norm_w), float(eps), ptr(resid), y.data_ptr(),
-                         ptr(act), _stream()))
+                         ptr(act), ws.ptr, ws.nbytes, _stream()))
     return y
 
 
-def gemv_batch(w, X, Y=None, M: int | None = None, K: int | None = None):
+def gemv_batch(w, X, Y=None, M: int | None = None, K: int | None = None, ws=None):
     torch = _torch()
     if M is None:
         M, K = weight_shape(w)
     _weights(w, M, K)
-    _dev_tensor(X, torch.float32, "X")
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [N, K=%d]" % K)
     N = X.shape[0]
-    if X.numel() != N * K:
-        raise ValueError("X must be [N, K]")
+    _tensor(X, torch.float32, "X", N * K)
     if Y is None:
         Y = torch.empty((N, M), dtype=torch.float32, device=w.device)
-    _dev_tensor(Y, torch.float32, "Y")
-    check(load().q4k_gemv_batch(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, N, _stream()))
+    _tensor(Y, torch.float32, "Y", N * M)
+    _on_gpu(w=w, X=X, Y=Y)
+    ws = _ws(OP_GEMV_BATCH, M, K, N, ws)
+    check(load().q4k_gemv_batch(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, N, ws.ptr,
+                                ws.nbytes, _stream()))
     return Y
 
 
-def gemm(w, X, Y=None, M: int | None = None, K: int | None = None):
+def gemm(w, X, Y=None, M: int | None = None, K: int | None = None, ws=None):
     torch = _torch()
     if M is None:
         M, K = weight_shape(w)
     _weights(w, M, K)
-    _dev_tensor(X, torch.float32, "X")
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [P, K=%d]" % K)
     P = X.shape[0]
-    if X.numel() != P * K:
-        raise ValueError("X must be [P, K]")
+    _tensor(X, torch.float32, "X", P * K)
     if Y is None:
         Y = torch.empty((P, M), dtype=torch.float32, device=w.device)
-    _dev_tensor(Y, torch.float32, "Y")
-    check(load().q4k_gemm(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, P, _stream()))
+    _tensor(Y, torch.float32, "Y", P * M)
+    _on_gpu(w=w, X=X, Y=Y)
+    ws = _ws(OP_GEMM, M, K, P, ws)
+    check(load().q4k_gemm(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, P, ws.ptr, ws.nbytes,
+                          _stream()))
     return Y
 
 
@@ -316,15 +393,13 @@ def gemm_config(M: int, K: int, P: int) -> tuple[int, int]:
 def tune_gemv(waves_per_group: int = 0, workgroups: int = 0) -> None:
     """Force the GEMV workgroup count (0: automatic); waves_per_group must be 0 or 4."""
     check(load().q4k_tune_gemv(waves_per_group, workgroups))
+    _ws_need.clear()
 
 
 def tune_gemm(tile_tokens: int = 0, workgroups: int = 0) -> None:
     """Force the GEMM tile width (0, 32, 64, 128 or 256 tokens) and workgroup count (0: automatic)."""
     check(load().q4k_tune_gemm(tile_tokens, workgroups))
-
-
-def release_workspaces() -> None:
-    load().q4k_release_workspaces()
+    _ws_need.clear()
 
 
 class DecodeStack:
@@ -346,10 +421,12 @@ class DecodeStack:
                 t = L[name]
                 M, K = weight_shape(t)
                 _weights(t, M, K)
+                _on_gpu(**{name: t})
                 self._keep.append(t)
                 setattr(ld, name, MatDesc(t.data_ptr(), M, K))
         M, K = weight_shape(lm_head)
         _weights(lm_head, M, K)
+        _on_gpu(lm_head=lm_head)
         self._keep.append(lm_head)
         self.hidden = hidden
         self.vocab = M
@@ -364,19 +441,19 @@ class DecodeStack:
 
     def __call__(self, h_in, logits=None):
         torch = _torch()
-        _dev_tensor(h_in, torch.float32, "h_in")
-        if h_in.numel() != self.hidden:
-            raise ValueError("h_in must have %d elements" % self.hidden)
+        _tensor(h_in, torch.float32, "h_in", self.hidden)
         if logits is None:
             logits = torch.empty(self.vocab, dtype=torch.float32, device=h_in.device)
-        _dev_tensor(logits, torch.float32, "logits")
+        _tensor(logits, torch.float32, "logits", self.vocab)
+        _on_gpu(h_in=h_in, logits=logits)
         check(load().q4k_decode_stack(self._h, h_in.data_ptr(), logits.data_ptr(), _stream()))
         return logits
 
     def run_no_copy(self, h_in):
         """Launch one token and leave the logits in the arena (see ``buffer``)."""
         torch = _torch()
-        _dev_tensor(h_in, torch.float32, "h_in")
+        _tensor(h_in, torch.float32, "h_in", self.hidden)
+        _on_gpu(h_in=h_in)
         check(load().q4k_decode_stack(self._h, h_in.data_ptr(), None, _stream()))
 
     def buffer_ptr(self, layer: int, which: int) -> tuple[int, int]:

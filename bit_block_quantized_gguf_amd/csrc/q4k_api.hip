@@ -1,5 +1,7 @@
 // q4k_api.hip — C ABI entry points of libq4k: argument validation, error
-// reporting, the split-K workspace cache, and dispatch to the kernels.
+// reporting, workspace layout, and dispatch to the kernels.  Hot calls never
+// allocate or synchronise: the scratch memory they need comes from the
+// caller's workspace, whose size q4k_workspace_size() reports.
 #include "q4k_internal.hpp"
 
 #include <stdarg.h>
@@ -20,11 +22,10 @@ namespace {
 
 thread_local std::string t_error;
 
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
 std::mutex g_dev_mutex;
 std::map<int, bool> g_dev_ok;
+
+size_t round256(size_t bytes) { return (bytes + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -44,64 +45,41 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(Q4K_EHIP, "%s failed: %s", what, hipGetErrorString(e));
 }
 
+size_t region_bytes(size_t partial_floats) {
+    return kCounterBytes + round256(partial_floats * sizeof(float));
+}
+
+Workspace carve(void *base, size_t partial_floats) {
+    Workspace ws;
+    char *b = static_cast<char *>(base);
+    ws.counters = reinterpret_cast<unsigned *>(b);
+    ws.n_counters = kMaxCounters;
+    ws.partials = reinterpret_cast<float *>(b + kCounterBytes);
+    ws.partial_floats = partial_floats;
+    return ws;
+}
+
 void free_workspace(Workspace *ws) {
-    if (ws->partials) (void)hipFree(ws->partials);
+    // counters and partials share one allocation that starts at the counters
     if (ws->counters) (void)hipFree(ws->counters);
     *ws = Workspace();
 }
 
 int alloc_workspace(size_t partial_floats, size_t n_counters, Workspace *out) {
-    Workspace ws;
-    if (partial_floats) {
-        if (hipMalloc(&ws.partials, partial_floats * sizeof(float)) != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(Q4K_ENOMEM, "workspace: cannot allocate %zu floats", partial_floats);
-        }
-        ws.partial_floats = partial_floats;
+    if (n_counters > kMaxCounters) return fail(Q4K_EUNSUPPORTED, "more than %zu workgroups", kMaxCounters);
+    const size_t bytes = region_bytes(partial_floats);
+    void *base = nullptr;
+    if (hipMalloc(&base, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(Q4K_ENOMEM, "workspace: cannot allocate %zu bytes", bytes);
     }
-    if (n_counters) {
-        if (hipMalloc(&ws.counters, n_counters * sizeof(unsigned)) != hipSuccess) {
-            (void)hipGetLastError();
-            free_workspace(&ws);
-            return fail(Q4K_ENOMEM, "workspace: cannot allocate %zu counters", n_counters);
-        }
-        ws.n_counters = n_counters;
-        hipError_t e = hipMemset(ws.counters, 0, n_counters * sizeof(unsigned));
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e != hipSuccess) {
-            free_workspace(&ws);
-            return hip_fail(e, "hipMemset(workspace counters)");
-        }
+    hipError_t e = hipMemset(base, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        return hip_fail(e, "hipMemset(workspace)");
     }
-    *out = ws;
-    return Q4K_OK;
-}
-
-int stream_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters,
-                     Workspace *out) {
-    int dev = 0;
-    Q4K_HIP(hipGetDevice(&dev));
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &ws = g_ws[std::make_pair(dev, stream)];
-    if (ws.partial_floats >= partial_floats && ws.n_counters >= n_counters) {
-        *out = ws;
-        return Q4K_OK;
-    }
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    Q4K_HIP(hipStreamIsCapturing(stream, &cap));
-    if (cap != hipStreamCaptureStatusNone)
-        return fail(Q4K_EUNSUPPORTED,
-                    "workspace must grow during graph capture: make one call of this size on "
-                    "the stream before capturing");
-    // Work already queued on this stream may still use the old buffers.
-    Q4K_HIP(hipStreamSynchronize(stream));
-    Workspace grown;
-    int rc = alloc_workspace(std::max(partial_floats, ws.partial_floats),
-                             std::max(n_counters, ws.n_counters), &grown);
-    if (rc) return rc;
-    free_workspace(&ws);
-    ws = grown;
-    *out = ws;
+    *out = carve(base, partial_floats);
     return Q4K_OK;
 }
 
@@ -111,7 +89,9 @@ using namespace q4k;
 
 namespace {
 
-constexpr int64_t kMaxDim = 0x7FFFFFFF;
+constexpr int64_t kMaxRows = (int64_t)1 << 30;   // M
+constexpr int64_t kMaxCols = (int64_t)1 << 24;   // K: 63 row strides + a row run stay below 2^32
+constexpr int64_t kMaxDim = 0x7FFFFFFF;          // N, P
 
 int check_device() {
     int dev = 0;
@@ -131,11 +111,17 @@ int check_device() {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Shape limits.  Inside a 64-row tile the kernels address weights with
+// 32-bit offsets (row * row_bytes + chunk, row < 64) and the GEMM addresses
+// its bf16 X slice with a 32-bit byte offset of at most 16 * 2K; K <= 2^24
+// keeps both far below 2^31 for every block format (Q8_0's 34/32 bytes per
+// weight is the widest).  M <= 2^30 keeps tile indices times rows in int.
 int check_mk(int64_t M, int64_t K) {
     if (M < 0 || K <= 0 || K % 256 != 0)
         return fail(Q4K_ESHAPE, "need M >= 0 and K a positive multiple of 256 (M=%lld K=%lld)",
                     (long long)M, (long long)K);
-    if (M > kMaxDim || K > kMaxDim) return fail(Q4K_EUNSUPPORTED, "dimension beyond 2^31-1");
+    if (M > kMaxRows) return fail(Q4K_EUNSUPPORTED, "M=%lld beyond 2^30", (long long)M);
+    if (K > kMaxCols) return fail(Q4K_EUNSUPPORTED, "K=%lld beyond 2^24", (long long)K);
     return Q4K_OK;
 }
 
@@ -145,24 +131,77 @@ int check_ptr(const void *p, const char *name) {
     return Q4K_OK;
 }
 
+int check_ws(const void *ws, size_t ws_bytes, size_t need, const char *what) {
+    if (need == 0) return Q4K_OK;
+    if (!ws) return fail(Q4K_EINVAL, "%s: workspace is NULL (needs %zu bytes)", what, need);
+    if (((uintptr_t)ws & 255u) != 0)
+        return fail(Q4K_EALIGN, "%s: workspace is not 256-byte aligned", what);
+    if (ws_bytes < need)
+        return fail(Q4K_EINVAL, "%s: workspace of %zu bytes, needs %zu (q4k_workspace_size)", what,
+                    ws_bytes, need);
+    return Q4K_OK;
+}
+
 #define Q4K_TRY(expr)            \
     do {                         \
         int rc_ = (expr);        \
         if (rc_) return rc_;     \
     } while (0)
 
+// ---- workspace sizes (bytes) -------------------------------------------
+
+// A batched call splits N greedily into launches of 16, 8, 4, 2 and 1
+// vectors; its workspace covers the largest of them.
+size_t gemv_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    size_t partials = 0;
+    for (int nv = 16; nv >= 1; nv >>= 1) {
+        if (nv > N) continue;
+        const GemvLaunch L = choose_gemv_launch(M, K, nv, 1);
+        partials = std::max(partials, gemv_partial_floats(L, nv));
+    }
+    return region_bytes(partials);
+}
+
+size_t q8_ws_bytes(int64_t M, int64_t K) {
+    const GemvLaunch L = choose_gemv_q8_launch(M, K);
+    return region_bytes(gemv_partial_floats(L, 1));
+}
+
+size_t q6_ws_bytes(int64_t M, int64_t K) {
+    const GemvLaunch L = choose_gemv_q6_launch(M, K);
+    return region_bytes(gemv_partial_floats(L, 1));
+}
+
+// MLP workspace: [counters][partials][x * (1 + w)][sums of squares of x][activation]
+struct MlpLayout {
+    GemvLaunch Lg, Ld;
+    size_t partials, off_xg, off_sq, off_act, total;  // offsets in bytes
+};
+
+MlpLayout mlp_layout(int64_t hidden, int64_t inter, bool resid) {
+    MlpLayout m;
+    m.Lg = choose_gemv_launch(inter, hidden, 1, 2, EPI_SWIGLU);
+    m.Ld = choose_gemv_launch(hidden, inter, 1, 1, resid ? EPI_RESID : EPI_PLAIN);
+    m.partials = std::max(gemv_partial_floats(m.Lg, 1), gemv_partial_floats(m.Ld, 1));
+    m.off_xg = region_bytes(m.partials);
+    m.off_sq = m.off_xg + round256((size_t)hidden * sizeof(float));
+    m.off_act = m.off_sq + round256((size_t)((hidden + 31) / 32) * sizeof(float));
+    m.total = m.off_act + round256((size_t)inter * sizeof(float));
+    return m;
+}
+
+// GEMM workspace: [counter region, unused][partial tiles][bf16 copy of X]
+size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t P) {
+    const GemmLaunch L = choose_gemm_launch(M, K, P);
+    return region_bytes(gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P));
+}
+
+// The caller has checked the workspace against gemv_ws_bytes(M, K, N).
 int gemv_multi(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
-               hipStream_t stream) {
+               void *wsp, size_t ws_bytes, hipStream_t stream) {
+    (void)ws_bytes;
     // Pick the largest supported vector count at each step (16, 8, 4, 2, 1).
     int64_t done = 0;
-    size_t need_partials = 0;
-    const size_t need_counters = gemv_counters(M);
-    for (int nv = 16; nv >= 1; nv >>= 1) {
-        const GemvLaunch L = choose_gemv_launch(M, K, nv, 1);
-        need_partials = std::max(need_partials, gemv_partial_floats(L, M, nv, 1));
-    }
-    Workspace ws;
-    Q4K_TRY(stream_workspace(stream, need_partials, need_counters, &ws));
     while (done < N) {
         int nv = 16;
         while (nv > N - done) nv >>= 1;
@@ -177,6 +216,7 @@ int gemv_multi(const void *w, const float *X, float *Y, int64_t M, int64_t K, in
         p.nb = (int32_t)(K / 256);
         p.row_bytes = (K / 256) * 144;
         const GemvLaunch L = choose_gemv_launch(M, K, nv, 1);
+        const Workspace ws = carve(wsp, gemv_partial_floats(L, nv));
         p.ks = L.ks;
         p.ws = ws.partials;
         p.cnt = ws.counters;
@@ -192,7 +232,50 @@ extern "C" {
 
 const char *q4k_last_error(void) { return t_error.c_str(); }
 
-int q4k_version(void) { return 10000; }
+int q4k_version(void) { return 10100; }
+
+int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *bytes) {
+    clear_error();
+    if (!bytes) return fail(Q4K_EINVAL, "NULL output");
+    *bytes = 0;
+    switch (op) {
+        case Q4K_OP_GEMV:
+            Q4K_TRY(check_mk(M, K));
+            if (M > 0) *bytes = gemv_ws_bytes(M, K, 1);
+            return Q4K_OK;
+        case Q4K_OP_GEMV_BATCH:
+            Q4K_TRY(check_mk(M, K));
+            if (N < 0) return fail(Q4K_ESHAPE, "N must be >= 0");
+            if (N > kMaxDim) return fail(Q4K_EUNSUPPORTED, "N beyond 2^31-1");
+            if (M > 0 && N > 0) *bytes = gemv_ws_bytes(M, K, N);
+            return Q4K_OK;
+        case Q4K_OP_GEMV_Q8_0:
+            Q4K_TRY(check_mk(M, K));
+            if (M > 0) *bytes = q8_ws_bytes(M, K);
+            return Q4K_OK;
+        case Q4K_OP_GEMV_Q6_K:
+            Q4K_TRY(check_mk(M, K));
+            if (K % 1024 != 0)
+                return fail(Q4K_ESHAPE, "q4k_gemv_q6_k: K must be a multiple of 1024");
+            if (M > 0) *bytes = q6_ws_bytes(M, K);
+            return Q4K_OK;
+        case Q4K_OP_GEMM:
+            Q4K_TRY(check_mk(M, K));
+            if (N < 0) return fail(Q4K_ESHAPE, "P must be >= 0");
+            if (N > kMaxDim) return fail(Q4K_EUNSUPPORTED, "P beyond 2^31-1");
+            if (M > 0 && N > 0) *bytes = gemm_ws_bytes(M, K, N);
+            return Q4K_OK;
+        case Q4K_OP_MLP:
+            Q4K_TRY(check_mk(M, K));  // inter x hidden
+            Q4K_TRY(check_mk(K, M));  // hidden x inter
+            if (M == 0) return fail(Q4K_ESHAPE, "inter must be positive");
+            // sized for the residual variant, which needs at least as much
+            *bytes = std::max(mlp_layout(K, M, true).total, mlp_layout(K, M, false).total);
+            return Q4K_OK;
+        default:
+            return fail(Q4K_EINVAL, "unknown op %d", op);
+    }
+}
 
 int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream) {
     clear_error();
@@ -204,19 +287,21 @@ int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream) {
     return launch_dequant((const uint8_t *)w, out, M, K, (hipStream_t)stream);
 }
 
-int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream) {
+int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+             size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
     if (M == 0) return Q4K_OK;
     Q4K_TRY(check_ptr(w, "w"));
     Q4K_TRY(check_ptr(x, "x"));
     Q4K_TRY(check_ptr(y, "y"));
+    Q4K_TRY(check_ws(ws, ws_bytes, gemv_ws_bytes(M, K, 1), "gemv"));
     Q4K_TRY(check_device());
-    return gemv_multi(w, x, y, M, K, 1, (hipStream_t)stream);
+    return gemv_multi(w, x, y, M, K, 1, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
-                   void *stream) {
+                   void *ws, size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
     if (N < 0) return fail(Q4K_ESHAPE, "N must be >= 0");
@@ -225,12 +310,13 @@ int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K
     Q4K_TRY(check_ptr(w, "w"));
     Q4K_TRY(check_ptr(X, "X"));
     Q4K_TRY(check_ptr(Y, "Y"));
+    Q4K_TRY(check_ws(ws, ws_bytes, gemv_ws_bytes(M, K, N), "gemv_batch"));
     Q4K_TRY(check_device());
-    return gemv_multi(w, X, Y, M, K, N, (hipStream_t)stream);
+    return gemv_multi(w, X, Y, M, K, N, ws, ws_bytes, (hipStream_t)stream);
 }
 
-int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
-             void *stream) {
+int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P, void *ws,
+             size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
     if (P < 0) return fail(Q4K_ESHAPE, "P must be >= 0");
@@ -239,16 +325,15 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
     Q4K_TRY(check_ptr(w, "w"));
     Q4K_TRY(check_ptr(X, "X"));
     Q4K_TRY(check_ptr(Y, "Y"));
-    Q4K_TRY(check_device());
     const GemmLaunch L = choose_gemm_launch(M, K, P);
-    Workspace ws;
-    Q4K_TRY(stream_workspace((hipStream_t)stream,
-                             gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P),
-                             gemm_counters(M, P), &ws));
-    return launch_gemm((const uint8_t *)w, X, Y, M, K, P, L, ws, (hipStream_t)stream);
+    Q4K_TRY(check_ws(ws, ws_bytes, gemm_ws_bytes(M, K, P), "gemm"));
+    Q4K_TRY(check_device());
+    const Workspace w2 = carve(ws, gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P));
+    return launch_gemm((const uint8_t *)w, X, Y, M, K, P, L, w2, (hipStream_t)stream);
 }
 
-int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream) {
+int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+                  size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
     if (K % 1024 != 0)
@@ -257,11 +342,10 @@ int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K,
     Q4K_TRY(check_ptr(w, "w"));
     Q4K_TRY(check_ptr(x, "x"));
     Q4K_TRY(check_ptr(y, "y"));
-    Q4K_TRY(check_device());
     const GemvLaunch L = choose_gemv_q6_launch(M, K);
-    Workspace ws;
-    Q4K_TRY(stream_workspace((hipStream_t)stream, gemv_partial_floats(L, M, 1, 1),
-                             gemv_counters(M), &ws));
+    Q4K_TRY(check_ws(ws, ws_bytes, q6_ws_bytes(M, K), "gemv_q6_k"));
+    Q4K_TRY(check_device());
+    const Workspace w2 = carve(ws, gemv_partial_floats(L, 1));
     GemvParams p = {};
     p.w0 = (const uint8_t *)w;
     p.x = x;
@@ -273,23 +357,23 @@ int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K,
     p.nb = (int32_t)(K / 256);
     p.row_bytes = (K / 256) * 210;
     p.ks = L.ks;
-    p.ws = ws.partials;
-    p.cnt = ws.counters;
+    p.ws = w2.partials;
+    p.cnt = w2.counters;
     return launch_gemv_q6(p, L, (hipStream_t)stream);
 }
 
-int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream) {
+int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+                  size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(M, K));
     if (M == 0) return Q4K_OK;
     Q4K_TRY(check_ptr(w, "w"));
     Q4K_TRY(check_ptr(x, "x"));
     Q4K_TRY(check_ptr(y, "y"));
-    Q4K_TRY(check_device());
     const GemvLaunch L = choose_gemv_q8_launch(M, K);
-    Workspace ws;
-    Q4K_TRY(stream_workspace((hipStream_t)stream, gemv_partial_floats(L, M, 1, 1),
-                             gemv_counters(M), &ws));
+    Q4K_TRY(check_ws(ws, ws_bytes, q8_ws_bytes(M, K), "gemv_q8_0"));
+    Q4K_TRY(check_device());
+    const Workspace w2 = carve(ws, gemv_partial_floats(L, 1));
     GemvParams p = {};
     p.w0 = (const uint8_t *)w;
     p.x = x;
@@ -301,14 +385,14 @@ int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K,
     p.nb = (int32_t)(K / 32);
     p.row_bytes = (K / 32) * 34;
     p.ks = L.ks;
-    p.ws = ws.partials;
-    p.cnt = ws.counters;
+    p.ws = w2.partials;
+    p.cnt = w2.counters;
     return launch_gemv_q8(p, L, (hipStream_t)stream);
 }
 
 int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hidden,
             int64_t inter, const float *x, const float *norm_w, float eps, const float *resid,
-            float *y, float *act, void *stream) {
+            float *y, float *act, void *ws, size_t ws_bytes, void *stream) {
     clear_error();
     Q4K_TRY(check_mk(inter, hidden));  // gate and up: inter x hidden
     Q4K_TRY(check_mk(hidden, inter));  // down: hidden x inter
@@ -319,23 +403,16 @@ int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hi
     Q4K_TRY(check_ptr(x, "x"));
     Q4K_TRY(check_ptr(y, "y"));
     if (act) Q4K_TRY(check_ptr(act, "act"));
-    Q4K_TRY(check_device());
     const hipStream_t st = (hipStream_t)stream;
     const int epi_down = resid ? EPI_RESID : EPI_PLAIN;
-    const GemvLaunch Lg = choose_gemv_launch(inter, hidden, 1, 2, EPI_SWIGLU);
-    const GemvLaunch Ld = choose_gemv_launch(hidden, inter, 1, 1, epi_down);
-    auto round64 = [](size_t n) { return (n + 63) / 64 * 64; };
-    // workspace: [GEMV partials][x * (1 + w)][sums of squares of x][activation]
-    const size_t off_xg = round64(std::max(gemv_partial_floats(Lg, inter, 1, 2),
-                                           gemv_partial_floats(Ld, hidden, 1, 1)));
-    const size_t off_sq = off_xg + round64((size_t)hidden);
-    const size_t off_act = off_sq + round64((size_t)((hidden + 31) / 32));
-    const size_t total = off_act + (act ? 0 : round64((size_t)inter));
-    Workspace ws;
-    Q4K_TRY(stream_workspace(st, total, std::max(gemv_counters(inter), gemv_counters(hidden)),
-                             &ws));
-    float *xg = ws.partials + off_xg, *sq = ws.partials + off_sq;
-    float *a = act ? act : ws.partials + off_act;
+    const MlpLayout m = mlp_layout(hidden, inter, resid != nullptr);
+    Q4K_TRY(check_ws(ws, ws_bytes, m.total, "mlp"));
+    Q4K_TRY(check_device());
+    char *base = static_cast<char *>(ws);
+    const Workspace w2 = carve(base, m.partials);
+    float *xg = reinterpret_cast<float *>(base + m.off_xg);
+    float *sq = reinterpret_cast<float *>(base + m.off_sq);
+    float *a = act ? act : reinterpret_cast<float *>(base + m.off_act);
     Q4K_TRY(launch_norm_gain(x, norm_w, hidden, xg, sq, st));
     // a = silu(W_gate n) * (W_up n), n = x / rms(x) * (1 + w): the gain goes on
     // the input, the 1/rms on the outputs
@@ -350,14 +427,14 @@ int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hi
     p.K = (int32_t)hidden;
     p.nb = (int32_t)(hidden / 256);
     p.row_bytes = (hidden / 256) * 144;
-    p.ks = Lg.ks;
-    p.ws = ws.partials;
-    p.cnt = ws.counters;
+    p.ks = m.Lg.ks;
+    p.ws = w2.partials;
+    p.cnt = w2.counters;
     p.in_sq = sq;
     p.in_sq_n = (int32_t)((hidden + 31) / 32);
     p.in_len = (int32_t)hidden;
     p.eps = eps;
-    Q4K_TRY(launch_gemv(p, 1, 2, EPI_SWIGLU, Lg, st));
+    Q4K_TRY(launch_gemv(p, 1, 2, EPI_SWIGLU, m.Lg, st));
     // y = resid + W_down a (the activation is not normalised)
     GemvParams q = {};
     q.w0 = (const uint8_t *)w_down;
@@ -369,19 +446,11 @@ int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hi
     q.K = (int32_t)inter;
     q.nb = (int32_t)(inter / 256);
     q.row_bytes = (inter / 256) * 144;
-    q.ks = Ld.ks;
-    q.ws = ws.partials;
-    q.cnt = ws.counters;
+    q.ks = m.Ld.ks;
+    q.ws = w2.partials;
+    q.cnt = w2.counters;
     q.resid = resid;
-    return launch_gemv(q, 1, 1, epi_down, Ld, st);
-}
-
-void q4k_release_workspaces(void) {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (g_ws.empty()) return;
-    (void)hipDeviceSynchronize();
-    for (auto &kv : g_ws) free_workspace(&kv.second);
-    g_ws.clear();
+    return launch_gemv(q, 1, 1, epi_down, m.Ld, st);
 }
 
 /* Benchmark knobs: force the GEMV workgroup count and the GEMM tile width and
@@ -391,8 +460,8 @@ int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups) {
     clear_error();
     if (waves_per_group != 0 && waves_per_group != 4)
         return fail(Q4K_EINVAL, "waves_per_group must be 0 or 4");
-    if (workgroups < 0 || workgroups > (1 << 20))
-        return fail(Q4K_EINVAL, "workgroups must be in 0..2^20");
+    if (workgroups < 0 || workgroups > (int32_t)kMaxCounters)
+        return fail(Q4K_EINVAL, "workgroups must be in 0..%zu", kMaxCounters);
     set_gemv_override(workgroups);
     return Q4K_OK;
 }

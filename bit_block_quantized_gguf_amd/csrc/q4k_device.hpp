@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t and_mask(uint32_t v, uint32_t m) {
     return r;
 }
 
+// (v & m) | c in one v_and_or_b32, hidden from the optimiser like and_mask.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float ubyte(uint32_t v, int b) {
     return (float)((v >> (8 * b)) & 0xFFu);
 }

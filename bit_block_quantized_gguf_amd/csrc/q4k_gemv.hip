@@ -125,14 +125,36 @@ __device__ __forceinline__ WordQ word_unpack(uint32_t v) {
     return q;
 }
 
-// byte e of word w of the stage
+// Weight factors of one 32-byte quant group g (sub-blocks 2g and 2g+1): a
+// nibble c in a binary16 half is the subnormal c * 2^-24 (high nibbles sit
+// in place as 16 q), so with al = d*sc*2^24, ah = d*sc*2^20 and b = -dmin*m
+// one v_fma_mix_f32 fma(half, a, b) yields d*sc*q - dmin*m rounded once:
+// every product is exact (d has 11 significant bits, sc 6, q 4) and the
+// scaling by a power of two is exact, so the value is the dequantised weight,
+// bit for bit.
+struct GroupF {
+    float al, bl, ah, bh;
+};
+
+__device__ __forceinline__ GroupF group_factors(const Scales &sc, int g, float d24, float d20,
+                                                float ndm) {
+    GroupF f;
+    f.al = d24 * scale_of(sc, 2 * g);
+    f.bl = ndm * min_of(sc, 2 * g);
+    f.ah = d20 * scale_of(sc, 2 * g + 1);
+    f.bh = ndm * min_of(sc, 2 * g + 1);
+    return f;
+}
+
+// byte e of word w of the stage: the two weights it carries, each formed
+// exactly (one v_fma_mix_f32), then one FMA per vector and weight
 template <int NV, int SW>
-__device__ __forceinline__ void byte_fma(const WordQ &q, const XStage<NV, SW> &s, int w, int e,
-                                         float (&cl)[NV][2], float (&ch)[NV][2]) {
+__device__ __forceinline__ void byte_fma(const WordQ &q, const GroupF &f, const XStage<NV, SW> &s,
+                                         int w, int e, float (&cl)[NV][2], float (&ch)[NV][2]) {
     const int c = e & 1;
     const half2v ql = c ? q.l13 : q.l02, qh = c ? q.h13 : q.h02;
-    const float wl = (e & 2) ? (float)ql.y : (float)ql.x;
-    const float wh = (e & 2) ? (float)qh.y : (float)qh.x;
+    const float wl = fmaf((e & 2) ? (float)ql.y : (float)ql.x, f.al, f.bl);
+    const float wh = fmaf((e & 2) ? (float)qh.y : (float)qh.x, f.ah, f.bh);
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         cl[n][c] = fmaf(wl, s.l[n][4 * w + e], cl[n][c]);
@@ -140,12 +162,12 @@ __device__ __forceinline__ void byte_fma(const WordQ &q, const XStage<NV, SW> &s
     }
 }
 
-// block_dot for one or two vectors.  A nibble value c (0..15, or 16q for a
-// high nibble kept in place) sitting in a 16-bit half is, read as binary16,
-// the subnormal c * 2^-24 exactly, and v_fma_mix_f32 takes such a half as an
-// operand: each weight costs one FMA and no byte-to-float conversion.  The
-// sums carry the exact factor 2^-24, removed at the end by a power-of-two
-// scaling (exact unless a product falls below the f32 normal range).
+// block_dot for one or two vectors: acc[n] += sum over the block of w * x_n.
+// Each weight is formed exactly (group_factors) and enters one FMA per
+// vector, into four chains per vector (low/high nibbles, even/odd bytes) so
+// that neighbouring FMAs are independent.  Summing w*x rather than applying
+// the scales to separate sums of q*x and of x keeps the rounding error a
+// multiple of sum |w*x|, also on rows whose weights cancel (d*sc*q = dmin*m).
 // The activations are software-pipelined through SGPRs: the scalar loads of stage st+1 are issued
 // right after the first word of stage st has consumed its (already waited)
 // operands, so each wait for scalar data covers loads issued one stage
@@ -154,32 +176,31 @@ __device__ __forceinline__ void byte_fma(const WordQ &q, const XStage<NV, SW> &s
 // in flight.
 template <int NV>
 __device__ __forceinline__ void block_dot_mix(const uint4 (&b)[9], const float *xblk, int64_t xs,
-                                              const float4 (&xq)[NV], float (&acc)[NV]) {
+                                              float (&acc)[NV]) {
     constexpr int SW = NV == 1 ? 2 : 1;  // quant words per stage
     constexpr int SPG = 8 / SW;          // stages per group
     constexpr int NST = 4 * SPG;         // stages per block
     const float d = half_lo(b[0].x);
-    const float dmin = half_hi(b[0].x);
+    const float ndm = -half_hi(b[0].x);
+    const float d24 = d * 16777216.0f, d20 = d * 1048576.0f;
     const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
     cfloat *xc = as_const(xblk);
-    float A_lo[NV], A_hi[NV], B[NV];
     float cl[NV][2], ch[NV][2];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        A_lo[n] = A_hi[n] = B[n] = 0.f;
-        cl[n][0] = cl[n][1] = ch[n][0] = ch[n][1] = 0.f;
-    }
+    for (int n = 0; n < NV; ++n) cl[n][0] = cl[n][1] = ch[n][0] = ch[n][1] = 0.f;
     XStage<NV, SW> xs_a, xs_b;
     load_stage<NV, SW>(xs_a, xc, xs, 0);
+    GroupF f = group_factors(sc, 0, d24, d20, ndm);
     auto stage = [&](int st, const XStage<NV, SW> &cur, XStage<NV, SW> &nxt) {
         const int g = st / SPG;
+        if (st % SPG == 0 && g > 0) f = group_factors(sc, g, d24, d20, ndm);
 #pragma unroll
         for (int w = 0; w < SW; ++w) {
             const int i = SW * (st % SPG) + w;  // word of the group
             const WordQ q = word_unpack(word_of(b[1 + 2 * g + (i >> 2)], i & 3));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                byte_fma<NV, SW>(q, cur, w, e, cl, ch);
+                byte_fma<NV, SW>(q, f, cur, w, e, cl, ch);
                 if (w == 0 && e == 3) {
                     // The stage's first word has waited for its activations.
                     // The chains pass through an empty volatile asm, so the
@@ -194,102 +215,54 @@ __device__ __forceinline__ void block_dot_mix(const uint4 (&b)[9], const float *
                 }
             }
         }
-        if (st % SPG == SPG - 1) {  // group complete
-            const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
-#pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                A_lo[n] = fmaf(sl, cl[n][0] + cl[n][1], A_lo[n]);
-                A_hi[n] = fmaf(sh, ch[n][0] + ch[n][1], A_hi[n]);
-                cl[n][0] = cl[n][1] = ch[n][0] = ch[n][1] = 0.f;
-            }
-        }
     };
 #pragma unroll
     for (int st = 0; st < NST; st += 2) {
         stage(st, xs_a, xs_b);
         stage(st + 1, xs_b, xs_a);
     }
-    constexpr float kScale = 16777216.0f;  // 2^24 removes the binary16 subnormal scale
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        float s = (xq[n].x + xq[n].y) + (xq[n].z + xq[n].w);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb)
-            B[n] = fmaf(min_of(sc, sb),
-                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
-        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f * kScale, A_lo[n] * kScale), -dmin * B[n]);
-    }
+    for (int n = 0; n < NV; ++n) acc[n] += (cl[n][0] + cl[n][1]) + (ch[n][0] + ch[n][1]);
 }
 
-// acc[n] += sum over the block of w * x_n (factored form).  For three or
-// more vectors one byte-to-float conversion per weight is shared by NV FMAs
-// (the binary16 operand trick of block_dot_mix would cost a register pair per
-// weight instead); one and two vectors go to block_dot_mix.
+// acc[n] += sum over the block of w * x_n.  For three or more vectors each
+// weight is formed exactly once (one v_fma_mix_f32, as in block_dot_mix) and
+// shared by NV FMAs; one and two vectors go to block_dot_mix.
 template <int NV>
 __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk, int64_t xs,
-                                          const float4 (&xq)[NV], float (&acc)[NV]) {
+                                          float (&acc)[NV]) {
     if constexpr (NV <= 2) {
-        block_dot_mix<NV>(b, xblk, xs, xq, acc);
+        block_dot_mix<NV>(b, xblk, xs, acc);
         return;
     }
     const float d = half_lo(b[0].x);
-    const float dmin = half_hi(b[0].x);
+    const float ndm = -half_hi(b[0].x);
+    const float d24 = d * 16777216.0f, d20 = d * 1048576.0f;
     const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
-    float A_lo[NV], A_hi[NV], B[NV];
+    float tl[NV], th[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) A_lo[n] = A_hi[n] = B[n] = 0.f;
+    for (int n = 0; n < NV; ++n) tl[n] = th[n] = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        float tl[NV], th[NV];
-#pragma unroll
-        for (int n = 0; n < NV; ++n) tl[n] = th[n] = 0.f;
+        const GroupF f = group_factors(sc, g, d24, d20, ndm);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-            const uint32_t lo = and_mask(v, 0x0F0F0F0Fu);  // q
+            const WordQ q = word_unpack(word_of(b[1 + 2 * g + (i >> 2)], i & 3));
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const float q = ubyte(lo, bb);
+            for (int e = 0; e < 4; ++e) {
+                const half2v ql = (e & 1) ? q.l13 : q.l02, qh = (e & 1) ? q.h13 : q.h02;
+                const float wl = fmaf((e & 2) ? (float)ql.y : (float)ql.x, f.al, f.bl);
+                const float wh = fmaf((e & 2) ? (float)qh.y : (float)qh.x, f.ah, f.bh);
 #pragma unroll
-                for (int n = 0; n < NV; ++n)
-                    tl[n] = fmaf(q, as_const(xblk + n * xs + 64 * g)[4 * i + bb], tl[n]);
+                for (int n = 0; n < NV; ++n) {
+                    tl[n] = fmaf(wl, as_const(xblk + n * xs + 64 * g)[4 * i + e], tl[n]);
+                    th[n] = fmaf(wh, as_const(xblk + n * xs + 64 * g + 32)[4 * i + e], th[n]);
+                }
             }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t v = word_of(b[1 + 2 * g + (i >> 2)], i & 3);
-            const uint32_t hi = and_mask(v, 0xF0F0F0F0u);  // 16*q
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const float q = ubyte(hi, bb);
-#pragma unroll
-                for (int n = 0; n < NV; ++n)
-                    th[n] = fmaf(q, as_const(xblk + n * xs + 64 * g + 32)[4 * i + bb], th[n]);
-            }
-        }
-        const float sl = scale_of(sc, 2 * g), sh = scale_of(sc, 2 * g + 1);
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            A_lo[n] = fmaf(sl, tl[n], A_lo[n]);
-            A_hi[n] = fmaf(sh, th[n], A_hi[n]);
         }
     }
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        // per-sub-block sums of x: lanes 8s..8s+7 hold sub-block s's 32 values
-        float s = (xq[n].x + xq[n].y) + (xq[n].z + xq[n].w);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb)
-            B[n] = fmaf(min_of(sc, sb),
-                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * sb)), B[n]);
-        acc[n] += fmaf(d, fmaf(A_hi[n], 0.0625f, A_lo[n]), -dmin * B[n]);
-    }
+    for (int n = 0; n < NV; ++n) acc[n] += tl[n] + th[n];
 }
 
 // Inverse RMS of an input vector from its per-32-element sums of squares.
@@ -409,14 +382,21 @@ struct Units {
 };
 
 // A tile whose units are split between workgroups: each contributor stores
-// its partial sums with device-coherent stores (they bypass the per-XCD L2
-// copies, so no cache write-back or invalidation is needed), waits until they
-// have completed, and counts itself in on the tile's arrival counter.  The
-// last contributor adds all partials in workgroup order — the same sum
-// whichever workgroup arrives last — applies the epilogue and resets the
-// counter to zero for the next launch.  Counters start at zero when the
-// workspace is allocated.  The partials are loaded in chunks of 16 / NV
-// contributors, all loads of a chunk in flight together.
+// its partial sums with device-coherent stores (sc1: they bypass the per-XCD
+// L2 copies, so no cache write-back or invalidation is needed), waits until
+// they have completed, and counts itself in on the tile's arrival counter.
+// The last contributor reads the partials with device-coherent loads, adds
+// them in workgroup order — the same sum whichever workgroup arrives last —
+// applies the epilogue and resets the counter to zero for the next launch.
+// Counters start at zero in a fresh (zero-filled) workspace.  The partials
+// are loaded in chunks of 16 / NV contributors, all loads of a chunk in
+// flight together.
+//
+// Memory ordering rests on that hardware behaviour of gfx950 (completed sc1
+// stores are visible to sc1 loads from any XCD), not on release/acquire
+// atomics: those add an L2 write-back before the counter update and an L2
+// invalidate after it, which measured about twice the kernel time on the
+// 50 MB matrices (17408x5120: 18.3 -> 35.6 us).
 template <int NV, int NMAT, int EPI>
 __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Units &un, int g,
                                                   int t, int slot, int lane,
@@ -430,12 +410,15 @@ __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Uni
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores have completed
     const int gf = un.owner((int64_t)t * un.upt);
     const int gl = un.owner((int64_t)(t + 1) * un.upt - 1);
+    // The counter of tile t is that of its first contributor gf: a workgroup
+    // owns the first unit of at most one cut tile (any later tile starting in
+    // its range would make this one whole).
     unsigned old = 0;
     if (lane == 0)
-        old = __hip_atomic_fetch_add(&p.cnt[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __hip_atomic_fetch_add(&p.cnt[gf], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != (unsigned)(gl - gf)) return;  // not the last contributor
-    if (lane == 0) __hip_atomic_store(&p.cnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&p.cnt[gf], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Contributor g2 stored its partial in slot 0 when tile t is its first
     // tile.  Every contributor after gf starts inside tile t; gf does when its
     // range starts exactly at the tile's first unit.
@@ -561,14 +544,6 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         const bool active = j < p.nb;
         const bool last_of_tile = k + 1 == un.upt;
         const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
-        // activation sums for this block first, then the next unit's loads
-        float4 xq[NV];
-        if (active) {
-#pragma unroll
-            for (int n = 0; n < NV; ++n)
-                xq[n] = *reinterpret_cast<const float4 *>(p.x + n * p.x_stride + 256 * (int64_t)j +
-                                                          4 * lane);
-        }
         const bool more = u + 1 < ub;
         if (more) fetch(tn, kn);
         if (active) {
@@ -576,7 +551,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
             uint4 b[9];
 #pragma unroll
             for (int i = 0; i < 9; ++i) b[i] = *reinterpret_cast<const uint4 *>(lp + 16 * i);
-            block_dot<NV>(b, p.x + 256 * (int64_t)j, p.x_stride, xq, acc);
+            block_dot<NV>(b, p.x + 256 * (int64_t)j, p.x_stride, acc);
         }
         const bool seg_end = !more || last_of_tile;
         if (seg_end) {
@@ -648,19 +623,24 @@ constexpr int Q8_CH_UNIT = 64 * Q8_CH_ROW;     // 2176 chunks per unit
 constexpr int Q8_CH_THREAD = (Q8_CH_UNIT + 64 * WK - 1) / (64 * WK);  // 9 (the last for half the threads)
 static_assert(Q8_SEG % 16 == 0 && Q8_SEGP % 16 == 0, "16-byte chunks");
 
-// sum over a block's 32 quants of u * x (in units of 2^-24), u = q + 128;
-// q8 holds the 8 quant dwords, x the block's 32 activations.
+// sum over a block's 32 quants of q * x; q8 holds the 8 quant dwords, x the
+// block's 32 activations.  Two bytes at a time go into the 16-bit halves of
+// a dword as 0x6400 | (q + 128), the binary16 value 1024 + (q + 128), and one
+// v_pk_add_f16 of -1152 leaves q itself, exactly (small integers are exact in
+// binary16); each weight then costs one v_fma_mix_f32.
 __device__ __forceinline__ float q8_block_dot(const uint32_t (&q8)[8], cfloat *x) {
+    const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     float c0 = 0.f, c1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t u = q8[i] ^ 0x80808080u;
-        const half2v u02 = __builtin_bit_cast(half2v, and_mask(u, 0x00FF00FFu));       // u0, u2
-        const half2v u13 = __builtin_bit_cast(half2v, and_mask(u >> 8, 0x00FF00FFu));  // u1, u3
-        c0 = fmaf((float)u02.x, x[4 * i + 0], c0);
-        c1 = fmaf((float)u13.x, x[4 * i + 1], c1);
-        c0 = fmaf((float)u02.y, x[4 * i + 2], c0);
-        c1 = fmaf((float)u13.y, x[4 * i + 3], c1);
+        const uint32_t u = q8[i] ^ 0x80808080u;  // q + 128 per byte
+        const half2v q02 = __builtin_bit_cast(half2v, and_or(u, 0x00FF00FFu, 0x64006400u)) + bias;
+        const half2v q13 =
+            __builtin_bit_cast(half2v, and_or(u >> 8, 0x00FF00FFu, 0x64006400u)) + bias;
+        c0 = fmaf((float)q02.x, x[4 * i + 0], c0);
+        c1 = fmaf((float)q13.x, x[4 * i + 1], c1);
+        c0 = fmaf((float)q02.y, x[4 * i + 2], c0);
+        c1 = fmaf((float)q13.y, x[4 * i + 3], c1);
     }
     return c0 + c1;
 }
@@ -719,10 +699,6 @@ __global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, co
         const bool active = j < p.nb;                // nb is a multiple of 8: all 4 or none
         const bool last_of_tile = k + 1 == un.upt;
         const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
-        // block sums of x first (lanes 8b .. 8b+7 hold block b's 32 values),
-        // then the next unit's loads
-        float4 xq = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (active && lane < 32) xq = *reinterpret_cast<const float4 *>(p.x + 32 * (int64_t)j + 4 * lane);
         const bool more = u + 1 < ub;
         if (more) fetch(tn, kn);
         if (active) {
@@ -734,10 +710,6 @@ __global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, co
                 D[2 * i] = v.x;
                 D[2 * i + 1] = v.y;
             }
-            float s = (xq.x + xq.y) + (xq.z + xq.w);
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            s += __shfl_xor(s, 4);
             cfloat *xb = as_const(p.x + 32 * (int64_t)j);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -750,10 +722,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_q8_kernel(const GemvParams p, co
                 for (int i = 0; i < 8; ++i)
                     q8[i] = (b & 1) ? D[w0 + 1 + i]
                                     : __builtin_amdgcn_alignbyte(D[w0 + 1 + i], D[w0 + i], 2);
-                const float T = q8_block_dot(q8, xb + 32 * b);
-                const float X = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * b));
                 const float d = __half2float(__ushort_as_half((unsigned short)dbits));
-                acc = fmaf(d, fmaf(T, 16777216.0f, -128.0f * X), acc);
+                acc = fmaf(d, q8_block_dot(q8, xb + 32 * b), acc);
             }
         }
         const bool seg_end = !more || last_of_tile;
@@ -865,9 +835,6 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
         const int j = k * WK + wave;  // this wave's block
         const bool last_of_tile = k + 1 == un.upt;
         const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
-        // group sums of x first (lanes 4g .. 4g+3 hold group g's 16 values),
-        // then the next unit's loads
-        const float4 xq = *reinterpret_cast<const float4 *>(p.x + 256 * (int64_t)j + 4 * lane);
         const bool more = u + 1 < ub;
         if (more) fetch(tn, kn);
         {
@@ -883,11 +850,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
 #pragma unroll
                 for (int i = 0; i < 53; ++i) B[i] = __builtin_amdgcn_alignbit(D[i + 1], D[i], sh);
             }
-            float s = (xq.x + xq.y) + (xq.z + xq.w);
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
             cfloat *xb = as_const(p.x + 256 * (int64_t)j);
-            float A = 0.f, Bs = 0.f;
+            const half2v bias = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+            float A = 0.f;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -903,9 +868,13 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
                             const uint32_t hi = (c < 1 ? QH << 4 : c < 2 ? QH << 2 : c < 3 ? QH : QH >> 2) &
                                                 0x30303030u;
                             const uint32_t q4 = lo | hi;  // four six-bit quants, one per byte
-                            // bytes 0, 2 and 1, 3 into binary16 halves: q * 2^-24 exactly
-                            const half2v q02 = __builtin_bit_cast(half2v, and_mask(q4, 0x00FF00FFu));
-                            const half2v q13 = __builtin_bit_cast(half2v, and_mask(q4 >> 8, 0x00FF00FFu));
+                            // bytes 0, 2 and 1, 3 into binary16 halves as
+                            // 0x6400 | q = 1024 + q; adding -1056 leaves
+                            // q - 32 exactly
+                            const half2v q02 =
+                                __builtin_bit_cast(half2v, and_or(q4, 0x00FF00FFu, 0x64006400u)) + bias;
+                            const half2v q13 =
+                                __builtin_bit_cast(half2v, and_or(q4 >> 8, 0x00FF00FFu, 0x64006400u)) + bias;
                             const int kx = 128 * h + 32 * c + 4 * i;
                             t0 = fmaf((float)q02.x, xb[kx + 0], t0);
                             t1 = fmaf((float)q13.x, xb[kx + 1], t1);
@@ -916,13 +885,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_q6_kernel(const GemvParams p, co
                         const float scg =
                             (float)(int8_t)((B[48 + (grp >> 2)] >> (8 * (grp & 3))) & 0xFFu);
                         A = fmaf(scg, t0 + t1, A);
-                        Bs = fmaf(scg,
-                                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 4 * grp)),
-                                  Bs);
                     }
             const float d = __half2float(__ushort_as_half((unsigned short)(B[52] & 0xFFFFu)));
-            // A carries the exact factor 2^-24 of the binary16 quants
-            acc = fmaf(d, fmaf(-32.0f, Bs, A * 16777216.0f), acc);
+            acc = fmaf(d, A, acc);
         }
         const bool seg_end = !more || last_of_tile;
         if (seg_end) {
@@ -1062,15 +1027,11 @@ GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat, int epi) {
     return L;
 }
 
-size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat) {
-    (void)M;
-    (void)nmat;
+size_t gemv_partial_floats(const GemvLaunch &L, int nv) {
     return (size_t)L.ks * 2 * (size_t)nv * 64;
 }
 
-size_t gemv_counters(int64_t M) {
-    return (size_t)((M + 31) / 32);  // one arrival counter per tile (32 rows for the fused gate|up)
-}
+size_t gemv_counters(const GemvLaunch &L) { return (size_t)L.ks; }
 
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,
                 hipStream_t stream) {

@@ -20,9 +20,10 @@ int hip_fail(hipError_t e, const char *what);
     } while (0)
 
 // ---------------------------------------------------------------- workspace
-// Split-K partial sums and per-tile arrival counters.  Counters start at zero
-// and every kernel that uses one returns it to zero, so no clearing work is
-// ever enqueued on the hot path (and none is recorded into a graph).
+// Split-K partial sums and arrival counters.  They live in the caller's
+// workspace (a stack plan allocates its own at creation).  Counters start at
+// zero and every kernel that uses one returns it to zero, so no clearing work
+// is ever enqueued on the hot path (and none is recorded into a graph).
 struct Workspace {
     float *partials = nullptr;
     size_t partial_floats = 0;
@@ -30,12 +31,18 @@ struct Workspace {
     size_t n_counters = 0;
 };
 
-// Workspace of (current device, stream), grown to at least the given sizes.
-// Growth synchronises the stream before the old buffers are released.
-int stream_workspace(hipStream_t stream, size_t partial_floats, size_t n_counters,
-                     Workspace *out);
+// Every workspace layout starts with the same counter region of
+// kMaxCounters arrival counters (a GEMV grid has at most that many
+// workgroups), and no call writes data there: a workspace shared by calls of
+// different kinds keeps its counters at zero.  The call's own data follow.
+constexpr size_t kMaxCounters = 16384;
+constexpr size_t kCounterBytes = kMaxCounters * sizeof(unsigned);
+// Bytes of the counter region plus `partial_floats` floats; carve() splits a
+// base pointer into the two.
+size_t region_bytes(size_t partial_floats);
+Workspace carve(void *base, size_t partial_floats);
 
-// Allocate a zeroed workspace owned by the caller (used by stack plans).
+// Allocate a zeroed workspace owned by a stack plan (plan creation only).
 int alloc_workspace(size_t partial_floats, size_t n_counters, Workspace *out);
 void free_workspace(Workspace *ws);
 
@@ -79,9 +86,12 @@ struct GemvLaunch {
 // (from the kernel's occupancy), capped by the number of work units.
 GemvLaunch choose_gemv_launch(int64_t M, int64_t K, int nv, int nmat, int epi = EPI_PLAIN);
 
-// Workspace needs of a launch.
-size_t gemv_partial_floats(const GemvLaunch &L, int64_t M, int nv, int nmat);
-size_t gemv_counters(int64_t M);
+// Workspace needs of a launch: partial sums of the cut tiles (two slots of
+// nv x 64 floats per workgroup) and one arrival counter per workgroup (the
+// counter of a cut tile is that of the workgroup owning its first unit: a
+// workgroup owns the first unit of at most one cut tile).
+size_t gemv_partial_floats(const GemvLaunch &L, int nv);
+size_t gemv_counters(const GemvLaunch &L);
 
 // Enqueue one GEMV kernel.  nv in {1,2,4,8,16} for EPI_PLAIN; nv = 1 otherwise.
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,

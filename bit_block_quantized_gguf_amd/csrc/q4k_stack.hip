@@ -223,8 +223,8 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     size_t max_partials = 0, max_counters = 0;
     auto need = [&](int64_t M, int64_t K, int nmat, int epi) {
         const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
-        max_partials = std::max(max_partials, gemv_partial_floats(L, M, 1, nmat));
-        max_counters = std::max(max_counters, gemv_counters(M));
+        max_partials = std::max(max_partials, gemv_partial_floats(L, 1));
+        max_counters = std::max(max_counters, gemv_counters(L));
     };
     for (int32_t l = 0; l <= s->n_layers; ++l) {
         s->off_h.push_back(take(off, H));

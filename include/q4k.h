@@ -39,17 +39,44 @@
  *    enqueued, a negative q4k_status is returned and q4k_last_error() gives a
  *    message (per calling thread).
  *  - M, N or P equal to 0 is a valid no-op.  K must be a positive multiple of
- *    256.  Dimensions are limited to 2^31-1 rows/columns.
+ *    256.  Dimension limits: see "Supported sizes" below.
  *  - Required alignment: 16 bytes for w, x/X, y/Y and out.
  *  - Results are deterministic: the same call on the same inputs returns the
  *    same bits (all reductions run in a fixed order; no float atomics).
- *  - Partial sums of work split between workgroups live in a per-(device,
- *    stream) workspace that the library allocates on first use and keeps
- *    until q4k_release_workspaces() or process exit.  Calls queued on one stream are ordered; calls on
- *    different streams use different workspaces.  Make the first call on a
- *    stream outside HIP graph capture.
+ *  - Workspaces.  The GEMV-family calls, the MLP block and the GEMM use device
+ *    scratch memory besides their inputs and outputs (partial sums of work
+ *    split between workgroups and their arrival counters, the bf16 copy of
+ *    X, the MLP's intermediate vectors).  The caller owns it:
+ *    q4k_workspace_size() gives the bytes a call needs for its shape; pass
+ *    a device buffer `ws` of at least `ws_bytes` >= that many bytes,
+ *    256-byte aligned and zero-filled before its first use.  Every call
+ *    returns the buffer to a state valid for the next call (its counters to
+ *    zero), so a buffer is zeroed once, not per call.  If a call did not run
+ *    to completion (a failed launch, a device fault), zero it again.  Calls
+ *    that may execute at the same time (on different streams, or a captured
+ *    graph replayed while other work runs) need distinct workspaces; calls
+ *    ordered on one stream may share one, whatever their kind (every layout
+ *    starts with the same counter region, which no call writes data into).
+ *    A HIP graph that captured a call keeps using that call's workspace,
+ *    which must outlive the graph.
+ *  - Hot calls (everything except q4k_decode_stack_create and _destroy)
+ *    allocate no memory and never synchronise; they may be captured into a
+ *    HIP graph, the first call included.
+ *  - Supported sizes: K <= 2^24 (so that 32-bit offsets inside a 64-row tile
+ *    cannot wrap), M <= 2^30 rows; N and P <= 2^31 - 1.  Larger shapes return
+ *    Q4K_EUNSUPPORTED before anything is enqueued.
  *  - Non-finite d/dmin propagate as IEEE arithmetic does; they are outside
  *    the tested contract.
+ *  - Hardware assumption of the split-tile hand-off (gfx950): a tile cut
+ *    between workgroups is finished by its last-arriving contributor.  The
+ *    contributors store their partial sums with device-coherent (sc1) stores,
+ *    wait until those stores have completed, and count themselves in with a
+ *    device-scope atomic; the last one reads the partials with
+ *    device-coherent loads.  sc1 accesses bypass the per-XCD L2, so the
+ *    completed stores are visible to those loads without a cache-wide
+ *    write-back/invalidate.  Under the HIP memory model the atomics are
+ *    relaxed (release/acquire ordering would add an L2 write-back and
+ *    invalidate per hand-off, which measured twice the GEMV's time).
  */
 #ifndef Q4K_H
 #define Q4K_H
@@ -81,19 +108,47 @@ const char *q4k_last_error(void);
 int q4k_version(void);
 
 /*
- * Dequantise: out[i][k] = w_ik as f32, row-major [M][K].
+ * Dequantise: out[i][k] = w_ik as f32, row-major [M][K] (the per-weight value
+ * d*sc*q - dmin*m of a Q4_K super-block; the decode path reads the weights as
+ * raw q4_k blocks, "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", TL;DR and §4b,
+ * and its prefill dequantises them for the matrix cores, §4b q4k_gemm).
  * Bit-exact: the value is the exact d*sc*q - dmin*m rounded once to f32, the
- * same for any evaluation order (every product is exact in f32).
+ * same for any evaluation order (every product is exact in f32).  w, out:
+ * device pointers, 16-byte aligned; out holds M*K floats.  Needs no
+ * workspace.  Errors: Q4K_ESHAPE, Q4K_EINVAL (NULL), Q4K_EALIGN.
  */
 int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
+
+/*
+ * Bytes of workspace a call needs (see "Workspaces" above), for the current
+ * device and the current tuning knobs:
+ *   Q4K_OP_GEMV, Q4K_OP_GEMV_Q8_0, Q4K_OP_GEMV_Q6_K:  M x K matrix;
+ *   Q4K_OP_GEMV_BATCH: M x K matrix, N vectors;
+ *   Q4K_OP_GEMM: M x K matrix, P = N tokens;
+ *   Q4K_OP_MLP: M = inter, K = hidden (N ignored).
+ * Writes *bytes (a multiple of 256, possibly 0).  Errors: Q4K_EINVAL for an
+ * unknown op or NULL bytes, and the shape errors of the call itself.
+ */
+enum {
+    Q4K_OP_GEMV = 0, Q4K_OP_GEMV_BATCH = 1, Q4K_OP_GEMM = 2, Q4K_OP_GEMV_Q8_0 = 3,
+    Q4K_OP_GEMV_Q6_K = 4, Q4K_OP_MLP = 5
+};
+int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *bytes);
 
 /*
  * Batch-1 GEMV: y[i] = sum_k w_ik * x[k], x f32 [K], y f32 [M].
  * The decode matmul ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §2 decode
  * profile and §3): bandwidth-bound, one pass over the weight bytes.
  * f32 accumulation; |y - exact| stays within 1e-4 * sum_k |w_ik x_k| + 1e-6.
+ * Each weight is formed exactly (d*sc*q - dmin*m rounded once) before it
+ * meets x, so the bound also holds on rows whose weights cancel (a row of
+ * zero weights gives exactly 0).  ws/ws_bytes: the call's workspace (see
+ * "Workspaces"); Q4K_EINVAL if ws is NULL or ws_bytes is below
+ * q4k_workspace_size(Q4K_OP_GEMV, M, K, 1), Q4K_EALIGN if ws is not
+ * 256-byte aligned.
  */
-int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+             size_t ws_bytes, void *stream);
 
 /*
  * Q8_0 GEMV: y[i] = sum_k w_ik * x[k] for a Q8_0 matrix (public GGUF layout:
@@ -102,10 +157,13 @@ int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void
  * blocks).  The pages run the lm_head matmul in Q8 ("Mac Qwen3.6-27B Metal
  * Q4_K perf diagnosis", §2 decode profile).  K must be a positive multiple
  * of 256 (so row runs stay 16-byte aligned), x f32 [K], y f32 [M]; w, x, y
- * 16-byte aligned.  f32 accumulation within the q4k_gemv bound.  Same error
+ * 16-byte aligned.  f32 accumulation within the q4k_gemv bound (each quant
+ * enters as the exact small integer q, the scale once per block).
+ * Workspace: q4k_workspace_size(Q4K_OP_GEMV_Q8_0, M, K, 1).  Same error
  * codes as q4k_gemv.
  */
-int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /*
  * Q6_K GEMV: y[i] = sum_k w_ik * x[k] for a Q6_K matrix (public GGUF layout,
@@ -117,10 +175,13 @@ int q4k_gemv_q8_0(const void *w, const float *x, float *y, int64_t M, int64_t K,
  * K / 256 consecutive blocks.  K must be a positive multiple of 1024 (rows
  * of a multiple of four blocks, so row runs stay 8-byte aligned; every
  * Qwen3.6-27B shape qualifies), otherwise Q4K_ESHAPE.  x f32 [K], y f32 [M];
- * w, x, y 16-byte aligned.  f32 accumulation within the q4k_gemv bound.
+ * w, x, y 16-byte aligned.  f32 accumulation within the q4k_gemv bound (each
+ * quant enters as the exact small integer q - 32, the scales once per 16
+ * weights).  Workspace: q4k_workspace_size(Q4K_OP_GEMV_Q6_K, M, K, 1).
  * Other error codes as q4k_gemv.
  */
-int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *stream);
+int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /*
  * MLP block of one token (the model's SwiGLU feed-forward with its RMSNorm in
@@ -133,27 +194,30 @@ int q4k_gemv_q6_k(const void *w, const float *x, float *y, int64_t M, int64_t K,
  * w_gate, w_up: Q4_K [inter][hidden]; w_down: Q4_K [hidden][inter]; hidden and
  * inter positive multiples of 256.  x, norm_w, resid: f32 [hidden]; y: f32
  * [hidden]; act: optional f32 [inter] that receives a (NULL: kept in the
- * library's workspace).  Two GEMV launches (gate and up fused into one pass
+ * workspace).  Two GEMV launches (gate and up fused into one pass
  * with the SwiGLU in its epilogue, then down with the residual add) after a
  * small prologue that applies the gain.  y may alias x or resid (the down
  * pass runs after gate|up has read x); act must not alias the other vectors.
- * Each GEMV meets the q4k_gemv bound on its own inputs.  Errors:
- * Q4K_ESHAPE for bad dims, Q4K_EINVAL for NULL w/x/y or eps < 0 or not
- * finite, Q4K_EALIGN for w, x, y, act not 16-byte aligned.
+ * Each GEMV meets the q4k_gemv bound on its own inputs.  Workspace:
+ * q4k_workspace_size(Q4K_OP_MLP, inter, hidden, 0).  Errors: Q4K_ESHAPE for
+ * bad dims, Q4K_EINVAL for NULL w/x/y/ws, a workspace below that size, or
+ * eps < 0 or not finite, Q4K_EALIGN for w, x, y, act not 16-byte aligned or
+ * ws not 256-byte aligned.
  */
 int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hidden,
             int64_t inter, const float *x, const float *norm_w, float eps, const float *resid,
-            float *y, float *act, void *stream);
+            float *y, float *act, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * N-vector GEMV in one launch, weights read once:
  *   Y[n][i] = sum_k w_ik * X[n][k],  X f32 [N][K], Y f32 [N][M].
  * The batched witness of "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4b,
  * with N distinct activation vectors.  Any N >= 0; the kernels handle up to 16
- * vectors per weight pass.
+ * vectors per weight pass (N = 1 gives the q4k_gemv bits).  Workspace:
+ * q4k_workspace_size(Q4K_OP_GEMV_BATCH, M, K, N).  Errors as q4k_gemv.
  */
 int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
-                   void *stream);
+                   void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Prefill GEMM:  Y[p][i] = sum_k w_ik * X[p][k],  X f32 [P][K], Y f32 [P][M].
@@ -161,10 +225,13 @@ int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K
  * prefill phases and §4b; "Qwen3.6-27B on Apple M3 Pro — the llama.cpp
  * parity bar", the compute-bound prefill argument).  Weight tiles are
  * dequantised to bf16 (round to nearest even) in LDS, X is rounded to bf16,
- * products accumulate in f32 on the matrix cores.
+ * products accumulate in f32 on the matrix cores; |y - exact| stays within
+ * 5e-3 * sum_k |w_ik x_pk| + 1e-6.  Workspace (the bf16 copy of X and the
+ * partial tiles of stream-K): q4k_workspace_size(Q4K_OP_GEMM, M, K, P).
+ * Errors as q4k_gemv.
  */
 int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
-             void *stream);
+             void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Decode stack: the per-token chain of projection and MLP GEMVs of a
@@ -259,7 +326,7 @@ int q4k_gemv_config(int64_t M, int64_t K, int64_t N, int32_t *waves_per_group,
  * for a shape. */
 int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32_t *workgroups);
 
-/* Force the GEMV workgroup count (workgroups in 1..2^20, capped at the
+/* Force the GEMV workgroup count (workgroups in 1..16384, capped at the
  * number of work units; waves_per_group must be 0 or 4), or the GEMM tile
  * width (tile_tokens 0, 32, 64, 128 or 256) and workgroup count (0..4096, capped at
  * the number of tile x super-block work items); 0 restores the default of
@@ -267,10 +334,6 @@ int q4k_gemm_config(int64_t M, int64_t K, int64_t P, int32_t *tile_tokens, int32
  * for benchmark sweeps. */
 int q4k_tune_gemv(int32_t waves_per_group, int32_t workgroups);
 int q4k_tune_gemm(int32_t tile_tokens, int32_t workgroups);
-
-/* Free the split-K workspaces of all (device, stream) pairs.  Synchronises
- * the device first.  Safe to call at any time when no call is in flight. */
-void q4k_release_workspaces(void);
 
 #ifdef __cplusplus
 }

@@ -47,29 +47,34 @@ def test_library_is_gfx950_only():
 
 
 def test_version(lib):
-    assert lib.q4k_version() == 10000
+    assert lib.q4k_version() == 10100
 
 
 P = 0x10000  # fake, 16-byte aligned "device" address: never dereferenced
+WS = 0x40000  # fake 256-byte aligned workspace address
+BIG = 1 << 40  # a workspace size no call exceeds
 
 
 @pytest.mark.parametrize("M,K,code", [(-1, 256, -2), (4, 0, -2), (4, 100, -2), (4, 257, -2),
-                                      (4, -256, -2), (1 << 31, 256, -6)])
+                                      (4, -256, -2), (1 << 31, 256, -6), ((1 << 30) + 1, 256, -6),
+                                      (4, (1 << 24) + 256, -6)])
 def test_gemv_shape_errors(lib, M, K, code):
-    assert lib.q4k_gemv(P, P, P, M, K, None) == code
+    """Shapes outside the contract, including the limits that keep the
+    kernels' 32-bit in-tile offsets from wrapping (K <= 2^24, M <= 2^30)."""
+    assert lib.q4k_gemv(P, P, P, M, K, WS, BIG, None) == code
     assert lib.q4k_last_error()
 
 
 def test_null_and_alignment_errors(lib):
-    assert lib.q4k_gemv(None, P, P, 4, 256, None) == -1
-    assert lib.q4k_gemv(P, None, P, 4, 256, None) == -1
-    assert lib.q4k_gemv(P, P, None, 4, 256, None) == -1
-    assert lib.q4k_gemv(P + 4, P, P, 4, 256, None) == -3
-    assert lib.q4k_gemv(P, P + 8, P, 4, 256, None) == -3
+    assert lib.q4k_gemv(None, P, P, 4, 256, WS, BIG, None) == -1
+    assert lib.q4k_gemv(P, None, P, 4, 256, WS, BIG, None) == -1
+    assert lib.q4k_gemv(P, P, None, 4, 256, WS, BIG, None) == -1
+    assert lib.q4k_gemv(P + 4, P, P, 4, 256, WS, BIG, None) == -3
+    assert lib.q4k_gemv(P, P + 8, P, 4, 256, WS, BIG, None) == -3
     assert lib.q4k_dequant(P, P + 2, 4, 256, None) == -3
     assert b"aligned" in lib.q4k_last_error()
-    assert lib.q4k_gemv_batch(P, P, P, 4, 256, -1, None) == -2
-    assert lib.q4k_gemm(P, P, P, 4, 256, -3, None) == -2
+    assert lib.q4k_gemv_batch(P, P, P, 4, 256, -1, WS, BIG, None) == -2
+    assert lib.q4k_gemm(P, P, P, 4, 256, -3, WS, BIG, None) == -2
     assert b"P must be" in lib.q4k_last_error()
 
 
@@ -80,7 +85,7 @@ def test_mlp_validation(lib):
     ok = lambda **kw: dict(dict(wg=P, wu=P, wd=P, H=512, I=768, x=P, nw=None, eps=f(1e-6),
                                 r=None, y=P, act=None), **kw)
     call = lambda a: lib.q4k_mlp(a["wg"], a["wu"], a["wd"], a["H"], a["I"], a["x"], a["nw"],
-                                 a["eps"], a["r"], a["y"], a["act"], None)
+                                 a["eps"], a["r"], a["y"], a["act"], WS, BIG, None)
     for kw, code in (({"H": 500}, -2), ({"I": 0}, -2), ({"I": 100}, -2), ({"H": -256}, -2),
                      ({"wg": None}, -1), ({"wu": None}, -1), ({"wd": None}, -1),
                      ({"x": None}, -1), ({"y": None}, -1), ({"eps": f(-1.0)}, -1),
@@ -92,10 +97,10 @@ def test_mlp_validation(lib):
 
 def test_zero_sizes_are_noops(lib):
     # nothing is enqueued and no device is touched
-    assert lib.q4k_gemv(None, None, None, 0, 256, None) == 0
+    assert lib.q4k_gemv(None, None, None, 0, 256, None, 0, None) == 0
     assert lib.q4k_dequant(None, None, 0, 512, None) == 0
-    assert lib.q4k_gemv_batch(None, None, None, 5, 256, 0, None) == 0
-    assert lib.q4k_gemm(None, None, None, 5, 256, 0, None) == 0
+    assert lib.q4k_gemv_batch(None, None, None, 5, 256, 0, None, 0, None) == 0
+    assert lib.q4k_gemm(None, None, None, 5, 256, 0, None, 0, None) == 0
     assert lib.q4k_last_error() == b""
 
 
@@ -185,16 +190,113 @@ def test_product_path_has_no_oracle_or_fallback():
 def test_gemv_q6_k_shape_errors(lib, M, K, code):
     """K must be a positive multiple of 1024 (rows of a multiple of four
     210-byte blocks); checked before the pointers and the device."""
-    assert lib.q4k_gemv_q6_k(None, None, None, M, K, None) == code
+    assert lib.q4k_gemv_q6_k(None, None, None, M, K, WS, BIG, None) == code
     assert lib.q4k_last_error()
 
 
 def test_gemv_q6_k_pointer_errors_and_zero_rows(lib):
-    assert lib.q4k_gemv_q6_k(None, P, P, 4, 1024, None) == -1
-    assert lib.q4k_gemv_q6_k(P, None, P, 4, 1024, None) == -1
-    assert lib.q4k_gemv_q6_k(P, P, None, 4, 1024, None) == -1
-    assert lib.q4k_gemv_q6_k(P + 8, P, P, 4, 1024, None) == -3
-    assert lib.q4k_gemv_q6_k(P, P + 4, P, 4, 1024, None) == -3
-    assert lib.q4k_gemv_q6_k(P, P, P + 12, 4, 1024, None) == -3
-    assert lib.q4k_gemv_q6_k(None, None, None, 0, 2048, None) == 0
+    assert lib.q4k_gemv_q6_k(None, P, P, 4, 1024, WS, BIG, None) == -1
+    assert lib.q4k_gemv_q6_k(P, None, P, 4, 1024, WS, BIG, None) == -1
+    assert lib.q4k_gemv_q6_k(P, P, None, 4, 1024, WS, BIG, None) == -1
+    assert lib.q4k_gemv_q6_k(P + 8, P, P, 4, 1024, WS, BIG, None) == -3
+    assert lib.q4k_gemv_q6_k(P, P + 4, P, 4, 1024, WS, BIG, None) == -3
+    assert lib.q4k_gemv_q6_k(P, P, P + 12, 4, 1024, WS, BIG, None) == -3
+    assert lib.q4k_gemv_q6_k(None, None, None, 0, 2048, None, 0, None) == 0
     assert lib.q4k_last_error() == b""
+
+
+# ---------------------------------------------------------------- workspaces
+
+OPS = [(q4k.OP_GEMV, 17408, 5120, 1), (q4k.OP_GEMV_BATCH, 17408, 5120, 16),
+       (q4k.OP_GEMM, 5120, 17408, 1024), (q4k.OP_GEMV_Q8_0, 248320, 5120, 1),
+       (q4k.OP_GEMV_Q6_K, 5120, 17408, 1), (q4k.OP_MLP, 17408, 5120, 0)]
+
+
+@pytest.mark.parametrize("op,M,K,N", OPS)
+def test_workspace_size_reports(lib, op, M, K, N):
+    n = q4k.workspace_size(op, M, K, N)
+    assert n > 0 and n % 256 == 0
+
+
+def test_workspace_size_errors(lib):
+    n = ctypes.c_size_t(7)
+    assert lib.q4k_workspace_size(99, 4, 256, 1, ctypes.byref(n)) == -1
+    assert lib.q4k_workspace_size(q4k.OP_GEMV, 4, 256, 1, None) == -1
+    assert lib.q4k_workspace_size(q4k.OP_GEMV, 4, 100, 1, ctypes.byref(n)) == -2
+    assert lib.q4k_workspace_size(q4k.OP_GEMV_Q6_K, 4, 512, 1, ctypes.byref(n)) == -2
+    assert lib.q4k_workspace_size(q4k.OP_GEMV_BATCH, 4, 256, -1, ctypes.byref(n)) == -2
+    assert lib.q4k_workspace_size(q4k.OP_GEMV, 0, 256, 1, ctypes.byref(n)) == 0 and n.value == 0
+    # the batch needs at least the single-vector workspace and grows with N
+    one = q4k.workspace_size(q4k.OP_GEMV_BATCH, 4096, 5120, 1)
+    assert one == q4k.workspace_size(q4k.OP_GEMV, 4096, 5120)
+    assert q4k.workspace_size(q4k.OP_GEMV_BATCH, 4096, 5120, 16) > one
+    # the GEMM's workspace holds the bf16 copy of X: grows with P
+    assert (q4k.workspace_size(q4k.OP_GEMM, 5120, 5120, 1024)
+            > q4k.workspace_size(q4k.OP_GEMM, 5120, 5120, 256) >= 256 * 5120 * 2)
+
+
+@pytest.mark.parametrize("op,M,K,N", OPS)
+def test_workspace_checked_before_any_device_work(lib, op, M, K, N):
+    """A NULL, misaligned or too small workspace is rejected before the
+    device is touched (also here, with no GPU)."""
+    need = q4k.workspace_size(op, M, K, N)
+    f = ctypes.c_float(1e-6)
+
+    def call(ws, nbytes):
+        if op == q4k.OP_GEMV:
+            return lib.q4k_gemv(P, P, P, M, K, ws, nbytes, None)
+        if op == q4k.OP_GEMV_BATCH:
+            return lib.q4k_gemv_batch(P, P, P, M, K, N, ws, nbytes, None)
+        if op == q4k.OP_GEMM:
+            return lib.q4k_gemm(P, P, P, M, K, N, ws, nbytes, None)
+        if op == q4k.OP_GEMV_Q8_0:
+            return lib.q4k_gemv_q8_0(P, P, P, M, K, ws, nbytes, None)
+        if op == q4k.OP_GEMV_Q6_K:
+            return lib.q4k_gemv_q6_k(P, P, P, M, K, ws, nbytes, None)
+        return lib.q4k_mlp(P, P, P, K, M, P, None, f, None, P, None, ws, nbytes, None)
+
+    assert call(None, need) == -1 and b"NULL" in lib.q4k_last_error()
+    assert call(WS, need - 256) == -1 and b"workspace" in lib.q4k_last_error()
+    assert call(WS + 128, need) == -3
+    # with a large enough workspace the call gets as far as the device check
+    assert call(WS, need) not in (-1, -2, -3)
+
+
+# ---------------------------------------------------------------- binding checks
+
+def test_binding_checks_sizes_before_the_device():
+    """The binding checks the element count of every input and output (an
+    undersized tensor would make a kernel write past it) before anything
+    else; on this GPU-less host a correctly sized CPU tensor then fails the
+    device check instead."""
+    torch = pytest.importorskip("torch")
+    f32, u8 = torch.float32, torch.uint8
+    w = torch.zeros(64 * 2 * 144, dtype=u8)               # 64 x 512 Q4_K
+    x, y = torch.zeros(512, dtype=f32), torch.zeros(64, dtype=f32)
+
+    def raises(msg, fn):
+        with pytest.raises((ValueError, TypeError)) as e:
+            fn()
+        assert msg in str(e.value), str(e.value)
+
+    raises("w holds", lambda: q4k.gemv(w[:-1], x, y, M=64, K=512))
+    raises("x has 511", lambda: q4k.gemv(w, x[:-1], y, M=64, K=512))
+    raises("y has 63", lambda: q4k.gemv(w, x, y[:-1], M=64, K=512))
+    raises("device", lambda: q4k.gemv(w, x, y, M=64, K=512))
+    raises("out has", lambda: q4k.dequant(w, 64, 512, out=torch.zeros(64 * 511, dtype=f32)))
+    X = torch.zeros((3, 512), dtype=f32)
+    raises("Y has", lambda: q4k.gemv_batch(w, X, torch.zeros((3, 63), dtype=f32), M=64, K=512))
+    raises("X must be", lambda: q4k.gemv_batch(w, torch.zeros((3, 500), dtype=f32), M=64, K=512))
+    raises("Y has", lambda: q4k.gemm(w, X, torch.zeros((2, 64), dtype=f32), M=64, K=512))
+    wq8 = torch.zeros(64 * 16 * 34, dtype=u8)
+    raises("y has", lambda: q4k.gemv_q8_0(wq8, x, y[:10], M=64, K=512))
+    wq6 = torch.zeros(64 * 4 * 210, dtype=u8)
+    raises("x has", lambda: q4k.gemv_q6_k(wq6, torch.zeros(1000, dtype=f32), M=64, K=1024))
+    wg = torch.zeros(256 * 2 * 144, dtype=u8)             # 256 x 512
+    wd = torch.zeros(512 * 1 * 144, dtype=u8)             # 512 x 256
+    h = torch.zeros(512, dtype=f32)
+    for kw, msg in (({"y": torch.zeros(511, dtype=f32)}, "y has"),
+                    ({"resid": torch.zeros(100, dtype=f32)}, "resid has"),
+                    ({"norm_w": torch.zeros(513, dtype=f32)}, "norm_w has"),
+                    ({"act": torch.zeros(255, dtype=f32)}, "act has")):
+        raises(msg, lambda: q4k.mlp(wg, wg, wd, h, hidden=512, inter=256, **kw))
