@@ -32,7 +32,7 @@ EXPORTS = (
     "q4k_gemv_q8_0", "q4k_gemv_q6_k", "q4k_mlp", "q4k_gemv_batch", "q4k_gemm",
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
-    "q4k_tune_gemv", "q4k_tune_gemm",
+    "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc",
 )
 OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP = range(6)
 
@@ -88,6 +88,8 @@ def load(path: str | None = None):
     L.q4k_gemm.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
     L.q4k_mlp.argtypes = [p, p, p, i64, i64, p, p, ctypes.c_float, p, p, p, p, sz, p]
     L.q4k_gemv_q8_0.argtypes = [p, p, p, i64, i64, p, sz, p]
+    L.q4k_gemv_noalloc.argtypes = [p, p, p, i64, i64, p]
+    L.q4k_gemv_noalloc.restype = ctypes.c_int
     L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p, sz, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
     L.q4k_decode_stack.argtypes = [p, p, p, p]
@@ -261,6 +263,22 @@ def gemv(w, x, y=None, M: int | None = None, K: int | None = None, ws=None):
     ws = _ws(OP_GEMV, M, K, 1, ws)
     check(load().q4k_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, ws.ptr, ws.nbytes,
                           _stream()))
+    return y
+
+
+def gemv_noalloc(w, x, y=None, M: int | None = None, K: int | None = None):
+    """q4k_gemv_noalloc: the GEMV with its scratch in the library's fixed
+    per-device array (no workspace; calls on one GPU must not overlap)."""
+    torch = _torch()
+    if M is None:
+        M, K = weight_shape(w)
+    _weights(w, M, K)
+    _tensor(x, torch.float32, "x", K)
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=w.device)
+    _tensor(y, torch.float32, "y", M)
+    _on_gpu(w=w, x=x, y=y)
+    check(load().q4k_gemv_noalloc(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, K, _stream()))
     return y
 
 

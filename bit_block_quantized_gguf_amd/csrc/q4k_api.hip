@@ -300,6 +300,18 @@ int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void
     return gemv_multi(w, x, y, M, K, 1, ws, ws_bytes, (hipStream_t)stream);
 }
 
+int q4k_gemv_noalloc(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                     void *stream) {
+    clear_error();
+    Q4K_TRY(check_mk(M, K));
+    if (M == 0) return Q4K_OK;
+    Q4K_TRY(check_ptr(w, "w"));
+    Q4K_TRY(check_ptr(x, "x"));
+    Q4K_TRY(check_ptr(y, "y"));
+    Q4K_TRY(check_device());
+    return gemv_noalloc(w, x, y, M, K, (hipStream_t)stream);
+}
+
 int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
                    void *ws, size_t ws_bytes, void *stream) {
     clear_error();

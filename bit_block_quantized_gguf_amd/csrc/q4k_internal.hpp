@@ -107,6 +107,11 @@ int launch_gemv_q8(const GemvParams &p, const GemvLaunch &L, hipStream_t stream)
 GemvLaunch choose_gemv_q6_launch(int64_t M, int64_t K);
 int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream);
 
+// q4k_gemv with its split-tile scratch in a fixed per-device array instead of
+// a caller workspace (q4k_noalloc.hip).
+int gemv_noalloc(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                 hipStream_t stream);
+
 // Per-32-element sums of squares of v[0..n) (used to seed the stack).
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
 

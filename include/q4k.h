@@ -151,6 +151,24 @@ int q4k_gemv(const void *w, const float *x, float *y, int64_t M, int64_t K, void
              size_t ws_bytes, void *stream);
 
 /*
+ * q4k_gemv for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture that must not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation): same kernel, same
+ * launch shape and the same output bits as q4k_gemv, with the split-tile
+ * scratch (partial sums and arrival counters, about 0.6 MB) in a fixed
+ * device array that the library holds on each GPU it runs on until the
+ * process ends.  Every call on a GPU shares that GPU's array: calls that may
+ * overlap in time on one GPU (different streams, concurrent graph replays)
+ * race and must be ordered by the caller.  The counters start at zero and
+ * every completed call leaves them at zero.  Limit: the launch may use at
+ * most 1024 workgroups (the GEMV uses at most two per CU); beyond it the
+ * call returns Q4K_EUNSUPPORTED before anything is enqueued.  Other errors
+ * as q4k_gemv.  Allocates nothing, never synchronises.
+ */
+int q4k_gemv_noalloc(const void *w, const float *x, float *y, int64_t M, int64_t K,
+                     void *stream);
+
+/*
  * Q8_0 GEMV: y[i] = sum_k w_ik * x[k] for a Q8_0 matrix (public GGUF layout:
  * 34 bytes per 32 weights, a little-endian binary16 scale d then 32
  * two's-complement int8 quants, w = d * q; rows of K / 32 consecutive
