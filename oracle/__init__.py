@@ -17,6 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q4k_oracle.c")
+_SRC_MIX = os.path.join(_HERE, "mixer_oracle.c")
 _HDR = os.path.join(_HERE, "q4k_oracle.h")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
@@ -31,12 +32,12 @@ _i64 = ctypes.c_int64
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (OpenMP over rows, -O2, strict IEEE)."""
-    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_MIX), os.path.getmtime(_HDR))
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp",
                                "-ffp-contract=off", "-fno-fast-math",
-                               "-o", tmp, _SRC, "-lm"])
+                               "-o", tmp, _SRC, _SRC_MIX, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -76,6 +77,12 @@ def _load():
         L.oracle_dequant_q8_0.argtypes = [_p, _i64, _i64, _p]
         L.oracle_gemv_q8_0_rows_d.restype = ctypes.c_int
         L.oracle_gemv_q8_0_rows_d.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        i32, dbl = ctypes.c_int32, ctypes.c_double
+        L.oracle_gdn_step.restype = ctypes.c_int
+        L.oracle_gdn_step.argtypes = [i32, i32, i32, i32, dbl] + [_p] * 8
+        L.oracle_attn_step.restype = ctypes.c_int
+        L.oracle_attn_step.argtypes = [i32, i32, i32, i32, dbl, dbl, _p, _p, _p, _p, _p, _i64,
+                                       _i64, _p]
         L.oracle_dequant_q6_k_block.restype = None
         L.oracle_dequant_q6_k_block.argtypes = [_p, _p]
         L.oracle_dequant_q6_k.restype = ctypes.c_int
@@ -304,3 +311,43 @@ def stack(mats, shapes, n_layers: int, hidden: int, h0, eps: float = RMS_EPS,
                                 h0.ctypes.data, logits.ctypes.data,
                                 hid.ctypes.data if hid is not None else None))
     return (logits, hid) if want_hidden else logits
+
+
+def _d(a, n=None):
+    a = np.ascontiguousarray(a, np.float64)
+    assert n is None or a.size == n, (a.size, n)
+    return a
+
+
+def gdn_step(u, conv_w, a_log, dt_bias, norm_w, conv_state, S, Hk=16, Hv=48, Dk=128, Dv=128,
+             eps=RMS_EPS):
+    """One Gated DeltaNet decode step (mixer_oracle.c) in double.  Returns
+    (out [Hv*Dv], new conv_state [C][3], new S [Hv][Dv][Dk]); inputs are not
+    modified.  u: [2*Hk*Dk + 2*Hv*Dv + 2*Hv]."""
+    C = 2 * Hk * Dk + Hv * Dv
+    u = _d(u, C + Hv * Dv + 2 * Hv)
+    cs = _d(conv_state, 3 * C).copy()
+    St = _d(S, Hv * Dv * Dk).copy()
+    out = np.empty(Hv * Dv, np.float64)
+    _check(_load().oracle_gdn_step(Hk, Hv, Dk, Dv, float(eps), u.ctypes.data,
+                                   _d(conv_w, 4 * C).ctypes.data, _d(a_log, Hv).ctypes.data,
+                                   _d(dt_bias, Hv).ctypes.data, _d(norm_w, Dv).ctypes.data,
+                                   cs.ctypes.data, St.ctypes.data, out.ctypes.data))
+    return out, cs.reshape(C, 3), St.reshape(Hv, Dv, Dk)
+
+
+def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos, Hq=24, Hkv=4, D=256, R=64,
+              theta=1e7, eps=RMS_EPS):
+    """One gated full-attention decode step at position pos (mixer_oracle.c)
+    in double.  Caches [Hkv][cap][D] (positions < pos filled).  Returns (out
+    [Hq*D], new k_cache, new v_cache); inputs are not modified."""
+    kc = np.array(k_cache, np.float64, copy=True, order="C")
+    vc = np.array(v_cache, np.float64, copy=True, order="C")
+    cap = kc.shape[1]
+    u = _d(u, Hq * 2 * D + 2 * Hkv * D)
+    out = np.empty(Hq * D, np.float64)
+    _check(_load().oracle_attn_step(Hq, Hkv, D, R, float(theta), float(eps), u.ctypes.data,
+                                    _d(q_norm_w, D).ctypes.data, _d(k_norm_w, D).ctypes.data,
+                                    kc.ctypes.data, vc.ctypes.data, cap, int(pos),
+                                    out.ctypes.data))
+    return out, kc, vc

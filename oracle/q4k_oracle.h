@@ -96,6 +96,16 @@ int oracle_stack(const uint8_t *const *mats, const int64_t *Ms, const int64_t *K
 void oracle_set_threads(int32_t n);
 int32_t oracle_get_threads(void);
 
+/* Token mixers (mixer_oracle.c): one decode step of the Gated DeltaNet
+ * recurrence and of gated full attention, in double.  See that file for the
+ * equations.  Return 0, or -1 for bad sizes. */
+int oracle_gdn_step(int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, double eps, const double *u,
+                    const double *conv_w, const double *a_log, const double *dt_bias,
+                    const double *norm_w, double *conv_state, double *S, double *out);
+int oracle_attn_step(int32_t Hq, int32_t Hkv, int32_t D, int32_t R, double theta, double eps,
+                     const double *u, const double *q_norm_w, const double *k_norm_w,
+                     double *k_cache, double *v_cache, int64_t cap, int64_t pos, double *out);
+
 #ifdef __cplusplus
 }
 #endif
