@@ -32,9 +32,9 @@ EXPORTS = (
     "q4k_gemv_q8_0", "q4k_gemv_q6_k", "q4k_mlp", "q4k_gemv_batch", "q4k_gemm",
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
-    "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc",
+    "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc", "q4k_gdn_step", "q4k_attn_step",
 )
-OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP = range(6)
+OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP = range(7)
 
 _lib = None
 
@@ -52,6 +52,20 @@ class MatDesc(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("mix_in", MatDesc), ("mix_out", MatDesc),
                 ("gate", MatDesc), ("up", MatDesc), ("down", MatDesc)]
+
+
+class GdnParams(ctypes.Structure):
+    _fields_ = [("key_heads", ctypes.c_int32), ("value_heads", ctypes.c_int32),
+                ("key_dim", ctypes.c_int32), ("value_dim", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("conv_w", ctypes.c_void_p), ("a_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float),
+                ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p)]
 
 
 class StackDesc(ctypes.Structure):
@@ -90,6 +104,10 @@ def load(path: str | None = None):
     L.q4k_gemv_q8_0.argtypes = [p, p, p, i64, i64, p, sz, p]
     L.q4k_gemv_noalloc.argtypes = [p, p, p, i64, i64, p]
     L.q4k_gemv_noalloc.restype = ctypes.c_int
+    L.q4k_gdn_step.argtypes = [ctypes.POINTER(GdnParams), p, p, p, p, p, sz, p]
+    L.q4k_gdn_step.restype = ctypes.c_int
+    L.q4k_attn_step.argtypes = [ctypes.POINTER(AttnParams), p, p, p, i64, i64, p, p]
+    L.q4k_attn_step.restype = ctypes.c_int
     L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p, sz, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
     L.q4k_decode_stack.argtypes = [p, p, p, p]
@@ -393,6 +411,59 @@ def gemm(w, X, Y=None, M: int | None = None, K: int | None = None, ws=None):
     check(load().q4k_gemm(w.data_ptr(), X.data_ptr(), Y.data_ptr(), M, K, P, ws.ptr, ws.nbytes,
                           _stream()))
     return Y
+
+
+def gdn_step(u, conv_w, a_log, dt_bias, norm_w, conv_state, state, out=None, key_heads=16,
+             value_heads=48, eps: float = 1e-6, ws=None):
+    """One Gated DeltaNet token (q4k_gdn_step): updates conv_state [C, 3] and
+    state [Hv, 128, 128] in place, returns out [Hv*128]."""
+    torch = _torch()
+    Hk, Hv, D = key_heads, value_heads, 128
+    C = (2 * Hk + Hv) * D
+    f32 = torch.float32
+    _tensor(u, f32, "u", C + Hv * D + 2 * Hv)
+    _tensor(conv_w, f32, "conv_w", 4 * C)
+    _tensor(a_log, f32, "a_log", Hv)
+    _tensor(dt_bias, f32, "dt_bias", Hv)
+    _tensor(norm_w, f32, "norm_w", D)
+    _tensor(conv_state, f32, "conv_state", 3 * C)
+    _tensor(state, f32, "state", Hv * D * D)
+    if out is None:
+        out = torch.empty(Hv * D, dtype=f32, device=u.device)
+    _tensor(out, f32, "out", Hv * D)
+    _on_gpu(u=u, conv_w=conv_w, a_log=a_log, dt_bias=dt_bias, norm_w=norm_w,
+            conv_state=conv_state, state=state, out=out)
+    ws = _ws(OP_GDN_STEP, Hk, Hv, 0, ws)
+    prm = GdnParams(Hk, Hv, D, D, float(eps), conv_w.data_ptr(), a_log.data_ptr(),
+                    dt_bias.data_ptr(), norm_w.data_ptr())
+    check(load().q4k_gdn_step(ctypes.byref(prm), u.data_ptr(), conv_state.data_ptr(),
+                              state.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes, _stream()))
+    return out
+
+
+def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos: int, out=None, q_heads=24,
+              kv_heads=4, rope_dim=64, rope_theta: float = 1e7, eps: float = 1e-6):
+    """One gated full-attention token at position pos (q4k_attn_step): writes
+    position pos of k_cache/v_cache [Hkv, capacity, 256], returns out [Hq*256]."""
+    torch = _torch()
+    D, f32 = 256, torch.float32
+    _tensor(u, f32, "u", q_heads * 2 * D + 2 * kv_heads * D)
+    _tensor(q_norm_w, f32, "q_norm_w", D)
+    _tensor(k_norm_w, f32, "k_norm_w", D)
+    if k_cache.dim() != 3 or k_cache.shape[0] != kv_heads or k_cache.shape[2] != D:
+        raise ValueError("k_cache must be [kv_heads, capacity, 256]")
+    cap = k_cache.shape[1]
+    _tensor(k_cache, f32, "k_cache", kv_heads * cap * D)
+    _tensor(v_cache, f32, "v_cache", kv_heads * cap * D)
+    if out is None:
+        out = torch.empty(q_heads * D, dtype=f32, device=u.device)
+    _tensor(out, f32, "out", q_heads * D)
+    _on_gpu(u=u, q_norm_w=q_norm_w, k_norm_w=k_norm_w, k_cache=k_cache, v_cache=v_cache, out=out)
+    prm = AttnParams(q_heads, kv_heads, D, rope_dim, float(rope_theta), float(eps),
+                     q_norm_w.data_ptr(), k_norm_w.data_ptr())
+    check(load().q4k_attn_step(ctypes.byref(prm), u.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), cap, int(pos), out.data_ptr(), _stream()))
+    return out
 
 
 def gemv_config(M: int, K: int, N: int = 1) -> tuple[int, int]:

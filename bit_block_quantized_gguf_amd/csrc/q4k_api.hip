@@ -196,6 +196,11 @@ size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t P) {
     return region_bytes(gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P));
 }
 
+// GDN step workspace: [counter region, unused][conv outputs, beta, alpha]
+size_t gdn_ws_bytes(int Hk, int Hv) {
+    return region_bytes((size_t)(2 * Hk + Hv) * 128 + 2 * (size_t)Hv);
+}
+
 // The caller has checked the workspace against gemv_ws_bytes(M, K, N).
 int gemv_multi(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
                void *wsp, size_t ws_bytes, hipStream_t stream) {
@@ -271,6 +276,12 @@ int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *byte
             if (M == 0) return fail(Q4K_ESHAPE, "inter must be positive");
             // sized for the residual variant, which needs at least as much
             *bytes = std::max(mlp_layout(K, M, true).total, mlp_layout(K, M, false).total);
+            return Q4K_OK;
+        case Q4K_OP_GDN_STEP:
+            if (M <= 0 || K <= 0 || K % M != 0 || M > 4096 || K > 4096)
+                return fail(Q4K_ESHAPE, "gdn: key heads %lld, value heads %lld", (long long)M,
+                            (long long)K);
+            *bytes = gdn_ws_bytes((int)M, (int)K);
             return Q4K_OK;
         default:
             return fail(Q4K_EINVAL, "unknown op %d", op);
@@ -463,6 +474,61 @@ int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hi
     q.cnt = w2.counters;
     q.resid = resid;
     return launch_gemv(q, 1, 1, epi_down, m.Ld, st);
+}
+
+int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, float *state,
+                 float *out, void *ws, size_t ws_bytes, void *stream) {
+    clear_error();
+    if (!p) return fail(Q4K_EINVAL, "NULL parameters");
+    if (p->key_heads <= 0 || p->value_heads <= 0 || p->value_heads % p->key_heads != 0 ||
+        p->key_heads > 4096 || p->value_heads > 4096)
+        return fail(Q4K_ESHAPE, "gdn: need value heads a positive multiple of key heads");
+    if (p->key_dim != 128 || p->value_dim != 128)
+        return fail(Q4K_ESHAPE, "gdn: key and value head dimensions must be 128");
+    if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return fail(Q4K_EINVAL, "eps must be finite and >= 0");
+    Q4K_TRY(check_ptr(u, "u"));
+    Q4K_TRY(check_ptr(conv_state, "conv_state"));
+    Q4K_TRY(check_ptr(state, "state"));
+    Q4K_TRY(check_ptr(out, "out"));
+    Q4K_TRY(check_ptr(p->conv_w, "conv_w"));
+    Q4K_TRY(check_ptr(p->a_log, "a_log"));
+    Q4K_TRY(check_ptr(p->dt_bias, "dt_bias"));
+    Q4K_TRY(check_ptr(p->norm_w, "norm_w"));
+    Q4K_TRY(check_ws(ws, ws_bytes, gdn_ws_bytes(p->key_heads, p->value_heads), "gdn_step"));
+    Q4K_TRY(check_device());
+    GdnShape sh{p->key_heads, p->value_heads, p->eps};
+    float *scratch = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
+    return launch_gdn_step(sh, u, p->conv_w, p->a_log, p->dt_bias, p->norm_w, conv_state, state,
+                           out, scratch, (hipStream_t)stream);
+}
+
+int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, float *v_cache,
+                  int64_t capacity, int64_t pos, float *out, void *stream) {
+    clear_error();
+    if (!p) return fail(Q4K_EINVAL, "NULL parameters");
+    if (p->head_dim != 256) return fail(Q4K_ESHAPE, "attention: head dimension must be 256");
+    if (p->q_heads <= 0 || p->kv_heads <= 0 || p->q_heads % p->kv_heads != 0 ||
+        p->q_heads > 65536)
+        return fail(Q4K_ESHAPE, "attention: need query heads a positive multiple of kv heads");
+    if (p->rope_dim < 0 || p->rope_dim > 256 || p->rope_dim % 2 != 0)
+        return fail(Q4K_ESHAPE, "attention: rope_dim must be even and in 0..256");
+    if (capacity <= 0 || pos < 0 || pos >= capacity)
+        return fail(Q4K_ESHAPE, "attention: position %lld outside the cache of %lld",
+                    (long long)pos, (long long)capacity);
+    if (capacity > ((int64_t)1 << 40) / 256 / p->kv_heads)
+        return fail(Q4K_EUNSUPPORTED, "attention: cache too large");
+    if (!(p->eps >= 0.f) || !std::isfinite(p->eps) || !(p->rope_theta > 0.f))
+        return fail(Q4K_EINVAL, "eps must be >= 0 and rope_theta > 0");
+    Q4K_TRY(check_ptr(u, "u"));
+    Q4K_TRY(check_ptr(k_cache, "k_cache"));
+    Q4K_TRY(check_ptr(v_cache, "v_cache"));
+    Q4K_TRY(check_ptr(out, "out"));
+    Q4K_TRY(check_ptr(p->q_norm_w, "q_norm_w"));
+    Q4K_TRY(check_ptr(p->k_norm_w, "k_norm_w"));
+    Q4K_TRY(check_device());
+    AttnShape sh{p->q_heads, p->kv_heads, p->rope_dim, p->rope_theta, p->eps};
+    return launch_attn_step(sh, u, p->q_norm_w, p->k_norm_w, k_cache, v_cache, capacity, pos,
+                            nullptr, out, (hipStream_t)stream);
 }
 
 /* Benchmark knobs: force the GEMV workgroup count and the GEMM tile width and

@@ -123,6 +123,24 @@ int launch_norm_gain(const float *x, const float *w, int64_t n, float *xg, float
 // Tuning override for benchmarks: workgroup count (0 = occupancy-based).
 void set_gemv_override(int groups);
 
+// ---------------------------------------------------------------- token mixers
+struct GdnShape {
+    int Hk, Hv;   // key heads, value heads (head dimension 128 for both)
+    float eps;
+};
+struct AttnShape {
+    int Hq, Hkv, R;  // query heads, key/value heads (head dimension 256), rotary dims
+    float theta, eps;
+};
+// scratch: (2*Hk + Hv) * 128 + 2*Hv floats (conv outputs, beta and alpha)
+int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, const float *a_log,
+                    const float *dt_bias, const float *norm_w, float *conv_state, float *S,
+                    float *out, float *scratch, hipStream_t stream);
+// pos_dev, when not null, holds the position (read on the device); else pos.
+int launch_attn_step(const AttnShape &s, const float *u, const float *q_norm_w,
+                     const float *k_norm_w, float *k_cache, float *v_cache, int64_t cap,
+                     int64_t pos, const int64_t *pos_dev, float *out, hipStream_t stream);
+
 // ---------------------------------------------------------------- dequant
 int launch_dequant(const uint8_t *w, float *out, int64_t M, int64_t K, hipStream_t stream);
 

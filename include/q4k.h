@@ -125,13 +125,14 @@ int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
  *   Q4K_OP_GEMV, Q4K_OP_GEMV_Q8_0, Q4K_OP_GEMV_Q6_K:  M x K matrix;
  *   Q4K_OP_GEMV_BATCH: M x K matrix, N vectors;
  *   Q4K_OP_GEMM: M x K matrix, P = N tokens;
- *   Q4K_OP_MLP: M = inter, K = hidden (N ignored).
+ *   Q4K_OP_MLP: M = inter, K = hidden (N ignored);
+ *   Q4K_OP_GDN_STEP: M = key heads, K = value heads (N ignored).
  * Writes *bytes (a multiple of 256, possibly 0).  Errors: Q4K_EINVAL for an
  * unknown op or NULL bytes, and the shape errors of the call itself.
  */
 enum {
     Q4K_OP_GEMV = 0, Q4K_OP_GEMV_BATCH = 1, Q4K_OP_GEMM = 2, Q4K_OP_GEMV_Q8_0 = 3,
-    Q4K_OP_GEMV_Q6_K = 4, Q4K_OP_MLP = 5
+    Q4K_OP_GEMV_Q6_K = 4, Q4K_OP_MLP = 5, Q4K_OP_GDN_STEP = 6
 };
 int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *bytes);
 
@@ -250,6 +251,67 @@ int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K
  */
 int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
              void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Token mixers of the hybrid model, one decode token ("Qwen3.6-27B on Apple
+ * M3 Pro — the llama.cpp parity bar", architecture list: Gated DeltaNet
+ * layers with a kernel-4 causal conv, 16 key / 48 value heads of 128, swish
+ * output gate and an f32 recurrent state; full-attention layers with 24
+ * query / 4 key-value heads of 256, output gate, partial rotary over a
+ * quarter of each head with theta 1e7, (1 + w) q/k RMSNorm).  They run
+ * between a layer's mixer-in and mixer-out projections ("Mac Qwen3.6-27B
+ * Metal Q4_K perf diagnosis", §2: the recurrence and the attention/conv/
+ * norm/gate work outside the matmuls; §4: on the device, one submission per
+ * token).  All pointers are device pointers, f32, 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+
+/* Gated DeltaNet, one token.  With Hk key heads, Hv value heads (a multiple
+ * of Hk) and head dimension 128, C = (2*Hk + Hv) * 128 conv channels:
+ *   u       [C + Hv*128 + 2*Hv]  mixer-in output: q | k | v | z | b | a
+ *   conv_w  [C][4]   depthwise causal conv taps, oldest input first
+ *   conv_state [C][3] the channel's last three inputs, oldest first (updated)
+ *   a_log, dt_bias [Hv];  norm_w [128]
+ *   state   [Hv][128][128] recurrent state, value-dimension major:
+ *           state[h][dv][dk] (updated)
+ *   out     [Hv*128]
+ * Per token: c = silu(conv), q and k L2-normalised per key head (q also by
+ * 1/sqrt(128)), value head h reads key head h / (Hv/Hk);
+ * beta = sigmoid(b), alpha = exp(-exp(a_log) * softplus(a + dt_bias));
+ * S <- alpha S; S <- S + k (beta (v - S^T k))^T; o = S^T q;
+ * out = norm_w * o / sqrt(mean(o^2) + eps) * silu(z).
+ * Workspace: q4k_workspace_size(Q4K_OP_GDN_STEP, Hk, Hv, 0).  Two kernels;
+ * the state is read and written once (64 KB per value head).  Errors:
+ * Q4K_EINVAL (NULL, bad eps, small workspace), Q4K_ESHAPE (Hk, Hv not
+ * positive or Hv not a multiple of Hk, key_dim or value_dim not 128),
+ * Q4K_EALIGN. */
+typedef struct {
+    int32_t key_heads, value_heads, key_dim, value_dim; /* dims must be 128 */
+    float eps;                                           /* e.g. 1e-6 */
+    const float *conv_w, *a_log, *dt_bias, *norm_w;
+} q4k_gdn_params;
+int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, float *state,
+                 float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Gated full attention, one token at position pos (0 <= pos < capacity;
+ * the caches hold positions 0 .. pos-1 from earlier calls):
+ *   u       [Hq*2*256 + 2*Hkv*256]  per query head [q | gate], then k, then v
+ *   q_norm_w, k_norm_w [256]  (1 + w) RMSNorm weights
+ *   k_cache, v_cache [Hkv][capacity][256]  position pos is written
+ *   out     [Hq*256]
+ * q and k: x / sqrt(mean(x^2) + eps) * (1 + w), then rotary on the first
+ * rope_dim dims (pairs i, i + rope_dim/2; angle pos * theta^(-2i/rope_dim));
+ * query head h attends with key/value head h / (Hq/Hkv):
+ * out_h = softmax(q . k_t / 16) v over t = 0..pos, times sigmoid(gate_h).
+ * Needs no workspace.  Errors: Q4K_EINVAL (NULL), Q4K_ESHAPE (head_dim not
+ * 256, Hq not a multiple of Hkv, rope_dim odd or above 256, pos outside
+ * 0..capacity-1), Q4K_EALIGN. */
+typedef struct {
+    int32_t q_heads, kv_heads, head_dim, rope_dim; /* head_dim must be 256 */
+    float rope_theta, eps;                          /* e.g. 1e7, 1e-6 */
+    const float *q_norm_w, *k_norm_w;
+} q4k_attn_params;
+int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, float *v_cache,
+                  int64_t capacity, int64_t pos, float *out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Decode stack: the per-token chain of projection and MLP GEMVs of a

@@ -325,13 +325,14 @@ def gdn_step(u, conv_w, a_log, dt_bias, norm_w, conv_state, S, Hk=16, Hv=48, Dk=
     (out [Hv*Dv], new conv_state [C][3], new S [Hv][Dv][Dk]); inputs are not
     modified.  u: [2*Hk*Dk + 2*Hv*Dv + 2*Hv]."""
     C = 2 * Hk * Dk + Hv * Dv
+    # every converted array is held in a local until the call returns
     u = _d(u, C + Hv * Dv + 2 * Hv)
+    cw, al, dt, nw = _d(conv_w, 4 * C), _d(a_log, Hv), _d(dt_bias, Hv), _d(norm_w, Dv)
     cs = _d(conv_state, 3 * C).copy()
     St = _d(S, Hv * Dv * Dk).copy()
     out = np.empty(Hv * Dv, np.float64)
-    _check(_load().oracle_gdn_step(Hk, Hv, Dk, Dv, float(eps), u.ctypes.data,
-                                   _d(conv_w, 4 * C).ctypes.data, _d(a_log, Hv).ctypes.data,
-                                   _d(dt_bias, Hv).ctypes.data, _d(norm_w, Dv).ctypes.data,
+    _check(_load().oracle_gdn_step(Hk, Hv, Dk, Dv, float(eps), u.ctypes.data, cw.ctypes.data,
+                                   al.ctypes.data, dt.ctypes.data, nw.ctypes.data,
                                    cs.ctypes.data, St.ctypes.data, out.ctypes.data))
     return out, cs.reshape(C, 3), St.reshape(Hv, Dv, Dk)
 
@@ -345,9 +346,9 @@ def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos, Hq=24, Hkv=4, D=256,
     vc = np.array(v_cache, np.float64, copy=True, order="C")
     cap = kc.shape[1]
     u = _d(u, Hq * 2 * D + 2 * Hkv * D)
+    qw, kw = _d(q_norm_w, D), _d(k_norm_w, D)
     out = np.empty(Hq * D, np.float64)
     _check(_load().oracle_attn_step(Hq, Hkv, D, R, float(theta), float(eps), u.ctypes.data,
-                                    _d(q_norm_w, D).ctypes.data, _d(k_norm_w, D).ctypes.data,
-                                    kc.ctypes.data, vc.ctypes.data, cap, int(pos),
-                                    out.ctypes.data))
+                                    qw.ctypes.data, kw.ctypes.data, kc.ctypes.data,
+                                    vc.ctypes.data, cap, int(pos), out.ctypes.data))
     return out, kc, vc

@@ -300,3 +300,44 @@ def test_binding_checks_sizes_before_the_device():
                     ({"norm_w": torch.zeros(513, dtype=f32)}, "norm_w has"),
                     ({"act": torch.zeros(255, dtype=f32)}, "act has")):
         raises(msg, lambda: q4k.mlp(wg, wg, wd, h, hidden=512, inter=256, **kw))
+
+
+# ---------------------------------------------------------------- token mixers
+
+def test_gdn_step_validation(lib):
+    ok = dict(key_heads=16, value_heads=48, key_dim=128, value_dim=128, eps=1e-6,
+              conv_w=P, a_log=P, dt_bias=P, norm_w=P)
+    need = q4k.workspace_size(q4k.OP_GDN_STEP, 16, 48)
+    assert need >= (2 * 16 + 48) * 128 * 4 + 2 * 48 * 4
+
+    def call(ws=WS, nbytes=need, u=P, **kw):
+        prm = q4k.GdnParams(**dict(ok, **kw))
+        return lib.q4k_gdn_step(ctypes.byref(prm), u, P, P, P, ws, nbytes, None)
+
+    assert lib.q4k_gdn_step(None, P, P, P, P, WS, need, None) == -1
+    for kw, code in (({"value_heads": 40}, -2), ({"key_heads": 0}, -2), ({"key_dim": 64}, -2),
+                     ({"value_dim": 256}, -2), ({"eps": -1.0}, -1), ({"eps": float("nan")}, -1),
+                     ({"conv_w": None}, -1), ({"norm_w": P + 4}, -3), ({"u": None}, -1),
+                     ({"u": P + 8}, -3), ({"ws": None}, -1), ({"nbytes": need - 256}, -1),
+                     ({"ws": WS + 16}, -3)):
+        assert call(**kw) == code, kw
+        assert lib.q4k_last_error()
+    assert call() not in (-1, -2, -3)   # valid: gets as far as the device check
+
+
+def test_attn_step_validation(lib):
+    ok = dict(q_heads=24, kv_heads=4, head_dim=256, rope_dim=64, rope_theta=1e7, eps=1e-6,
+              q_norm_w=P, k_norm_w=P)
+
+    def call(cap=64, pos=3, u=P, kc=P, **kw):
+        prm = q4k.AttnParams(**dict(ok, **kw))
+        return lib.q4k_attn_step(ctypes.byref(prm), u, kc, P, cap, pos, P, None)
+
+    assert lib.q4k_attn_step(None, P, P, P, 64, 0, P, None) == -1
+    for kw, code in (({"head_dim": 128}, -2), ({"q_heads": 25}, -2), ({"kv_heads": 0}, -2),
+                     ({"rope_dim": 63}, -2), ({"rope_dim": 258}, -2), ({"pos": 64}, -2),
+                     ({"pos": -1}, -2), ({"cap": 0}, -2), ({"rope_theta": 0.0}, -1),
+                     ({"u": None}, -1), ({"kc": P + 4}, -3), ({"q_norm_w": None}, -1)):
+        assert call(**kw) == code, kw
+        assert lib.q4k_last_error()
+    assert call() not in (-1, -2, -3)
