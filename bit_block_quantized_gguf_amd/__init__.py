@@ -24,7 +24,9 @@ BLOCK_BYTES = 144
 Q4K_OK = 0
 STATUS = {0: "Q4K_OK", -1: "Q4K_EINVAL", -2: "Q4K_ESHAPE", -3: "Q4K_EALIGN",
           -4: "Q4K_ENOMEM", -5: "Q4K_EHIP", -6: "Q4K_EUNSUPPORTED"}
-BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS = range(7)
+(BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS, BUF_MIX, BUF_CONV_STATE, BUF_GDN_STATE,
+ BUF_K_CACHE, BUF_V_CACHE) = range(12)
+STACK_MIXERS = 1
 
 # Every symbol include/q4k.h declares (checked by the CPU test suite).
 EXPORTS = (
@@ -33,6 +35,7 @@ EXPORTS = (
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
     "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc", "q4k_gdn_step", "q4k_attn_step",
+    "q4k_decode_stack_reset", "q4k_decode_stack_position",
 )
 OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP = range(7)
 
@@ -68,10 +71,15 @@ class AttnParams(ctypes.Structure):
                 ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p)]
 
 
+class MixerDesc(ctypes.Structure):
+    _fields_ = [("gdn", GdnParams), ("attn", AttnParams)]
+
+
 class StackDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int64), ("n_layers", ctypes.c_int32),
                 ("layers", ctypes.POINTER(LayerDesc)), ("lm_head", MatDesc),
-                ("eps", ctypes.c_float), ("flags", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("flags", ctypes.c_int32),
+                ("mixers", ctypes.POINTER(MixerDesc)), ("attn_capacity", ctypes.c_int64)]
 
 
 def load(path: str | None = None):
@@ -113,6 +121,10 @@ def load(path: str | None = None):
     L.q4k_decode_stack.argtypes = [p, p, p, p]
     L.q4k_decode_stack_buffer.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(i64)]
     L.q4k_decode_stack_nodes.argtypes = [p, ctypes.POINTER(i64)]
+    L.q4k_decode_stack_reset.argtypes = [p, p]
+    L.q4k_decode_stack_reset.restype = ctypes.c_int
+    L.q4k_decode_stack_position.argtypes = [p, ctypes.POINTER(i64)]
+    L.q4k_decode_stack_position.restype = ctypes.c_int
     L.q4k_decode_stack_destroy.argtypes = [p]
     L.q4k_decode_stack_destroy.restype = None
     L.q4k_gemv_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -497,9 +509,16 @@ class DecodeStack:
     ``layers``: list of dicts with keys mix_in, mix_out, gate, up, down, each a
     uint8 device tensor [M, K/256*144]; ``lm_head`` likewise.  The tensors are
     borrowed (kept referenced here) and must not be freed while the plan lives.
+
+    ``mixers`` (optional): one dict per layer with the real token mixer's
+    parameters — for kind 0 (Gated DeltaNet) conv_w, a_log, dt_bias, norm_w
+    (f32 device tensors) and key_heads, value_heads; for kind 1 (attention)
+    q_norm_w, k_norm_w and q_heads, kv_heads, rope_dim, rope_theta — with
+    ``attn_capacity`` KV-cache positions.
     """
 
-    def __init__(self, layers, lm_head, hidden: int, eps: float = 1e-6, kinds=None):
+    def __init__(self, layers, lm_head, hidden: int, eps: float = 1e-6, kinds=None, mixers=None,
+                 attn_capacity: int = 0):
         torch = _torch()
         self._keep = []
         arr = (LayerDesc * max(1, len(layers)))()
@@ -520,13 +539,44 @@ class DecodeStack:
         self.hidden = hidden
         self.vocab = M
         self.n_layers = len(layers)
+        flags, mix_arr = 0, None
+        if mixers is not None:
+            flags = STACK_MIXERS
+            mix_arr = (MixerDesc * max(1, len(layers)))()
+            f32 = torch.float32
+            for i, m in enumerate(mixers):
+                for t in m.values():
+                    if isinstance(t, torch.Tensor):
+                        _tensor(t, f32, "mixer parameter")
+                        _on_gpu(mixer_parameter=t)
+                        self._keep.append(t)
+                ptr = lambda k: m[k].data_ptr() if k in m else None
+                if arr[i].kind == 0:
+                    mix_arr[i].gdn = GdnParams(m.get("key_heads", 16), m.get("value_heads", 48),
+                                               128, 128, float(m.get("eps", 1e-6)), ptr("conv_w"),
+                                               ptr("a_log"), ptr("dt_bias"), ptr("norm_w"))
+                else:
+                    mix_arr[i].attn = AttnParams(m.get("q_heads", 24), m.get("kv_heads", 4), 256,
+                                                 m.get("rope_dim", 64),
+                                                 float(m.get("rope_theta", 1e7)),
+                                                 float(m.get("eps", 1e-6)), ptr("q_norm_w"),
+                                                 ptr("k_norm_w"))
         desc = StackDesc(hidden, len(layers), arr, MatDesc(lm_head.data_ptr(), M, K),
-                         float(eps), 0)
-        self._desc_layers = arr
+                         float(eps), flags, mix_arr, int(attn_capacity))
+        self._desc_layers = (arr, mix_arr)
         h = ctypes.c_void_p()
         check(load().q4k_decode_stack_create(ctypes.byref(desc), _stream(), ctypes.byref(h)))
         self._h = h
         self._device = torch.cuda.current_device()
+
+    def reset(self):
+        """Mixer states to zero and the position to 0."""
+        check(load().q4k_decode_stack_reset(self._h, _stream()))
+
+    def position(self) -> int:
+        n = ctypes.c_int64()
+        check(load().q4k_decode_stack_position(self._h, ctypes.byref(n)))
+        return n.value
 
     def __call__(self, h_in, logits=None):
         torch = _torch()

@@ -203,6 +203,7 @@ __global__ __launch_bounds__(256) void attn_step_kernel(
     const int h = blockIdx.x, d = threadIdx.x;
     const int g = h / (Hq / Hkv);
     const int64_t pos = pos_dev ? *pos_dev : pos_val;
+    if (pos < 0 || pos >= cap) return;  // the callers keep pos inside the cache
     const float *uq = u + (int64_t)h * 2 * AD;
     const float *uk = u + (int64_t)Hq * 2 * AD + (int64_t)g * AD;
     const float *uv = u + (int64_t)Hq * 2 * AD + (int64_t)Hkv * AD + (int64_t)g * AD;

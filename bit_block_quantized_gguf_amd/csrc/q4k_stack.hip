@@ -17,6 +17,14 @@
 // Every GEMV's epilogue writes the per-32-row sums of squares of its
 // output; the consumer adds them in a fixed order to get its input's RMS, so
 // RMS normalisation costs no extra pass and no extra node.
+//
+// With the real token mixers ("Qwen3.6-27B on Apple M3 Pro — the llama.cpp
+// parity bar", architecture list; §4 of the diagnosis page asks for the GDN
+// recurrence and the attention on the device too), each layer runs
+//   u = W_in rmsn(h);  o = GDN step(u) or attention step(u, pos);
+//   sumsq(o);  h_mid = h + W_out rmsn(o);  then the MLP as above,
+// and a last one-thread node advances the device-side position.  The plan
+// owns the recurrent states and KV caches.
 #include "q4k_internal.hpp"
 
 #include <string.h>
@@ -36,27 +44,78 @@ struct q4k_stack {
     q4k_mat lm_head{};
     float *arena = nullptr;
     size_t arena_floats = 0;
-    std::vector<int64_t> off_h, off_u, off_hmid, off_g, off_v, off_a;
+    std::vector<int64_t> off_h, off_u, off_hmid, off_g, off_v, off_a, off_o;
     int64_t off_logits = 0;
     float *sq = nullptr;  // per-tile sums of squares
     size_t sq_floats = 0;
-    std::vector<int64_t> sq_h, sq_u, sq_hmid, sq_a;
+    std::vector<int64_t> sq_h, sq_u, sq_hmid, sq_a, sq_o;
     int64_t sq_logits = 0;
     Workspace ws;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     int64_t n_nodes = 0;
+    // token mixers
+    bool mixers = false;
+    std::vector<q4k_mixer> mix;
+    int64_t cap = 0;                  // KV-cache positions
+    float *states = nullptr;          // every layer's conv state, S or K/V caches
+    size_t state_floats = 0;
+    std::vector<int64_t> st_a, st_b;  // per layer: conv state / K cache, S / V cache
+    float *mix_scratch = nullptr;     // GDN conv outputs and gates
+    int64_t *pos_dev = nullptr;       // device-side position
+    int64_t host_pos = 0;             // tokens launched since creation or reset
 };
 
 namespace {
+
+constexpr int MD = 128;   // GDN head dimension
+constexpr int AHD = 256;  // attention head dimension
 
 int check_mat(const q4k_mat &m, const char *name, int layer) {
     if (!m.w) return fail(Q4K_EINVAL, "layer %d %s: NULL weights", layer, name);
     if (((uintptr_t)m.w & 15u) != 0)
         return fail(Q4K_EALIGN, "layer %d %s: weights not 16-byte aligned", layer, name);
-    if (m.M <= 0 || m.K <= 0 || m.K % 256 != 0 || m.M > 0x7FFFFFFF || m.K > 0x7FFFFFFF)
+    if (m.M <= 0 || m.K <= 0 || m.K % 256 != 0 || m.M > ((int64_t)1 << 30) ||
+        m.K > ((int64_t)1 << 24))
         return fail(Q4K_ESHAPE, "layer %d %s: bad shape %lld x %lld", layer, name,
                     (long long)m.M, (long long)m.K);
+    return Q4K_OK;
+}
+
+bool al16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+int check_mixer(const q4k_layer &L, const q4k_mixer &m, int l) {
+    if (L.kind == 0) {
+        const q4k_gdn_params &g = m.gdn;
+        if (g.key_heads <= 0 || g.value_heads <= 0 || g.value_heads % g.key_heads != 0 ||
+            g.key_dim != MD || g.value_dim != MD || g.key_heads > 4096 || g.value_heads > 4096)
+            return fail(Q4K_ESHAPE, "layer %d: GDN heads must be 128-dim, value heads a multiple "
+                        "of key heads", l);
+        if (!(g.eps >= 0.f)) return fail(Q4K_EINVAL, "layer %d: GDN eps", l);
+        if (!al16(g.conv_w) || !al16(g.a_log) || !al16(g.dt_bias) || !al16(g.norm_w))
+            return fail(Q4K_EINVAL, "layer %d: GDN parameter NULL or not 16-byte aligned", l);
+        const int64_t Min = (int64_t)(2 * g.key_heads + 2 * g.value_heads) * MD + 2 * g.value_heads;
+        if (L.mix_in.M != Min || L.mix_out.K != (int64_t)g.value_heads * MD)
+            return fail(Q4K_ESHAPE, "layer %d: GDN needs mix_in.M %lld and mix_out.K %lld", l,
+                        (long long)Min, (long long)g.value_heads * MD);
+    } else if (L.kind == 1) {
+        const q4k_attn_params &a = m.attn;
+        if (a.head_dim != AHD || a.q_heads <= 0 || a.kv_heads <= 0 ||
+            a.q_heads % a.kv_heads != 0 || a.rope_dim < 0 || a.rope_dim > AHD ||
+            a.rope_dim % 2 != 0 || a.q_heads > 65536)
+            return fail(Q4K_ESHAPE, "layer %d: attention heads must be 256-dim, q heads a "
+                        "multiple of kv heads, rope_dim even", l);
+        if (!(a.eps >= 0.f) || !(a.rope_theta > 0.f))
+            return fail(Q4K_EINVAL, "layer %d: attention eps / theta", l);
+        if (!al16(a.q_norm_w) || !al16(a.k_norm_w))
+            return fail(Q4K_EINVAL, "layer %d: attention norm weights NULL or not aligned", l);
+        const int64_t Min = (int64_t)(2 * a.q_heads + 2 * a.kv_heads) * AHD;
+        if (L.mix_in.M != Min || L.mix_out.K != (int64_t)a.q_heads * AHD)
+            return fail(Q4K_ESHAPE, "layer %d: attention needs mix_in.M %lld and mix_out.K %lld",
+                        l, (long long)Min, (long long)a.q_heads * AHD);
+    } else {
+        return fail(Q4K_EINVAL, "layer %d: kind must be 0 or 1 with mixers", l);
+    }
     return Q4K_OK;
 }
 
@@ -73,6 +132,13 @@ GemvParams base_params(const q4k_mat &m) {
     p.x_stride = m.K;
     p.y_stride = m.M;
     return p;
+}
+
+__global__ void advance_position_kernel(int64_t *pos) { *pos += 1; }
+
+__global__ __launch_bounds__(256) void zero_kernel(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
 }
 
 // Enqueue the whole token on `cs` (under capture).
@@ -103,11 +169,37 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
         p.in_len = (int32_t)s->hidden;
         p.out_sq = SQ + s->sq_u[l];
         if ((rc = run(p, 1, EPI_SCALE, L.mix_in.M, L.mix_in.K))) return rc;
-        // mixer-out: h_mid = h + W_out rmsn(u[:K_out])
+        // mixer-out: h_mid = h + W_out rmsn(m), m = the mixer output (or u[:K_out])
+        const float *mo = A + s->off_u[l];
+        const float *mo_sq = SQ + s->sq_u[l];
+        if (s->mixers) {
+            const q4k_mixer &m = s->mix[l];
+            float *o = A + s->off_o[l];
+            if (L.kind == 0) {
+                const GdnShape sh{m.gdn.key_heads, m.gdn.value_heads, m.gdn.eps};
+                if ((rc = launch_gdn_step(sh, A + s->off_u[l], m.gdn.conv_w, m.gdn.a_log,
+                                          m.gdn.dt_bias, m.gdn.norm_w, s->states + s->st_a[l],
+                                          s->states + s->st_b[l], o, s->mix_scratch, cs)))
+                    return rc;
+                n += 2;
+            } else {
+                const AttnShape sh{m.attn.q_heads, m.attn.kv_heads, m.attn.rope_dim,
+                                   m.attn.rope_theta, m.attn.eps};
+                if ((rc = launch_attn_step(sh, A + s->off_u[l], m.attn.q_norm_w, m.attn.k_norm_w,
+                                           s->states + s->st_a[l], s->states + s->st_b[l], s->cap,
+                                           0, s->pos_dev, o, cs)))
+                    return rc;
+                ++n;
+            }
+            if ((rc = launch_sumsq(o, L.mix_out.K, SQ + s->sq_o[l], cs))) return rc;
+            ++n;
+            mo = o;
+            mo_sq = SQ + s->sq_o[l];
+        }
         p = base_params(L.mix_out);
-        p.x = A + s->off_u[l];
+        p.x = mo;
         p.y = A + s->off_hmid[l];
-        p.in_sq = SQ + s->sq_u[l];
+        p.in_sq = mo_sq;
         p.in_sq_n = (int32_t)tiles_of(L.mix_out.K);
         p.in_len = (int32_t)L.mix_out.K;
         p.resid = A + s->off_h[l];
@@ -144,6 +236,11 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
     p.in_len = (int32_t)s->hidden;
     p.out_sq = SQ + s->sq_logits;
     if ((rc = run(p, 1, EPI_SCALE, s->lm_head.M, s->lm_head.K))) return rc;
+    if (s->mixers) {
+        hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, cs, s->pos_dev);
+        Q4K_HIP(hipGetLastError());
+        ++n;
+    }
     *nodes = n;
     return Q4K_OK;
 }
@@ -156,8 +253,26 @@ void release(q4k_stack *s) {
     if (s->graph) (void)hipGraphDestroy(s->graph);
     if (s->arena) (void)hipFree(s->arena);
     if (s->sq) (void)hipFree(s->sq);
+    if (s->states) (void)hipFree(s->states);
+    if (s->mix_scratch) (void)hipFree(s->mix_scratch);
+    if (s->pos_dev) (void)hipFree(s->pos_dev);
     free_workspace(&s->ws);
     delete s;
+}
+
+int zero_states(q4k_stack *s, hipStream_t st) {
+    if (!s->mixers) return Q4K_OK;
+    if (s->state_floats) {
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((s->state_floats + 255) / 256)), dim3(256),
+                           0, st, s->states, (int64_t)s->state_floats);
+        Q4K_HIP(hipGetLastError());
+    }
+    // the position too, by a kernel (a plan may be reset inside a captured graph)
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float *>(s->pos_dev),
+                       (int64_t)(sizeof(int64_t) / sizeof(float)));
+    Q4K_HIP(hipGetLastError());
+    s->host_pos = 0;
+    return Q4K_OK;
 }
 
 }  // namespace
@@ -168,13 +283,17 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     clear_error();
     if (!d || !out) return fail(Q4K_EINVAL, "NULL descriptor or output");
     *out = nullptr;
-    if (d->flags != 0) return fail(Q4K_EINVAL, "flags must be 0");
+    if (d->flags != 0 && d->flags != Q4K_STACK_MIXERS)
+        return fail(Q4K_EINVAL, "flags must be 0 or Q4K_STACK_MIXERS");
+    const bool mixers = d->flags == Q4K_STACK_MIXERS;
     if (d->n_layers < 0 || d->hidden <= 0 || d->hidden % 256 != 0)
         return fail(Q4K_ESHAPE, "need n_layers >= 0 and hidden a positive multiple of 256");
     if (d->n_layers > 0 && !d->layers) return fail(Q4K_EINVAL, "NULL layers");
     if (!(d->eps >= 0.0f)) return fail(Q4K_EINVAL, "eps must be >= 0");
+    if (mixers && d->n_layers > 0 && !d->mixers) return fail(Q4K_EINVAL, "NULL mixers");
     const int64_t H = d->hidden;
     int rc;
+    bool any_attn = false;
     for (int32_t l = 0; l < d->n_layers; ++l) {
         const q4k_layer &L = d->layers[l];
         if ((rc = check_mat(L.mix_in, "mix_in", l)) || (rc = check_mat(L.mix_out, "mix_out", l)) ||
@@ -189,7 +308,13 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
             return fail(Q4K_ESHAPE, "layer %d: mix_out K exceeds mix_in M", l);
         if (L.gate.M != L.up.M || L.down.K != L.gate.M)
             return fail(Q4K_ESHAPE, "layer %d: gate/up M must equal down K", l);
+        if (mixers) {
+            if ((rc = check_mixer(L, d->mixers[l], l))) return rc;
+            any_attn |= L.kind == 1;
+        }
     }
+    if (mixers && any_attn && (d->attn_capacity <= 0 || d->attn_capacity > ((int64_t)1 << 24)))
+        return fail(Q4K_ESHAPE, "attn_capacity must be in 1..2^24");
     if ((rc = check_mat(d->lm_head, "lm_head", -1))) return rc;
     if (d->lm_head.K != H) return fail(Q4K_ESHAPE, "lm_head K must equal hidden");
 
@@ -212,9 +337,14 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     s->eps = d->eps;
     s->layers.assign(d->layers, d->layers + d->n_layers);
     s->lm_head = d->lm_head;
+    s->mixers = mixers;
+    if (mixers) {
+        s->mix.assign(d->mixers, d->mixers + d->n_layers);
+        s->cap = d->attn_capacity;
+    }
 
     // arena layout
-    size_t off = 0, sqo = 0;
+    size_t off = 0, sqo = 0, sto = 0, scratch = 0;
     auto take = [](size_t &o, int64_t n) {
         const int64_t r = (int64_t)o;
         o += (size_t)((n + 63) / 64 * 64);  // keep every buffer 256-byte aligned
@@ -236,9 +366,25 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         s->off_g.push_back(take(off, L.gate.M));
         s->off_v.push_back(take(off, L.gate.M));
         s->off_a.push_back(take(off, L.gate.M));
+        s->off_o.push_back(mixers ? take(off, L.mix_out.K) : -1);
         s->sq_u.push_back(take(sqo, tiles_of(L.mix_in.M)));
         s->sq_hmid.push_back(take(sqo, tiles_of(H)));
         s->sq_a.push_back(take(sqo, tiles_of(L.gate.M)));
+        s->sq_o.push_back(mixers ? take(sqo, tiles_of(L.mix_out.K)) : -1);
+        if (mixers && L.kind == 0) {
+            const q4k_gdn_params &g = s->mix[l].gdn;
+            const int64_t C = (int64_t)(2 * g.key_heads + g.value_heads) * MD;
+            s->st_a.push_back(take(sto, 3 * C));
+            s->st_b.push_back(take(sto, (int64_t)g.value_heads * MD * MD));
+            scratch = std::max(scratch, (size_t)(C + 2 * g.value_heads));
+        } else if (mixers) {
+            const int64_t n = (int64_t)s->mix[l].attn.kv_heads * s->cap * AHD;
+            s->st_a.push_back(take(sto, n));
+            s->st_b.push_back(take(sto, n));
+        } else {
+            s->st_a.push_back(-1);
+            s->st_b.push_back(-1);
+        }
         need(L.mix_in.M, L.mix_in.K, 1, EPI_SCALE);
         need(L.mix_out.M, L.mix_out.K, 1, EPI_RESID);
         need(L.gate.M, L.gate.K, 2, EPI_SWIGLU);
@@ -249,9 +395,17 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     need(s->lm_head.M, s->lm_head.K, 1, EPI_SCALE);
     s->arena_floats = off;
     s->sq_floats = sqo;
+    s->state_floats = sto;
 
-    if (hipMalloc(&s->arena, off * sizeof(float)) != hipSuccess ||
-        hipMalloc(&s->sq, sqo * sizeof(float)) != hipSuccess) {
+    bool ok = hipMalloc(&s->arena, off * sizeof(float)) == hipSuccess &&
+              hipMalloc(&s->sq, sqo * sizeof(float)) == hipSuccess;
+    if (ok && mixers) {
+        ok = (sto == 0 || hipMalloc(&s->states, sto * sizeof(float)) == hipSuccess) &&
+             hipMalloc(&s->mix_scratch, std::max<size_t>(scratch, 64) * sizeof(float)) ==
+                 hipSuccess &&
+             hipMalloc(&s->pos_dev, sizeof(int64_t)) == hipSuccess;
+    }
+    if (!ok) {
         (void)hipGetLastError();
         release(s);
         return fail(Q4K_ENOMEM, "decode stack: arena allocation failed");
@@ -262,6 +416,8 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     }
     if (hipMemset(s->arena, 0, off * sizeof(float)) != hipSuccess ||
         hipMemset(s->sq, 0, sqo * sizeof(float)) != hipSuccess ||
+        (s->states && hipMemset(s->states, 0, sto * sizeof(float)) != hipSuccess) ||
+        (s->pos_dev && hipMemset(s->pos_dev, 0, sizeof(int64_t)) != hipSuccess) ||
         hipDeviceSynchronize() != hipSuccess) {
         release(s);
         return fail(Q4K_EHIP, "decode stack: arena clear failed");
@@ -309,6 +465,9 @@ int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *strea
     if (!s || !h_in) return fail(Q4K_EINVAL, "NULL plan or input");
     if (((uintptr_t)h_in & 15u) || ((uintptr_t)logits & 15u))
         return fail(Q4K_EALIGN, "h_in/logits not 16-byte aligned");
+    if (s->mixers && s->cap > 0 && s->host_pos >= s->cap)
+        return fail(Q4K_EINVAL, "attention cache full (%lld positions): q4k_decode_stack_reset",
+                    (long long)s->cap);
     hipStream_t st = (hipStream_t)stream;
     Q4K_HIP(hipMemcpyAsync(s->arena + s->off_h[0], h_in, (size_t)s->hidden * sizeof(float),
                            hipMemcpyDeviceToDevice, st));
@@ -316,6 +475,20 @@ int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *strea
     if (logits)
         Q4K_HIP(hipMemcpyAsync(logits, s->arena + s->off_logits,
                                (size_t)s->lm_head.M * sizeof(float), hipMemcpyDeviceToDevice, st));
+    ++s->host_pos;
+    return Q4K_OK;
+}
+
+int q4k_decode_stack_reset(q4k_stack *s, void *stream) {
+    clear_error();
+    if (!s) return fail(Q4K_EINVAL, "NULL plan");
+    return zero_states(s, (hipStream_t)stream);
+}
+
+int q4k_decode_stack_position(q4k_stack *s, int64_t *pos) {
+    clear_error();
+    if (!s || !pos) return fail(Q4K_EINVAL, "NULL argument");
+    *pos = s->host_pos;
     return Q4K_OK;
 }
 
@@ -330,6 +503,8 @@ int q4k_decode_stack_buffer(q4k_stack *s, int32_t layer, int32_t which, const fl
     }
     const int32_t max_layer = which == Q4K_BUF_H ? s->n_layers : s->n_layers - 1;
     if (layer < 0 || layer > max_layer) return fail(Q4K_EINVAL, "layer %d out of range", layer);
+    if (which >= Q4K_BUF_MIX && !s->mixers) return fail(Q4K_EINVAL, "plan has no mixers");
+    const int kind = which >= Q4K_BUF_MIX ? s->layers[layer].kind : -1;
     switch (which) {
         case Q4K_BUF_H: *ptr = s->arena + s->off_h[layer]; *n = s->hidden; break;
         case Q4K_BUF_U: *ptr = s->arena + s->off_u[layer]; *n = s->layers[layer].mix_in.M; break;
@@ -337,6 +512,30 @@ int q4k_decode_stack_buffer(q4k_stack *s, int32_t layer, int32_t which, const fl
         case Q4K_BUF_G: *ptr = s->arena + s->off_g[layer]; *n = s->layers[layer].gate.M; break;
         case Q4K_BUF_V: *ptr = s->arena + s->off_v[layer]; *n = s->layers[layer].gate.M; break;
         case Q4K_BUF_A: *ptr = s->arena + s->off_a[layer]; *n = s->layers[layer].gate.M; break;
+        case Q4K_BUF_MIX:
+            *ptr = s->arena + s->off_o[layer];
+            *n = s->layers[layer].mix_out.K;
+            break;
+        case Q4K_BUF_CONV_STATE:
+        case Q4K_BUF_GDN_STATE: {
+            if (kind != 0) return fail(Q4K_EINVAL, "layer %d is not a GDN layer", layer);
+            const q4k_gdn_params &g = s->mix[layer].gdn;
+            const int64_t C = (int64_t)(2 * g.key_heads + g.value_heads) * MD;
+            if (which == Q4K_BUF_CONV_STATE) {
+                *ptr = s->states + s->st_a[layer];
+                *n = 3 * C;
+            } else {
+                *ptr = s->states + s->st_b[layer];
+                *n = (int64_t)g.value_heads * MD * MD;
+            }
+            break;
+        }
+        case Q4K_BUF_K_CACHE:
+        case Q4K_BUF_V_CACHE:
+            if (kind != 1) return fail(Q4K_EINVAL, "layer %d is not an attention layer", layer);
+            *ptr = s->states + (which == Q4K_BUF_K_CACHE ? s->st_a[layer] : s->st_b[layer]);
+            *n = (int64_t)s->mix[layer].attn.kv_heads * s->cap * AHD;
+            break;
         default: return fail(Q4K_EINVAL, "unknown buffer %d", which);
     }
     return Q4K_OK;

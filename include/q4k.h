@@ -330,6 +330,14 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
  * and finally logits = W_lm rmsn(h).  The stand-in mixer (first mix_out.K
  * outputs of the mixer-in projection) replaces the Gated-DeltaNet recurrence
  * and attention body, which are not matmuls.
+ *
+ * With Q4K_STACK_MIXERS in flags the stand-in gives way to each layer's real
+ * token mixer: o = q4k_gdn_step(u) (kind 0) or q4k_attn_step(u, pos) (kind
+ * 1), and h_mid = h + W_out rmsn(o).  The plan then owns every layer's
+ * recurrent state (GDN conv state and S) or KV cache (attn_capacity
+ * positions), all zero at creation and after q4k_decode_stack_reset; the
+ * position lives on the device and the graph advances it by one per token,
+ * so a token is still one graph launch.
  * ---------------------------------------------------------------------- */
 
 typedef struct {
@@ -343,12 +351,22 @@ typedef struct {
 } q4k_layer;
 
 typedef struct {
+    q4k_gdn_params gdn;   /* kind 0 layers */
+    q4k_attn_params attn; /* kind 1 layers */
+} q4k_mixer;
+
+#define Q4K_STACK_MIXERS 1
+
+typedef struct {
     int64_t hidden;          /* residual width (K of mix_in/gate/up/lm_head, M of mix_out/down) */
     int32_t n_layers;        /* >= 0 */
     const q4k_layer *layers; /* n_layers entries, copied at create time */
     q4k_mat lm_head;
     float eps;               /* RMS epsilon, e.g. 1e-6 */
-    int32_t flags;           /* reserved, must be 0 */
+    int32_t flags;           /* 0 (stand-in mixer) or Q4K_STACK_MIXERS */
+    const q4k_mixer *mixers; /* Q4K_STACK_MIXERS: n_layers entries, copied (their weight
+                                pointers are borrowed); otherwise ignored */
+    int64_t attn_capacity;   /* Q4K_STACK_MIXERS: KV-cache positions of each attention layer */
 } q4k_stack_desc;
 
 typedef struct q4k_stack q4k_stack; /* opaque plan: owns its graph and activation arena */
@@ -356,15 +374,27 @@ typedef struct q4k_stack q4k_stack; /* opaque plan: owns its graph and activatio
 /* Validate the chain, allocate the arena, capture and instantiate the graph.
  * Synchronises `stream`.  Requirements: every K is a multiple of 256;
  * mix_in.K = gate.K = up.K = lm_head.K = hidden; mix_out.M = down.M = hidden;
- * mix_out.K <= mix_in.M; gate.M = up.M = down.K. */
+ * mix_out.K <= mix_in.M; gate.M = up.M = down.K.  With Q4K_STACK_MIXERS, in
+ * addition: a kind-0 layer's mix_in.M is (2*Hk + 2*Hv)*128 + 2*Hv and its
+ * mix_out.K is Hv*128 (q4k_gdn_step's sizes); a kind-1 layer's mix_in.M is
+ * (2*Hq + 2*Hkv)*256 and its mix_out.K is Hq*256 (q4k_attn_step's); the
+ * mixer parameters as those calls require; attn_capacity >= 1. */
 int q4k_decode_stack_create(const q4k_stack_desc *desc, void *stream, q4k_stack **out);
 
 /* One token: copy h_in (f32 [hidden], device) into the arena, launch the
  * graph, copy the logits (f32 [lm_head.M], device) out.  logits may be NULL
  * to leave them in the arena only.  Enqueue-only; h_in/logits must stay valid
  * until the stream reaches this point.  A plan must not run on two streams
- * at once. */
+ * at once.  With mixers, Q4K_EINVAL once attn_capacity tokens have run
+ * since creation or the last reset (nothing is enqueued then). */
 int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *stream);
+
+/* Mixer states back to zero and the position to 0 (enqueued on `stream`);
+ * a no-op without mixers. */
+int q4k_decode_stack_reset(q4k_stack *s, void *stream);
+
+/* Tokens launched since creation or the last reset. */
+int q4k_decode_stack_position(q4k_stack *s, int64_t *pos);
 
 /* Arena buffers of the last token, for per-stage checks.  `which`:
  *   Q4K_BUF_H     residual stream entering layer `layer` (layer = n_layers:
@@ -375,10 +405,17 @@ int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *strea
  *   Q4K_BUF_V     up output v of `layer`                        [gate.M]
  *   Q4K_BUF_A     silu(g) * v of `layer`                        [gate.M]
  *   Q4K_BUF_LOGITS logits (layer ignored)                       [lm_head.M]
+ * and with mixers:
+ *   Q4K_BUF_MIX   mixer output o of `layer`                     [mix_out.K]
+ *   Q4K_BUF_CONV_STATE, Q4K_BUF_GDN_STATE  a kind-0 layer's conv state
+ *                 [C][3] and recurrent state [Hv][128][128] (current values)
+ *   Q4K_BUF_K_CACHE, Q4K_BUF_V_CACHE  a kind-1 layer's caches
+ *                 [Hkv][attn_capacity][256]
  * Sets *ptr to the device address and *n to the element count. */
 enum {
     Q4K_BUF_H = 0, Q4K_BUF_U = 1, Q4K_BUF_HMID = 2, Q4K_BUF_G = 3,
-    Q4K_BUF_V = 4, Q4K_BUF_A = 5, Q4K_BUF_LOGITS = 6
+    Q4K_BUF_V = 4, Q4K_BUF_A = 5, Q4K_BUF_LOGITS = 6, Q4K_BUF_MIX = 7,
+    Q4K_BUF_CONV_STATE = 8, Q4K_BUF_GDN_STATE = 9, Q4K_BUF_K_CACHE = 10, Q4K_BUF_V_CACHE = 11
 };
 int q4k_decode_stack_buffer(q4k_stack *s, int32_t layer, int32_t which,
                             const float **ptr, int64_t *n);

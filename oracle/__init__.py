@@ -352,3 +352,43 @@ def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos, Hq=24, Hkv=4, D=256,
                                     qw.ctypes.data, kw.ctypes.data, kc.ctypes.data,
                                     vc.ctypes.data, cap, int(pos), out.ctypes.data))
     return out, kc, vc
+
+
+def _rmsn(v, eps):
+    v = np.asarray(v, np.float64)
+    return v / np.sqrt(np.mean(v * v) + eps)
+
+
+def stack_mixers_token(mats, shapes, kinds, mixers, states, hidden, h0, pos, eps=RMS_EPS):
+    """One token of the decode chain with the real token mixers, in double:
+    per layer u = W_in rmsn(h); o = gdn_step(u) or attn_step(u, pos);
+    h_mid = h + W_out rmsn(o); a = silu(W_gate rmsn(h_mid)) * (W_up rmsn(h_mid));
+    h = h_mid + W_down rmsn(a); then logits = W_lm rmsn(h).  A composition of
+    the oracle's gemv, gdn_step and attn_step.  `states[l]` is (conv_state, S)
+    for kind 0 or (k_cache, v_cache) for kind 1; returns (logits, new states)."""
+    h = np.asarray(h0, np.float64)
+    new_states = []
+    for l, kind in enumerate(kinds):
+        W = mats[5 * l:5 * l + 5]
+        S = shapes[5 * l:5 * l + 5]
+        u, _ = gemv(W[0], _rmsn(h, eps), *S[0])
+        m = mixers[l]
+        if kind == 0:
+            o, cs, St = gdn_step(u, m["conv_w"], m["a_log"], m["dt_bias"], m["norm_w"],
+                                 states[l][0], states[l][1], Hk=m["key_heads"],
+                                 Hv=m["value_heads"], eps=m.get("eps", eps))
+            new_states.append((cs, St))
+        else:
+            o, kc, vc = attn_step(u, m["q_norm_w"], m["k_norm_w"], states[l][0], states[l][1],
+                                  pos, Hq=m["q_heads"], Hkv=m["kv_heads"], R=m["rope_dim"],
+                                  theta=m["rope_theta"], eps=m.get("eps", eps))
+            new_states.append((kc, vc))
+        y, _ = gemv(W[1], _rmsn(o, eps), *S[1])
+        hm = h + y
+        g, _ = gemv(W[2], _rmsn(hm, eps), *S[2])
+        v, _ = gemv(W[3], _rmsn(hm, eps), *S[3])
+        a = g / (1.0 + np.exp(-g)) * v
+        y, _ = gemv(W[4], _rmsn(a, eps), *S[4])
+        h = hm + y
+    logits, _ = gemv(mats[-1], _rmsn(h, eps), *shapes[-1])
+    return logits, new_states

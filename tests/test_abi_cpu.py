@@ -341,3 +341,48 @@ def test_attn_step_validation(lib):
         assert call(**kw) == code, kw
         assert lib.q4k_last_error()
     assert call() not in (-1, -2, -3)
+
+
+def test_stack_create_validation_with_mixers(lib):
+    """With Q4K_STACK_MIXERS the plan checks each layer's mixer sizes against
+    its projections and the KV-cache capacity before touching a device."""
+    out = ctypes.c_void_p()
+    mk = lambda M, K: q4k.MatDesc(P, M, K)
+    L = (q4k.LayerDesc * 2)()
+    gdn_in = (2 * 2 + 2 * 4) * 128 + 8           # Hk = 2, Hv = 4
+    att_in = (2 * 2 + 2 * 1) * 256               # Hq = 2, Hkv = 1
+
+    def layers():
+        L[0].kind, L[1].kind = 0, 1
+        L[0].mix_in, L[0].mix_out = mk(gdn_in, 512), mk(512, 512)
+        L[1].mix_in, L[1].mix_out = mk(att_in, 512), mk(512, 512)
+        for l in (0, 1):
+            L[l].gate, L[l].up, L[l].down = mk(1024, 512), mk(1024, 512), mk(512, 1024)
+
+    mx = (q4k.MixerDesc * 2)()
+
+    def mixers():
+        mx[0].gdn = q4k.GdnParams(2, 4, 128, 128, 1e-6, P, P, P, P)
+        mx[1].attn = q4k.AttnParams(2, 1, 256, 64, 1e7, 1e-6, P, P)
+
+    bad = [
+        ("flags", lambda d: setattr(d, "flags", 3), -1),
+        ("mixers null", lambda d: setattr(d, "mixers", None), -1),
+        ("gdn in", lambda d: setattr(L[0], "mix_in", mk(gdn_in + 1, 512)), -2),
+        ("attn out", lambda d: setattr(L[1], "mix_out", mk(512, 768)), -2),
+        ("gdn heads", lambda d: setattr(mx[0], "gdn", q4k.GdnParams(3, 4, 128, 128, 1e-6, P, P, P, P)), -2),
+        ("attn dim", lambda d: setattr(mx[1], "attn", q4k.AttnParams(2, 1, 128, 64, 1e7, 1e-6, P, P)), -2),
+        ("gdn ptr", lambda d: setattr(mx[0], "gdn", q4k.GdnParams(2, 4, 128, 128, 1e-6, None, P, P, P)), -1),
+        ("capacity", lambda d: setattr(d, "attn_capacity", 0), -2),
+        ("kind", lambda d: setattr(L[1], "kind", 2), -1),
+    ]
+    for name, mut, code in bad:
+        layers()
+        mixers()
+        d = q4k.StackDesc(512, 2, L, mk(300, 512), 1e-6, q4k.STACK_MIXERS, mx, 16)
+        mut(d)
+        assert lib.q4k_decode_stack_create(ctypes.byref(d), None, ctypes.byref(out)) == code, name
+        assert not out.value
+    n = ctypes.c_int64()
+    assert lib.q4k_decode_stack_reset(None, None) == -1
+    assert lib.q4k_decode_stack_position(None, ctypes.byref(n)) == -1

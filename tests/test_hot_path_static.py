@@ -21,7 +21,8 @@ import bit_block_quantized_gguf_amd as q4k
 HOT = ("q4k_dequant", "q4k_gemv", "q4k_gemv_batch", "q4k_gemm", "q4k_gemv_q8_0",
        "q4k_gemv_q6_k", "q4k_mlp", "q4k_workspace_size", "q4k_decode_stack",
        "q4k_decode_stack_buffer", "q4k_decode_stack_nodes", "q4k_gemv_noalloc",
-       "q4k_gdn_step", "q4k_attn_step")
+       "q4k_gdn_step", "q4k_attn_step", "q4k_decode_stack_reset",
+       "q4k_decode_stack_position")
 FORBIDDEN = re.compile(r"^(hipMalloc\w*|hipExtMalloc\w*|hipHostMalloc|hipMallocManaged|hipFree\w*|"
                        r"hipHostFree|hipMemset|hipMemsetD\w*|hipDeviceSynchronize|"
                        r"hipStreamSynchronize|hipEventSynchronize|hipMemcpy|hipGraphInstantiate\w*|"
