@@ -480,7 +480,32 @@ def main():
                                "weight_bytes": tot, "roofline_us": roof, "frac_roofline": roof / med,
                                "GBps": tot / med / 1e3, "graph_nodes": stk.nodes()}
         log("stack: %.1f us/token (roofline %.1f)" % (med, roof))
+        ref_logits = logits.clone()
         stk.close()
+        # the same chain as one cooperative kernel per token
+        log("persistent decode plan")
+        pst = q4k.DecodeStack(layers, lm, hidden=wl.HIDDEN, persistent=True)
+        for _ in range(3):
+            pst(h0, logits)
+        settle(lambda i: pst(h0, logits))
+        pairs = []
+        for _ in range(args.stack_tokens):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            pst(h0, logits)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        pmed = float(np.median(ts))
+        same = bool(torch.equal(logits, ref_logits))
+        out["decode_stack_persistent"] = {
+            "us_per_token_median": pmed, "us_per_token_mean": float(np.mean(ts)),
+            "tokens": args.stack_tokens, "roofline_us": roof, "frac_roofline": roof / pmed,
+            "GBps": tot / pmed / 1e3, "kernels_per_token": 1, "logits_equal_graph": same,
+            "wait_timeouts": pst.status()}
+        log("persistent stack: %.1f us/token, logits equal to the graph plan's: %s" % (pmed, same))
+        pst.close()
         del layers, lm
         torch.cuda.empty_cache()
 

@@ -27,6 +27,7 @@ STATUS = {0: "Q4K_OK", -1: "Q4K_EINVAL", -2: "Q4K_ESHAPE", -3: "Q4K_EALIGN",
 (BUF_H, BUF_U, BUF_HMID, BUF_G, BUF_V, BUF_A, BUF_LOGITS, BUF_MIX, BUF_CONV_STATE, BUF_GDN_STATE,
  BUF_K_CACHE, BUF_V_CACHE) = range(12)
 STACK_MIXERS = 1
+STACK_PERSISTENT = 2
 
 # Every symbol include/q4k.h declares (checked by the CPU test suite).
 EXPORTS = (
@@ -35,7 +36,7 @@ EXPORTS = (
     "q4k_decode_stack_create", "q4k_decode_stack", "q4k_decode_stack_buffer",
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
     "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc", "q4k_gdn_step", "q4k_attn_step",
-    "q4k_decode_stack_reset", "q4k_decode_stack_position",
+    "q4k_decode_stack_reset", "q4k_decode_stack_position", "q4k_decode_stack_status",
 )
 OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP = range(7)
 
@@ -79,7 +80,8 @@ class StackDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int64), ("n_layers", ctypes.c_int32),
                 ("layers", ctypes.POINTER(LayerDesc)), ("lm_head", MatDesc),
                 ("eps", ctypes.c_float), ("flags", ctypes.c_int32),
-                ("mixers", ctypes.POINTER(MixerDesc)), ("attn_capacity", ctypes.c_int64)]
+                ("mixers", ctypes.POINTER(MixerDesc)), ("attn_capacity", ctypes.c_int64),
+                ("spin_limit", ctypes.c_int32)]
 
 
 def load(path: str | None = None):
@@ -125,6 +127,8 @@ def load(path: str | None = None):
     L.q4k_decode_stack_reset.restype = ctypes.c_int
     L.q4k_decode_stack_position.argtypes = [p, ctypes.POINTER(i64)]
     L.q4k_decode_stack_position.restype = ctypes.c_int
+    L.q4k_decode_stack_status.argtypes = [p, p, ctypes.POINTER(i32)]
+    L.q4k_decode_stack_status.restype = ctypes.c_int
     L.q4k_decode_stack_destroy.argtypes = [p]
     L.q4k_decode_stack_destroy.restype = None
     L.q4k_gemv_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -504,7 +508,9 @@ def tune_gemm(tile_tokens: int = 0, workgroups: int = 0) -> None:
 
 
 class DecodeStack:
-    """One hipGraph per plan replaying the per-token projection/MLP chain.
+    """The per-token projection/MLP chain: one hipGraph launch per token, or
+    with ``persistent=True`` one cooperative kernel per token (stand-in mixer
+    only; ``spin_limit`` bounds each wait between nodes, 0 = default).
 
     ``layers``: list of dicts with keys mix_in, mix_out, gate, up, down, each a
     uint8 device tensor [M, K/256*144]; ``lm_head`` likewise.  The tensors are
@@ -518,7 +524,7 @@ class DecodeStack:
     """
 
     def __init__(self, layers, lm_head, hidden: int, eps: float = 1e-6, kinds=None, mixers=None,
-                 attn_capacity: int = 0):
+                 attn_capacity: int = 0, persistent: bool = False, spin_limit: int = 0):
         torch = _torch()
         self._keep = []
         arr = (LayerDesc * max(1, len(layers)))()
@@ -539,9 +545,9 @@ class DecodeStack:
         self.hidden = hidden
         self.vocab = M
         self.n_layers = len(layers)
-        flags, mix_arr = 0, None
+        flags, mix_arr = (STACK_PERSISTENT if persistent else 0), None
         if mixers is not None:
-            flags = STACK_MIXERS
+            flags |= STACK_MIXERS
             mix_arr = (MixerDesc * max(1, len(layers)))()
             f32 = torch.float32
             for i, m in enumerate(mixers):
@@ -562,7 +568,7 @@ class DecodeStack:
                                                  float(m.get("eps", 1e-6)), ptr("q_norm_w"),
                                                  ptr("k_norm_w"))
         desc = StackDesc(hidden, len(layers), arr, MatDesc(lm_head.data_ptr(), M, K),
-                         float(eps), flags, mix_arr, int(attn_capacity))
+                         float(eps), flags, mix_arr, int(attn_capacity), int(spin_limit))
         self._desc_layers = (arr, mix_arr)
         h = ctypes.c_void_p()
         check(load().q4k_decode_stack_create(ctypes.byref(desc), _stream(), ctypes.byref(h)))
@@ -577,6 +583,13 @@ class DecodeStack:
         n = ctypes.c_int64()
         check(load().q4k_decode_stack_position(self._h, ctypes.byref(n)))
         return n.value
+
+    def status(self) -> int:
+        """0 if every wait between nodes ended normally since the last call
+        (persistent plans; synchronises the current stream), else 1."""
+        st = ctypes.c_int32()
+        check(load().q4k_decode_stack_status(self._h, _stream(), ctypes.byref(st)))
+        return st.value
 
     def __call__(self, h_in, logits=None):
         torch = _torch()

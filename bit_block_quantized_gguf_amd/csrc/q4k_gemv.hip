@@ -44,6 +44,8 @@
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
+#include <string.h>
+
 #include <algorithm>
 #include <atomic>
 #include <map>
@@ -269,6 +271,17 @@ __device__ __forceinline__ void block_dot(const uint4 (&b)[9], const float *xblk
 // Up to 1024 granules (K <= 32768) every lane issues its loads before adding
 // them (in the same order as the plain loop), so the latency is paid once.
 __device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
+    if (p.in_sq == nullptr && p.in_len > 0) {
+        // no per-32 sums of squares: add x's squares directly (lane-strided
+        // float4s, then the butterfly)
+        float ss = 0.f;
+        for (int i = 4 * lane; i < p.in_len; i += 256) {
+            const float4 v = *reinterpret_cast<const float4 *>(p.x + i);
+            ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+        }
+        ss = wave_sum(ss);
+        return 1.0f / sqrtf(ss / (float)p.in_len + p.eps);
+    }
     if (p.in_sq == nullptr) return 1.f;  // input taken as it is (no normalisation)
     float ss = 0.f;
     if (p.in_sq_n <= 16 * 64) {
@@ -287,17 +300,25 @@ __device__ __forceinline__ float inv_rms(const GemvParams &p, int lane) {
     return 1.0f / sqrtf(ss / (float)p.in_len + p.eps);
 }
 
+// Output store: plain, or device-coherent (sc1: written through past the
+// per-XCD L2) for outputs that other workgroups of the same kernel read.
+template <bool COH>
+__device__ __forceinline__ void st_out(float *ptr, float v) {
+    if constexpr (COH) __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *ptr = v;
+}
+
 // Epilogue for one wave holding the final sums of a tile's 64 lane rows.
 // NMAT == 1: lane = output row (row0 + lane).  NMAT == 2: lanes 0..31 hold the
 // gate rows row0 + lane, lanes 32..63 the up rows of the same indices.
-template <int NV, int NMAT, int EPI>
+template <int NV, int NMAT, int EPI, bool COH = false>
 __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane,
                                          const float (&tot)[NV], float inv) {
     if constexpr (EPI == EPI_PLAIN) {
         const int row = row0 + lane;
         if (row < p.M) {
 #pragma unroll
-            for (int n = 0; n < NV; ++n) p.y[(int64_t)n * p.y_stride + row] = tot[n];
+            for (int n = 0; n < NV; ++n) st_out<COH>(&p.y[(int64_t)n * p.y_stride + row], tot[n]);
         }
     } else {
         float val;
@@ -311,8 +332,8 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
             const float g = mine, v = other;
             val = g / (1.0f + expf(-g)) * v;
             if (ok && p.y_g) {
-                p.y_g[row] = g;
-                p.y_v[row] = v;
+                st_out<COH>(&p.y_g[row], g);
+                st_out<COH>(&p.y_v[row], v);
             }
         } else {
             row = row0 + lane;
@@ -321,7 +342,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
             if constexpr (EPI == EPI_SCALE) val = tot[0] * inv;
             else val = fmaf(tot[0], inv, p.resid[rowc]);
         }
-        if (ok) p.y[row] = val;
+        if (ok) st_out<COH>(&p.y[row], val);
         if (!p.out_sq) return;
         // sums of squares per 32 output rows (lanes 0..31 and 32..63)
         float sq = ok ? val * val : 0.f;
@@ -332,7 +353,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
         sq += __shfl_xor(sq, 1);
         if ((lane & 31) == 0) {
             const int granule = row0 / 32 + (lane >> 5);
-            if ((NMAT == 1 || lane == 0) && granule * 32 < p.M) p.out_sq[granule] = sq;
+            if ((NMAT == 1 || lane == 0) && granule * 32 < p.M) st_out<COH>(&p.out_sq[granule], sq);
         }
     }
 }
@@ -397,7 +418,7 @@ struct Units {
 // atomics: those add an L2 write-back before the counter update and an L2
 // invalidate after it, which measured about twice the kernel time on the
 // 50 MB matrices (17408x5120: 18.3 -> 35.6 us).
-template <int NV, int NMAT, int EPI>
+template <int NV, int NMAT, int EPI, bool COH = false>
 __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Units &un, int g,
                                                   int t, int slot, int lane,
                                                   const float (&tot)[NV], float inv) {
@@ -446,7 +467,7 @@ __device__ __forceinline__ void finish_split_tile(const GemvParams &p, const Uni
                 for (int n = 0; n < NV; ++n) sum[n] += part[c][n];
             }
     }
-    epilogue<NV, NMAT, EPI>(p, t * ROWS, lane, sum, inv);
+    epilogue<NV, NMAT, EPI, COH>(p, t * ROWS, lane, sum, inv);
 }
 
 template <int NV, int NMAT, int EPI>
@@ -583,6 +604,203 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
         k = kn;
         if (more) commit();
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent decode kernel: the whole per-token chain of GEMV nodes in one
+// launch ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4: one submission per
+// token with the activation resident).  Every workgroup walks the node list;
+// within a node it takes its unit range exactly as gemv_kernel does (same
+// unit loop, same in-kernel finishing of cut tiles).  Between nodes:
+//   * the workgroup loads its first unit of the next node into LDS and issues
+//     the loads of its second unit, then waits until every workgroup has
+//     finished the current node (a counter per node; weights do not depend on
+//     activations, so the memory pipe keeps streaming across the boundary);
+//   * outputs are written with device-coherent (sc1) stores and each
+//     workgroup counts itself in only after its stores have completed, so
+//     the next node's workgroups, on any XCD, read them after the wait.
+//     Every activation buffer is written once per token before any workgroup
+//     reads it, and caches are invalidated at each kernel start, so no stale
+//     copy can be read.
+// The counters grow by the grid size every token (epoch): token e waits for
+// (e + 1) * G arrivals, compared as a signed difference.  Each wait is
+// bounded: past spin_limit polls the workgroup records an error flag and
+// goes on, so every workgroup always reaches the end of the kernel.  The
+// grid must be co-resident (cooperative launch).
+struct StackNode {
+    GemvParams p;
+    Units un;
+    int32_t nmat, epi;
+};
+
+// The node parameters are read from memory, so the compiler cannot tell that
+// their pointers address global memory and would access through them with
+// flat instructions, which also count against the LDS wait counter (a wait
+// for the staged weights would then wait for the next unit's loads too).
+// A round trip through the global address space lets it use global ones.
+template <class T>
+__device__ __forceinline__ T *as_global(T *p) {
+    return (T *)(__attribute__((address_space(1))) T *)(uintptr_t)p;
+}
+
+__device__ __forceinline__ void wait_arrivals(unsigned *c, unsigned target, int spin_limit,
+                                              unsigned *err) {
+    int i = 0;
+    while ((int)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+        if (++i > spin_limit) {
+            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+template <int NMAT, int EPI>
+__device__ __forceinline__ void node_finish(const GemvParams &p, const Units &un, int g, int t,
+                                            int first_tile, bool whole, int lane,
+                                            const float (&tot)[1], float inv) {
+    constexpr int ROWS = 64 / NMAT;
+    if (whole)
+        epilogue<1, NMAT, EPI, true>(p, t * ROWS, lane, tot, inv);
+    else
+        finish_split_tile<1, NMAT, EPI, true>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot, inv);
+}
+
+__global__ __launch_bounds__(64 * WK) void stack_kernel(const StackNode *__restrict__ nodes,
+                                                        int n_nodes, unsigned *done,
+                                                        unsigned epoch, unsigned *err,
+                                                        int spin_limit) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * SEGP];
+    __shared__ float red[WK][1][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x;
+    const unsigned G = gridDim.x;
+    int coff[CH_THREAD], crow[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;
+        crow[i] = q / CH_ROW;
+        coff[i] = 16 * (q - crow[i] * CH_ROW);
+    }
+    uint4 reg[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+
+    for (int n = 0; n < n_nodes; ++n) {
+        GemvParams p = nodes[n].p;
+        p.w0 = as_global(p.w0);
+        p.w1 = as_global(p.w1);
+        p.x = as_global(p.x);
+        p.y = as_global(p.y);
+        p.y_g = as_global(p.y_g);
+        p.y_v = as_global(p.y_v);
+        p.ws = as_global(p.ws);
+        p.cnt = as_global(p.cnt);
+        p.in_sq = as_global(p.in_sq);
+        p.resid = as_global(p.resid);
+        p.out_sq = as_global(p.out_sq);
+        const Units un = nodes[n].un;
+        const int nmat = nodes[n].nmat, epi = nodes[n].epi;
+        const int rows = 64 / nmat;
+        // a node with fewer units than workgroups runs on its first U
+        // workgroups (un.G = min(G, U)), one unit or more each: every
+        // workgroup between a cut tile's first and last contributor then
+        // contributes to it
+        const bool have = g < un.G;
+        const int64_t ua = have ? un.begin(g) : 0, ub = have ? un.begin(g + 1) : 0;
+        const int first_tile =
+            !have ? 0 : un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
+        auto fetch = [&](int t, int k) {
+            const int j0 = k * WK;
+            const int64_t base = (int64_t)t * rows * p.row_bytes + (int64_t)j0 * kBlockBytes;
+            const uint8_t *b0 = p.w0 + base;
+            const uint8_t *b1 = nmat == 2 ? p.w1 + base : b0;
+            const int valid = min(WK, p.nb - j0) * kBlockBytes;
+            const int rmax = min(rows - 1, p.M - 1 - t * rows);
+#pragma unroll
+            for (int i = 0; i < CH_THREAD; ++i) {
+                const int cr = crow[i], co = coff[i] < valid ? coff[i] : 0;
+                const int r = nmat == 2 ? (cr & 31) : cr;
+                const uint32_t off = (uint32_t)min(r, rmax) * (uint32_t)p.row_bytes + (uint32_t)co;
+                const uint8_t *src = (nmat == 2 && cr >= 32) ? b1 : b0;
+                reg[i] = ldg16(src + off);
+            }
+        };
+        auto commit = [&]() {
+#pragma unroll
+            for (int i = 0; i < CH_THREAD; ++i)
+                *reinterpret_cast<uint4 *>(&stage[crow[i] * SEGP + coff[i]]) = reg[i];
+        };
+        int t = first_tile, k = have ? (int)(ua - (int64_t)first_tile * un.upt) : 0;
+        // this node's first unit into LDS and its second in flight, then the
+        // wait for the previous node (the LDS is free: the previous node's
+        // loop ended with a barrier)
+        if (have) {
+            fetch(t, k);
+            commit();
+            if (ua + 1 < ub) {
+                const bool lt = k + 1 == un.upt;
+                fetch(lt ? t + 1 : t, lt ? 0 : k + 1);
+            }
+        }
+        if (n > 0 && tid == 0) wait_arrivals(&done[n - 1], (epoch + 1u) * G, spin_limit, err);
+        __syncthreads();
+        if (have) {
+            const float inv = epi == EPI_PLAIN ? 1.f : inv_rms(p, lane);
+            float acc[1] = {0.f};
+            bool seg_first = k == 0;
+            for (int64_t u = ua; u < ub; ++u) {
+                const int j = k * WK + wave;
+                const bool active = j < p.nb;
+                const bool last_of_tile = k + 1 == un.upt;
+                const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
+                const bool more = u + 1 < ub;
+                if (more && u > ua) fetch(tn, kn);  // unit ua + 1 was fetched before the wait
+                if (active) {
+                    const uint8_t *lp = &stage[lane * SEGP + wave * kBlockBytes];
+                    uint4 b[9];
+#pragma unroll
+                    for (int i = 0; i < 9; ++i) b[i] = *reinterpret_cast<const uint4 *>(lp + 16 * i);
+                    block_dot<1>(b, p.x + 256 * (int64_t)j, p.x_stride, acc);
+                }
+                const bool seg_end = !more || last_of_tile;
+                if (seg_end) {
+                    red[wave][0][lane] = acc[0];
+                    acc[0] = 0.f;
+                }
+                __syncthreads();
+                if (seg_end && wave == 0) {
+                    float tot[1] = {red[0][0][lane]};
+#pragma unroll
+                    for (int w = 1; w < WK; ++w) tot[0] += red[w][0][lane];
+                    const bool whole = seg_first && last_of_tile;
+                    if (epi == EPI_SWIGLU)
+                        node_finish<2, EPI_SWIGLU>(p, un, g, t, first_tile, whole, lane, tot, inv);
+                    else if (epi == EPI_RESID)
+                        node_finish<1, EPI_RESID>(p, un, g, t, first_tile, whole, lane, tot, inv);
+                    else if (epi == EPI_SCALE)
+                        node_finish<1, EPI_SCALE>(p, un, g, t, first_tile, whole, lane, tot, inv);
+                    else
+                        node_finish<1, EPI_PLAIN>(p, un, g, t, first_tile, whole, lane, tot, inv);
+                }
+                if (seg_end) seg_first = true;
+                t = tn;
+                k = kn;
+                if (more) commit();
+                __syncthreads();
+            }
+        }
+        // count this workgroup in once its stores have completed (only wave 0
+        // stores node outputs)
+        if (wave == 0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (lane == 0)
+                __hip_atomic_fetch_add(&done[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -1113,6 +1331,41 @@ int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream)
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL(gemv_q6_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
     Q4K_HIP(hipGetLastError());
+    return Q4K_OK;
+}
+
+int stack_groups(int *G) {
+    int res = 0, cus = 0;
+    int rc = resident_groups((const void *)stack_kernel, &res, &cus);
+    if (rc) return rc;
+    *G = std::max(1, std::min(res, 2 * cus));
+    return Q4K_OK;
+}
+
+size_t stack_node_bytes() { return sizeof(StackNode); }
+
+int fill_stack_node(void *dst, const GemvParams &p, int nmat, int epi, int G) {
+    StackNode nd;
+    nd.p = p;
+    const int rows = 64 / nmat;
+    const int64_t tiles = (p.M + rows - 1) / rows;
+    if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "stack node: too many rows");
+    nd.un.upt = (p.nb + WK - 1) / WK;
+    nd.un.U = tiles * nd.un.upt;
+    nd.un.G = (int)std::min<int64_t>(G, nd.un.U);
+    nd.un.small = (nd.un.U + 1) * (int64_t)nd.un.G + nd.un.U < ((int64_t)1 << 32);
+    nd.nmat = nmat;
+    nd.epi = epi;
+    memcpy(dst, &nd, sizeof nd);
+    return Q4K_OK;
+}
+
+int launch_stack_kernel(const void *nodes, int n_nodes, unsigned *done, unsigned epoch,
+                        unsigned *err, int spin_limit, int G, hipStream_t stream) {
+    void *args[] = {(void *)&nodes, (void *)&n_nodes, (void *)&done, (void *)&epoch,
+                    (void *)&err, (void *)&spin_limit};
+    Q4K_HIP(hipLaunchCooperativeKernel((const void *)stack_kernel, dim3((unsigned)G),
+                                       dim3(64 * WK), args, 0, stream));
     return Q4K_OK;
 }
 

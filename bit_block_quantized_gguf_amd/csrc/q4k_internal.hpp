@@ -112,6 +112,15 @@ int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream)
 int gemv_noalloc(const void *w, const float *x, float *y, int64_t M, int64_t K,
                  hipStream_t stream);
 
+// Persistent decode kernel (q4k_gemv.hip): grid size (co-resident
+// workgroups, at most two per CU), node descriptor size, filling one node
+// descriptor (host memory), and the cooperative launch over n_nodes nodes.
+int stack_groups(int *G);
+size_t stack_node_bytes();
+int fill_stack_node(void *dst, const GemvParams &p, int nmat, int epi, int G);
+int launch_stack_kernel(const void *nodes, int n_nodes, unsigned *done, unsigned epoch,
+                        unsigned *err, int spin_limit, int G, hipStream_t stream);
+
 // Per-32-element sums of squares of v[0..n) (used to seed the stack).
 int launch_sumsq(const float *v, int64_t n, float *out, hipStream_t stream);
 

@@ -8,7 +8,6 @@
 // hipGraphLaunch; the activations never leave the device.
 //
 // Node list per token (4 GEMV kernels per layer, gate and up fused):
-//   sumsq(h0)
 //   for each layer:  u     = W_in rmsn(h)                 (EPI_SCALE)
 //                    h_mid = h + W_out rmsn(u[:K_out])    (EPI_RESID)
 //                    g, v, a = silu(g) * v                (EPI_SWIGLU, gate|up in one pass)
@@ -16,7 +15,12 @@
 //   logits = W_lm rmsn(h)                                 (EPI_SCALE)
 // Every GEMV's epilogue writes the per-32-row sums of squares of its
 // output; the consumer adds them in a fixed order to get its input's RMS, so
-// RMS normalisation costs no extra pass and no extra node.
+// RMS normalisation costs no extra pass and no extra node.  The first GEMV
+// adds the squares of h0 itself.
+//
+// A persistent plan (Q4K_STACK_PERSISTENT) runs the same GEMV nodes, with
+// the same parameters and the same unit split, inside one cooperative
+// kernel per token (stack_kernel in q4k_gemv.hip).
 //
 // With the real token mixers ("Qwen3.6-27B on Apple M3 Pro — the llama.cpp
 // parity bar", architecture list; §4 of the diagnosis page asks for the GDN
@@ -64,6 +68,13 @@ struct q4k_stack {
     float *mix_scratch = nullptr;     // GDN conv outputs and gates
     int64_t *pos_dev = nullptr;       // device-side position
     int64_t host_pos = 0;             // tokens launched since creation or reset
+    // persistent plan
+    bool persistent = false;
+    int pgroups = 0;                  // co-resident workgroups of the kernel
+    void *pnodes = nullptr;           // node descriptors (device)
+    unsigned *psync = nullptr;        // per-node arrival counters, then the error word
+    unsigned epoch = 0;               // tokens launched (counters grow by pgroups each)
+    int spin = 1 << 20;               // polls before a wait gives up
 };
 
 namespace {
@@ -141,21 +152,27 @@ __global__ __launch_bounds__(256) void zero_kernel(float *p, int64_t n) {
     if (i < n) p[i] = 0.f;
 }
 
-// Enqueue the whole token on `cs` (under capture).
-int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
+// Enqueue the whole token on `cs` (under capture), or, with `pn`, append the
+// GEMV nodes' descriptors for the persistent kernel instead (no mixers then).
+int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint8_t> *pn) {
     float *A = s->arena;
     float *SQ = s->sq;
     int64_t n = 0;
-    int rc = launch_sumsq(A + s->off_h[0], s->hidden, SQ + s->sq_h[0], cs);
-    if (rc) return rc;
-    ++n;
+    int rc;
+    // the first GEMV reads h0 and adds its squares itself
+    auto h_sq = [&](int32_t l) -> const float * { return l == 0 ? nullptr : SQ + s->sq_h[l]; };
     auto run = [&](GemvParams p, int nmat, int epi, int64_t M, int64_t K) -> int {
-        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
-        p.ks = L.ks;
         p.ws = s->ws.partials;
         p.cnt = s->ws.counters;
         p.eps = s->eps;
         ++n;
+        if (pn) {
+            const size_t at = pn->size();
+            pn->resize(at + stack_node_bytes());
+            return fill_stack_node(pn->data() + at, p, nmat, epi, s->pgroups);
+        }
+        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
+        p.ks = L.ks;
         return launch_gemv(p, 1, nmat, epi, L, cs);
     };
     for (int32_t l = 0; l < s->n_layers; ++l) {
@@ -164,7 +181,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
         GemvParams p = base_params(L.mix_in);
         p.x = A + s->off_h[l];
         p.y = A + s->off_u[l];
-        p.in_sq = SQ + s->sq_h[l];
+        p.in_sq = h_sq(l);
         p.in_sq_n = (int32_t)tiles_of(s->hidden);
         p.in_len = (int32_t)s->hidden;
         p.out_sq = SQ + s->sq_u[l];
@@ -173,6 +190,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
         const float *mo = A + s->off_u[l];
         const float *mo_sq = SQ + s->sq_u[l];
         if (s->mixers) {
+            if (pn) return fail(Q4K_EUNSUPPORTED, "persistent plans have no token mixers");
             const q4k_mixer &m = s->mix[l];
             float *o = A + s->off_o[l];
             if (L.kind == 0) {
@@ -231,7 +249,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes) {
     GemvParams p = base_params(s->lm_head);
     p.x = A + s->off_h[s->n_layers];
     p.y = A + s->off_logits;
-    p.in_sq = SQ + s->sq_h[s->n_layers];
+    p.in_sq = h_sq(s->n_layers);
     p.in_sq_n = (int32_t)tiles_of(s->hidden);
     p.in_len = (int32_t)s->hidden;
     p.out_sq = SQ + s->sq_logits;
@@ -256,6 +274,8 @@ void release(q4k_stack *s) {
     if (s->states) (void)hipFree(s->states);
     if (s->mix_scratch) (void)hipFree(s->mix_scratch);
     if (s->pos_dev) (void)hipFree(s->pos_dev);
+    if (s->pnodes) (void)hipFree(s->pnodes);
+    if (s->psync) (void)hipFree(s->psync);
     free_workspace(&s->ws);
     delete s;
 }
@@ -283,9 +303,11 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     clear_error();
     if (!d || !out) return fail(Q4K_EINVAL, "NULL descriptor or output");
     *out = nullptr;
-    if (d->flags != 0 && d->flags != Q4K_STACK_MIXERS)
-        return fail(Q4K_EINVAL, "flags must be 0 or Q4K_STACK_MIXERS");
+    if (d->flags != 0 && d->flags != Q4K_STACK_MIXERS && d->flags != Q4K_STACK_PERSISTENT)
+        return fail(Q4K_EINVAL, "flags must be 0, Q4K_STACK_MIXERS or Q4K_STACK_PERSISTENT");
     const bool mixers = d->flags == Q4K_STACK_MIXERS;
+    const bool persistent = d->flags == Q4K_STACK_PERSISTENT;
+    if (persistent && d->spin_limit < 0) return fail(Q4K_EINVAL, "spin_limit must be >= 0");
     if (d->n_layers < 0 || d->hidden <= 0 || d->hidden % 256 != 0)
         return fail(Q4K_ESHAPE, "need n_layers >= 0 and hidden a positive multiple of 256");
     if (d->n_layers > 0 && !d->layers) return fail(Q4K_EINVAL, "NULL layers");
@@ -338,6 +360,14 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     s->layers.assign(d->layers, d->layers + d->n_layers);
     s->lm_head = d->lm_head;
     s->mixers = mixers;
+    s->persistent = persistent;
+    if (persistent) {
+        if (d->spin_limit > 0) s->spin = d->spin_limit;
+        if ((rc = stack_groups(&s->pgroups))) {
+            delete s;
+            return rc;
+        }
+    }
     if (mixers) {
         s->mix.assign(d->mixers, d->mixers + d->n_layers);
         s->cap = d->attn_capacity;
@@ -352,7 +382,8 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     };
     size_t max_partials = 0, max_counters = 0;
     auto need = [&](int64_t M, int64_t K, int nmat, int epi) {
-        const GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
+        GemvLaunch L = choose_gemv_launch(M, K, 1, nmat, epi);
+        if (persistent) L.ks = s->pgroups;  // every node spans the whole grid
         max_partials = std::max(max_partials, gemv_partial_floats(L, 1));
         max_counters = std::max(max_counters, gemv_counters(L));
     };
@@ -423,6 +454,33 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         return fail(Q4K_EHIP, "decode stack: arena clear failed");
     }
 
+    if (persistent) {
+        // node descriptors built once on the host, then uploaded; counters
+        // and the error word start at zero
+        std::vector<uint8_t> pn;
+        int64_t nodes = 0;
+        if ((rc = enqueue_token(s, nullptr, &nodes, &pn))) {
+            release(s);
+            return rc;
+        }
+        const size_t sync_bytes = ((size_t)nodes + 1) * sizeof(unsigned);
+        if (hipMalloc(&s->pnodes, pn.size()) != hipSuccess ||
+            hipMalloc(&s->psync, sync_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            release(s);
+            return fail(Q4K_ENOMEM, "decode stack: node table allocation failed");
+        }
+        if (hipMemcpy(s->pnodes, pn.data(), pn.size(), hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemset(s->psync, 0, sync_bytes) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
+            release(s);
+            return fail(Q4K_EHIP, "decode stack: node table upload failed");
+        }
+        s->n_nodes = nodes;
+        *out = s;
+        return Q4K_OK;
+    }
+
     // capture on a private stream (default priority)
     hipStream_t cs = nullptr;
     if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) {
@@ -432,7 +490,7 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
     hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     int64_t nodes = 0;
     if (e == hipSuccess) {
-        rc = enqueue_token(s, cs, &nodes);
+        rc = enqueue_token(s, cs, &nodes, nullptr);
         hipGraph_t g = nullptr;
         hipError_t e2 = hipStreamEndCapture(cs, &g);
         if (rc == Q4K_OK && e2 != hipSuccess) rc = hip_fail(e2, "hipStreamEndCapture");
@@ -471,7 +529,14 @@ int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *strea
     hipStream_t st = (hipStream_t)stream;
     Q4K_HIP(hipMemcpyAsync(s->arena + s->off_h[0], h_in, (size_t)s->hidden * sizeof(float),
                            hipMemcpyDeviceToDevice, st));
-    Q4K_HIP(hipGraphLaunch(s->exec, st));
+    if (s->persistent) {
+        const int rc = launch_stack_kernel(s->pnodes, (int)s->n_nodes, s->psync, s->epoch,
+                                           s->psync + s->n_nodes, s->spin, s->pgroups, st);
+        if (rc) return rc;
+        ++s->epoch;
+    } else {
+        Q4K_HIP(hipGraphLaunch(s->exec, st));
+    }
     if (logits)
         Q4K_HIP(hipMemcpyAsync(logits, s->arena + s->off_logits,
                                (size_t)s->lm_head.M * sizeof(float), hipMemcpyDeviceToDevice, st));
@@ -489,6 +554,27 @@ int q4k_decode_stack_position(q4k_stack *s, int64_t *pos) {
     clear_error();
     if (!s || !pos) return fail(Q4K_EINVAL, "NULL argument");
     *pos = s->host_pos;
+    return Q4K_OK;
+}
+
+int q4k_decode_stack_status(q4k_stack *s, void *stream, int32_t *status) {
+    clear_error();
+    if (!s || !status) return fail(Q4K_EINVAL, "NULL argument");
+    *status = 0;
+    if (!s->persistent) return Q4K_OK;
+    hipStream_t st = (hipStream_t)stream;
+    unsigned word = 0;
+    Q4K_HIP(hipStreamSynchronize(st));
+    Q4K_HIP(hipMemcpy(&word, s->psync + s->n_nodes, sizeof word, hipMemcpyDeviceToHost));
+    if (word) {
+        // A workgroup that gave up may have run into the next node while its
+        // tiles were still being finished, leaving split-tile counters off
+        // zero: clear them with the record, so later tokens are sound.
+        Q4K_HIP(hipMemset(s->psync + s->n_nodes, 0, sizeof word));
+        Q4K_HIP(hipMemset(s->ws.counters, 0, kCounterBytes));
+    }
+    Q4K_HIP(hipDeviceSynchronize());
+    *status = word ? 1 : 0;
     return Q4K_OK;
 }
 

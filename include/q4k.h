@@ -338,6 +338,15 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
  * positions), all zero at creation and after q4k_decode_stack_reset; the
  * position lives on the device and the graph advances it by one per token,
  * so a token is still one graph launch.
+ *
+ * With Q4K_STACK_PERSISTENT in flags (stand-in mixer only) a token is ONE
+ * cooperative kernel instead of a graph of kernels: every workgroup walks
+ * the whole node list, loads its share of the next matrix while it waits for
+ * the current one to finish (a counter per node), and hands activations over
+ * through device-coherent stores.  The arithmetic of every node is that of
+ * the graph plan, so both give the same logits bit for bit.  Each wait is
+ * bounded (spin_limit polls, default 2^20); a wait that runs out records an
+ * error that q4k_decode_stack_status reports, and the kernel still ends.
  * ---------------------------------------------------------------------- */
 
 typedef struct {
@@ -356,6 +365,7 @@ typedef struct {
 } q4k_mixer;
 
 #define Q4K_STACK_MIXERS 1
+#define Q4K_STACK_PERSISTENT 2
 
 typedef struct {
     int64_t hidden;          /* residual width (K of mix_in/gate/up/lm_head, M of mix_out/down) */
@@ -363,10 +373,13 @@ typedef struct {
     const q4k_layer *layers; /* n_layers entries, copied at create time */
     q4k_mat lm_head;
     float eps;               /* RMS epsilon, e.g. 1e-6 */
-    int32_t flags;           /* 0 (stand-in mixer) or Q4K_STACK_MIXERS */
+    int32_t flags;           /* 0 (stand-in mixer, graph), Q4K_STACK_MIXERS or
+                                Q4K_STACK_PERSISTENT (not both) */
     const q4k_mixer *mixers; /* Q4K_STACK_MIXERS: n_layers entries, copied (their weight
                                 pointers are borrowed); otherwise ignored */
     int64_t attn_capacity;   /* Q4K_STACK_MIXERS: KV-cache positions of each attention layer */
+    int32_t spin_limit;      /* Q4K_STACK_PERSISTENT: polls before a wait between nodes
+                                gives up (0 = 2^20, about a second); otherwise ignored */
 } q4k_stack_desc;
 
 typedef struct q4k_stack q4k_stack; /* opaque plan: owns its graph and activation arena */
@@ -396,6 +409,14 @@ int q4k_decode_stack_reset(q4k_stack *s, void *stream);
 /* Tokens launched since creation or the last reset. */
 int q4k_decode_stack_position(q4k_stack *s, int64_t *pos);
 
+/* Health of a persistent plan: synchronises `stream`, sets *status to 0 if
+ * every wait between nodes ended normally since the last call, 1 if one ran
+ * out of polls (the logits of the tokens since the last call are then not to
+ * be trusted), and clears the record together with the plan's split-tile
+ * counters, so that later tokens are sound again.  Always 0 for graph plans.  Not a hot call (it waits
+ * for the device). */
+int q4k_decode_stack_status(q4k_stack *s, void *stream, int32_t *status);
+
 /* Arena buffers of the last token, for per-stage checks.  `which`:
  *   Q4K_BUF_H     residual stream entering layer `layer` (layer = n_layers:
  *                 the final residual that feeds lm_head)        [hidden]
@@ -420,7 +441,9 @@ enum {
 int q4k_decode_stack_buffer(q4k_stack *s, int32_t layer, int32_t which,
                             const float **ptr, int64_t *n);
 
-/* Number of kernel nodes in the plan's graph (for launch-overhead accounting). */
+/* Number of kernel nodes in the plan's graph (for launch-overhead
+ * accounting); for a persistent plan, the number of GEMV nodes its one
+ * kernel walks. */
 int q4k_decode_stack_nodes(q4k_stack *s, int64_t *n_nodes);
 
 /* Free the plan (graph, arena, workspace).  NULL-safe.  Synchronises the

@@ -383,6 +383,16 @@ def test_stack_create_validation_with_mixers(lib):
         mut(d)
         assert lib.q4k_decode_stack_create(ctypes.byref(d), None, ctypes.byref(out)) == code, name
         assert not out.value
+    # a persistent plan takes no mixers and a non-negative poll limit
+    layers()
+    mixers()
+    for flags, spin in ((q4k.STACK_MIXERS | q4k.STACK_PERSISTENT, 0), (q4k.STACK_PERSISTENT, -1),
+                        (4, 0)):
+        d = q4k.StackDesc(512, 2, L, mk(300, 512), 1e-6, flags, mx, 16, spin)
+        assert lib.q4k_decode_stack_create(ctypes.byref(d), None, ctypes.byref(out)) == -1, flags
+        assert not out.value
     n = ctypes.c_int64()
+    st = ctypes.c_int32(7)
     assert lib.q4k_decode_stack_reset(None, None) == -1
     assert lib.q4k_decode_stack_position(None, ctypes.byref(n)) == -1
+    assert lib.q4k_decode_stack_status(None, None, ctypes.byref(st)) == -1
