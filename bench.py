@@ -31,8 +31,11 @@ Also measured and reported in the same line:
   * gemv_q6_k_mlp: Q6_K GEMVs on the two MLP shapes (73 MB each, cold);
   * roofline: the dominant kernel (the MLP GEMV) — algorithmic bytes per
     launch over its HIP-event duration, against 8 TB/s;
-  * cpu_baseline: the CPU oracle (double precision, all host cores) on the
-    same three GEMVs.
+  * cpu_baseline: the CPU oracle (double precision, all threads) on the
+    same three GEMVs; cpu_baseline_detail: the oracle at one thread and at
+    all threads on every workload (C1 small GEMV, C2 MLP GEMVs, C3 decode
+    stack from a sampled layer pair, C4 batched N = 1..16, C5 GEMM from a
+    row sample), with the host CPU model.
 """
 from __future__ import annotations
 
@@ -73,6 +76,130 @@ def source_hash(paths):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_leg(x, step_bytes):
+    """The CPU oracle (oracle/, double precision) timed on this host: one
+    thread and all threads the harness allows (OMP_NUM_THREADS, else every
+    core), on bounded samples of each workload, scaled to each workload's
+    unit.  A reported baseline only: the oracle is never tuned for speed.
+    Bounded so that the whole leg takes about half a minute."""
+    import numpy as np  # noqa: F401  (arrays from synth)
+    import oracle
+    import synth
+    from synth import workloads as wl
+    n_all = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    modes = (("1_thread", 1), ("all_threads", n_all))
+
+    def med3(fn, min_s):
+        """median over 3 runs of (seconds per call), each run >= min_s"""
+        res = []
+        for _ in range(3):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                n += 1
+                if time.perf_counter() - t0 >= min_s:
+                    break
+            res.append((time.perf_counter() - t0) / n)
+        return float(sorted(res)[1])
+
+    def once(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    det = {"cpu_model": cpu_model(), "cores_visible": os.cpu_count(), "threads_all": n_all}
+    # C2: the three MLP GEMVs (the headline workload), whole matrices
+    ws = [synth.q4k_weight(synth.key(2, i), M, K) for i, (_, M, K) in enumerate(wl.MLP)]
+    a_h = synth.activations(2, 1, wl.INTER, first=1)[0]
+
+    def mlp_step():
+        for wh, (_, M, K) in zip(ws, wl.MLP):
+            oracle.gemv(wh, x if K == wl.HIDDEN else a_h, M, K)
+
+    c2 = {}
+    for name, n in modes:
+        oracle.set_threads(n)
+        t = med3(mlp_step, 1.0 if n > 1 else 0.5)
+        c2[name] = {"GBps": step_bytes / t / 1e9, "ms_per_step": t * 1e3,
+                    "threads": oracle.get_threads()}
+    det["C2_mlp_gemvs"] = c2
+    # C1: the 512x1024 GEMV, whole
+    w1 = synth.q4k_weight(synth.key(1, 0), 512, 1024)
+    x1 = synth.activations(1, 1, 1024)[0]
+    c1 = {}
+    for name, n in modes:
+        oracle.set_threads(n)
+        t = med3(lambda: oracle.gemv(w1, x1, 512, 1024), 0.2)
+        c1[name] = {"us": t * 1e6, "GBps": wbytes(512, 1024) / t / 1e9}
+    det["C1_gemv_512x1024"] = c1
+    # C4: batched GEMV on 17408x5120, N = 1..16, whole matrix
+    M4, K4 = wl.BATCH_SHAPE
+    w4 = ws[0]
+    c4 = {}
+    for name, n in modes:
+        oracle.set_threads(n)
+        per = {}
+        for N in (wl.BATCH_N if n > 1 else (1, 16)):
+            X = synth.activations(4, N, K4)
+            t = med3(lambda: oracle.gemv_batch(w4, X, M4, K4), 0.3) if n > 1 else \
+                once(lambda: oracle.gemv_batch(w4, X, M4, K4))
+            per[str(N)] = {"us": t * 1e6, "us_per_vector": t * 1e6 / N}
+        c4[name] = per
+    det["C4_batch_17408x5120"] = c4
+    # C5: prefill GEMM 17408x5120 at P = 256 on a sample of 256 rows, as TFLOP/s
+    rows = list(range(0, M4, M4 // 256))[:256]
+    X5 = synth.activations(5, 256, K4)
+    c5 = {}
+    for name, n in modes:
+        oracle.set_threads(n)
+        t = once(lambda: oracle.gemm(w4, X5, M4, K4, rows=rows))
+        c5[name] = {"TFLOPs": 2.0 * len(rows) * K4 * 256 / t / 1e12, "seconds": t}
+    det["C5_gemm_17408x5120_P256"] = dict(c5, sample="256 evenly spaced rows x all 256 tokens "
+                                                  "(0.67 GFLOP), one run")
+    # C3: decode stack, sampled: one GDN layer, one attention layer and the
+    # lm_head through the oracle chain, scaled to the 64-layer token by bytes
+    del ws
+    sample = [0, 3]
+    mats, shp = [], []
+    for l in sample:
+        for name in wl.LAYER_MATS:
+            M, K = wl.layer_shapes(l)[name]
+            mats.append(synth.q4k_weight(wl.stack_tensor_key(l, name), M, K))
+            shp.append((M, K))
+    mats.append(synth.q4k_weight(wl.stack_tensor_key(None, "lm_head"), wl.VOCAB, wl.HIDDEN))
+    shp.append((wl.VOCAB, wl.HIDDEN))
+    sb = sum(wbytes(M, K) for M, K in shp)
+    h0 = synth.activations(3, 1, wl.HIDDEN)[0]
+    c3 = {}
+    for name, n in modes:
+        oracle.set_threads(n)
+        t = once(lambda: oracle.stack(mats, shp, len(sample), wl.HIDDEN, h0))
+        c3[name] = {"us_per_token": t * 1e6 * wl.stack_bytes() / sb, "sample_seconds": t}
+    det["C3_decode_stack"] = dict(c3, sample="layers 0 (GDN-shaped) and 3 (attention-shaped) "
+                                             "plus the lm_head (%.2f GB), scaled by bytes to "
+                                             "the 14.41 GB token" % (sb / 1e9))
+    oracle.set_threads(n_all)
+    head = c2["all_threads"]
+    return {"cpu_baseline": {"value": head["GBps"], "unit": "GB/s", "cores": head["threads"],
+                             "kind": "oracle",
+                             "sample": "median of 3 runs (>= 1 s each) of the three full MLP "
+                                       "GEMVs (gate, up, down), double-precision oracle, rows "
+                                       "over %d threads on %s" % (head["threads"], det["cpu_model"])},
+            "cpu_baseline_detail": det}
 
 
 def main():
@@ -426,7 +553,13 @@ def main():
                 tf = 2.0 * M * K * P / t / 1e6
                 res.append({"M": M, "K": K, "P": P, "us": t, "TFLOPs": tf,
                             "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
-                            "tile_tokens_workgroups": list(q4k.gemm_config(M, K, P))})
+                            "tile_tokens_workgroups": list(q4k.gemm_config(M, K, P)),
+                            "roofline": {"bound": "mfma", "achieved": tf,
+                                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                                         "flops_per_call": 2.0 * M * K * P,
+                                         "timing": "HIP events around each call (prologue, "
+                                                   "main kernel and fix-up)"}})
                 del X, Y
         out["prefill_gemm"] = [r for r in res if r["P"] not in SHORT_P]
         out["prefill_gemm_short"] = [r for r in res if r["P"] in SHORT_P]
@@ -478,7 +611,14 @@ def main():
         out["decode_stack"] = {"us_per_token_median": med, "us_per_token_mean": float(np.mean(ts)),
                                "us_per_token_wall": wall_tok, "tokens": args.stack_tokens,
                                "weight_bytes": tot, "roofline_us": roof, "frac_roofline": roof / med,
-                               "GBps": tot / med / 1e3, "graph_nodes": stk.nodes()}
+                               "GBps": tot / med / 1e3, "graph_nodes": stk.nodes(),
+                               "roofline": {"bound": "hbm", "achieved": tot / med / 1e3,
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": tot / med / 1e3 / HBM_PEAK_GBS,
+                                            "traffic": None,
+                                            "bytes_per_token": tot,
+                                            "timing": "HIP events around each token (h copy "
+                                                      "in, graph launch, logits copy out)"}}
         log("stack: %.1f us/token (roofline %.1f)" % (med, roof))
         ref_logits = logits.clone()
         stk.close()
@@ -526,21 +666,7 @@ def main():
 
     # ------------------------------------------------------------ CPU baseline
     if "cpu" in sections:
-        import oracle
-        oracle.set_threads(os.cpu_count() or 1)
-        ws = [synth.q4k_weight(synth.key(2, i), M, K) for i, (_, M, K) in enumerate(wl.MLP)]
-        a_h = synth.activations(2, 1, wl.INTER, first=1)[0]
-        reps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < 10.0:
-            for wh, (_, M, K) in zip(ws, wl.MLP):
-                oracle.gemv(wh, x if K == wl.HIDDEN else a_h, M, K)
-            reps += 1
-        dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": reps * step_bytes / dt / 1e9, "unit": "GB/s",
-                               "cores": oracle.get_threads(), "kind": "oracle",
-                               "sample": "%d repeats of the three full MLP GEMVs (gate, up, down; "
-                                         "%.2f s), double-precision oracle, rows over all threads"
-                                         % (reps, dt)}
+        out.update(cpu_leg(x, step_bytes))
     if "value" not in out:
         out["value"] = None
         out["unit"] = "GB/s"

@@ -37,6 +37,7 @@ EXPORTS = (
     "q4k_decode_stack_nodes", "q4k_decode_stack_destroy", "q4k_gemv_config", "q4k_gemm_config",
     "q4k_tune_gemv", "q4k_tune_gemm", "q4k_gemv_noalloc", "q4k_gdn_step", "q4k_attn_step",
     "q4k_decode_stack_reset", "q4k_decode_stack_position", "q4k_decode_stack_status",
+    "q4k_check_partition",
 )
 OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP = range(7)
 
@@ -129,6 +130,8 @@ def load(path: str | None = None):
     L.q4k_decode_stack_position.restype = ctypes.c_int
     L.q4k_decode_stack_status.argtypes = [p, p, ctypes.POINTER(i32)]
     L.q4k_decode_stack_status.restype = ctypes.c_int
+    L.q4k_check_partition.argtypes = [i32, i64, i64, i64, i32]
+    L.q4k_check_partition.restype = ctypes.c_int
     L.q4k_decode_stack_destroy.argtypes = [p]
     L.q4k_decode_stack_destroy.restype = None
     L.q4k_gemv_config.argtypes = [i64, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -499,6 +502,12 @@ def tune_gemv(waves_per_group: int = 0, workgroups: int = 0) -> None:
     """Force the GEMV workgroup count (0: automatic); waves_per_group must be 0 or 4."""
     check(load().q4k_tune_gemv(waves_per_group, workgroups))
     _ws_need.clear()
+
+
+def check_partition(op: int, M: int, K: int, N: int = 1, workgroups: int = 0) -> None:
+    """Host-side check of the work partition a launch would use (no device
+    needed); raises Q4KError naming the first violation."""
+    check(load().q4k_check_partition(op, M, K, N, workgroups))
 
 
 def tune_gemm(tile_tokens: int = 0, workgroups: int = 0) -> None:

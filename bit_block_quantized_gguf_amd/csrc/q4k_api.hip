@@ -531,6 +531,30 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
                             nullptr, out, (hipStream_t)stream);
 }
 
+int q4k_check_partition(int32_t op, int64_t M, int64_t K, int64_t N, int32_t workgroups) {
+    clear_error();
+    if (workgroups < 0 || workgroups > (int32_t)kMaxCounters)
+        return fail(Q4K_EINVAL, "workgroups must be in 0..%zu", kMaxCounters);
+    if (M <= 0 || K <= 0 || M > kMaxRows || K > kMaxCols)
+        return fail(Q4K_ESHAPE, "bad shape %lld x %lld", (long long)M, (long long)K);
+    switch (op) {
+        case Q4K_OP_GEMV: return check_gemv_partition(M, K, 1, 1, workgroups);
+        case Q4K_OP_GEMV_BATCH:
+            if (N < 1) return fail(Q4K_ESHAPE, "N must be >= 1");
+            return check_gemv_partition(M, K, (int)std::min<int64_t>(N, 16), 1, workgroups);
+        case Q4K_OP_MLP: {  // M = intermediate, K = hidden
+            const int rc = check_gemv_partition(M, K, 1, 2, workgroups);
+            return rc ? rc : check_gemv_partition(K, M, 1, 1, workgroups);
+        }
+        case Q4K_OP_GEMM:
+            if (N < 1) return fail(Q4K_ESHAPE, "P must be >= 1");
+            return check_gemm_partition(M, K, N, 0, workgroups);
+        case Q4K_OP_GEMV_Q8_0: return check_gemv_q8_partition(M, K, workgroups);
+        case Q4K_OP_GEMV_Q6_K: return check_gemv_q6_partition(M, K, workgroups);
+        default: return fail(Q4K_EINVAL, "op %d has no partition to check", op);
+    }
+}
+
 /* Benchmark knobs: force the GEMV workgroup count and the GEMM tile width and
  * workgroup count (0 restores the shape heuristics).  Not thread-safe with
  * respect to concurrent calls; meant for sweeps. */

@@ -87,9 +87,9 @@ struct SKUnits {
     int rtiles;   // 256-row tiles
     int64_t U;    // total work items = tiles * nb
     int G;        // workgroups
-    __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
+    __host__ __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
     // workgroup whose range contains item u
-    __device__ __forceinline__ int owner(int64_t u) const {
+    __host__ __device__ __forceinline__ int owner(int64_t u) const {
         return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
     }
 };
@@ -581,6 +581,76 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
             default: hipLaunchKernelGGL(gemm_fixup_kernel<1>, fg, dim3(256), 0, stream, p, su); break;
         }
         Q4K_HIP(hipGetLastError());
+    }
+    return Q4K_OK;
+}
+
+// Host-side check of a GEMM launch's stream-K partition, with the kernels'
+// own range and owner arithmetic (SKUnits): contiguous non-empty ranges
+// covering every work item once; the segments a workgroup walks (as
+// gemm_kernel does) write at most one partial tile per slot, inside the
+// partial area the launch reserves, and read only token rows inside the
+// padded bf16 X copy; every tile the fix-up sums has consecutive
+// contributors that all wrote a partial of it, in the slot the fix-up reads.
+int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int groups) {
+    if (M <= 0 || K <= 0 || K % 256 != 0 || P <= 0)
+        return fail(Q4K_EINVAL, "check: bad arguments");
+    GemmLaunch L = choose_gemm_launch(M, K, P);
+    if (tile_tokens > 0) L.r = tile_tokens / 32;
+    if (groups > 0) L.ks = groups;
+    if (L.r != 1 && L.r != 2 && L.r != 4 && L.r != 8)
+        return fail(Q4K_EINVAL, "check: tile of %d tokens", 32 * L.r);
+    const SKUnits su = sk_units(M, K, P, L.r, L.ks);
+    const int64_t BN = 32 * L.r, tile_floats = (int64_t)BM * BN;
+    const int64_t partials = (int64_t)gemm_partial_floats(L, M, P);
+    const int64_t ptok = padded_tokens(P);
+    if ((int64_t)gemm_xb_floats(K, P) * 2 < ptok * K)
+        return fail(Q4K_EINVAL, "check: bf16 X copy smaller than its padded tokens");
+    int64_t prev = 0;
+    for (int g = 0; g < su.G; ++g) {
+        const int64_t ua = su.begin(g), ub = su.begin(g + 1);
+        if (ua != prev || ub <= ua)
+            return fail(Q4K_EINVAL, "check: range of workgroup %d is [%lld, %lld)", g,
+                        (long long)ua, (long long)ub);
+        prev = ub;
+        if (su.owner(ua) != g || su.owner(ub - 1) != g)
+            return fail(Q4K_EINVAL, "check: owner() disagrees with begin() at workgroup %d", g);
+        const int64_t first_tile = ua / su.nb;
+        int used[2] = {0, 0};
+        for (int64_t u = ua; u < ub;) {
+            const int64_t tile = u / su.nb, tb = tile * su.nb;
+            const int64_t je = std::min<int64_t>(ub, tb + su.nb) - tb, jb = u - tb;
+            const int64_t tt = tile / su.rtiles;
+            if ((tt + 1) * BN > ptok)
+                return fail(Q4K_EINVAL, "check: tile %lld reads tokens past the padded copy",
+                            (long long)tile);
+            if (!(jb == 0 && je == su.nb)) {
+                const int slot = tile == first_tile ? 0 : 1;
+                if (++used[slot] > 1)
+                    return fail(Q4K_EINVAL, "check: workgroup %d writes slot %d twice", g, slot);
+                if (((int64_t)g * 2 + slot + 1) * tile_floats > partials)
+                    return fail(Q4K_EINVAL, "check: partial slot of workgroup %d outside", g);
+            }
+            u = tb + je;
+        }
+    }
+    if (prev != su.U) return fail(Q4K_EINVAL, "check: ranges end at %lld of %lld items",
+                                  (long long)prev, (long long)su.U);
+    for (int bnd = 1; bnd < su.G; ++bnd) {  // the fix-up's view
+        const int64_t ub = su.begin(bnd), tile = ub / su.nb, tb = tile * su.nb;
+        if (ub == tb || su.begin(bnd - 1) > tb) continue;
+        const int gf = su.owner(tb), gl = su.owner(tb + su.nb - 1);
+        if (gf >= gl) return fail(Q4K_EINVAL, "check: cut tile %lld has one contributor",
+                                  (long long)tile);
+        for (int w = gf; w <= gl; ++w) {
+            const int64_t a = su.begin(w), b = su.begin(w + 1);
+            const int slot = a / su.nb == tile ? 0 : 1;
+            const bool wrote = a < tb + su.nb && b > tb && !(a <= tb && b >= tb + su.nb);
+            const bool slot_ok = slot == 0 ? a >= tb : (a < tb && (b - 1) / su.nb == tile);
+            if (!wrote || !slot_ok)
+                return fail(Q4K_EINVAL, "check: fix-up of tile %lld reads workgroup %d slot %d "
+                            "that it did not write", (long long)tile, w, slot);
+        }
     }
     return Q4K_OK;
 }

@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <atomic>
 #include <map>
+#include <vector>
 #include <mutex>
 #include <utility>
 
@@ -364,7 +365,7 @@ __device__ __forceinline__ void epilogue(const GemvParams &p, int row0, int lane
 // restoring division: a few scalar instructions of code instead of the long
 // inlined sequence a 64-bit '/' expands to (which grew every kernel to
 // 40 KB, most of it copies of that sequence).
-__device__ __forceinline__ uint64_t udiv64_compact(uint64_t n, uint64_t d) {
+__host__ __device__ __forceinline__ uint64_t udiv64_compact(uint64_t n, uint64_t d) {
     uint64_t q = 0, r = 0;
 #pragma unroll 1
     for (int i = 63; i >= 0; --i) {
@@ -376,10 +377,10 @@ __device__ __forceinline__ uint64_t udiv64_compact(uint64_t n, uint64_t d) {
     }
     return q;
 }
-__device__ __forceinline__ int64_t range_begin64(int g, int64_t U, int G) {
+__host__ __device__ __forceinline__ int64_t range_begin64(int g, int64_t U, int G) {
     return (int64_t)udiv64_compact((uint64_t)g * (uint64_t)U, (uint64_t)G);
 }
-__device__ __forceinline__ int range_owner64(int64_t u, int64_t U, int G) {
+__host__ __device__ __forceinline__ int range_owner64(int64_t u, int64_t U, int G) {
     return (int)udiv64_compact((uint64_t)(u + 1) * (uint64_t)G + (uint64_t)U - 1, (uint64_t)U) - 1;
 }
 
@@ -390,12 +391,12 @@ struct Units {
     int64_t U;    // total units = tiles * upt
     int G;        // workgroups in the main grid
     bool small;   // (U + 1) * G < 2^32
-    __device__ __forceinline__ int64_t begin(int g) const {
+    __host__ __device__ __forceinline__ int64_t begin(int g) const {
         if (small) return (int64_t)((uint32_t)g * (uint32_t)U / (uint32_t)G);
         return range_begin64(g, U, G);
     }
     // workgroup whose range contains unit u
-    __device__ __forceinline__ int owner(int64_t u) const {
+    __host__ __device__ __forceinline__ int owner(int64_t u) const {
         if (small)
             return (int)(((uint32_t)(u + 1) * (uint32_t)G + (uint32_t)U - 1) / (uint32_t)U) - 1;
         return range_owner64(u, U, G);
@@ -1202,15 +1203,24 @@ int groups_for(int64_t M, int64_t K, int *G) {
     return Q4K_OK;
 }
 
+// The unit partition of a launch (what the kernels receive): tiles of
+// 64 / nmat rows, units of bpu blocks of a tile's rows.
+Units make_units(int64_t M, int64_t nb, int nmat, int64_t groups, int bpu = WK) {
+    const int64_t rows = 64 / nmat;
+    const int64_t tiles = (M + rows - 1) / rows;
+    Units un;
+    un.upt = (int)((nb + bpu - 1) / bpu);
+    un.U = tiles * un.upt;
+    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(groups, un.U));
+    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    return un;
+}
+
 template <int NV, int NMAT, int EPI>
 int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     constexpr int ROWS = 64 / NMAT;
     const int64_t tiles = (p.M + ROWS - 1) / ROWS;
-    Units un;
-    un.upt = (p.nb + WK - 1) / WK;
-    un.U = tiles * un.upt;
-    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
-    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    const Units un = make_units(p.M, p.nb, NMAT, L.ks);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
                        stream, p, un);
@@ -1250,6 +1260,96 @@ size_t gemv_partial_floats(const GemvLaunch &L, int nv) {
 }
 
 size_t gemv_counters(const GemvLaunch &L) { return (size_t)L.ks; }
+
+// Host-side check of a GEMV launch's partition, with the kernels' own range
+// and owner arithmetic (Units): contiguous non-empty ranges covering every
+// unit once; each tile cut between workgroups has consecutive contributors
+// gf..gl that all hold some of its units, gf first-contributes to no other
+// cut tile (its counter is the tile's), and every partial slot and counter
+// index lies inside the workspace the launch reserves; the weight bytes the
+// first and last unit of every range fetch (rows clamped to M - 1, blocks
+// past the row end re-reading the unit's first block) stay inside the
+// matrix, with 32-bit lane offsets that do not wrap.
+namespace {
+int check_units(int64_t M, int64_t nb, int64_t block_bytes, int bpu, int nmat, int nvk,
+                int64_t groups) {
+    const int64_t row_bytes = nb * block_bytes, rows = 64 / nmat;
+    const Units un = make_units(M, nb, nmat, groups, bpu);
+    const int G = un.G;
+    const size_t partial_floats = gemv_partial_floats(GemvLaunch{WK, G}, nvk);
+    if (gemv_counters(GemvLaunch{WK, G}) > kMaxCounters)
+        return fail(Q4K_EINVAL, "check: %d workgroups exceed the counter region", G);
+    if (un.small && (un.U + 1) * (int64_t)G + un.U >= ((int64_t)1 << 32))
+        return fail(Q4K_EINVAL, "check: 32-bit range arithmetic would wrap");
+    std::vector<int> first_of(G, 0);
+    int64_t prev = 0;
+    for (int g = 0; g < G; ++g) {
+        const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+        if (ua != prev || ub <= ua)
+            return fail(Q4K_EINVAL, "check: range of workgroup %d is [%lld, %lld)", g,
+                        (long long)ua, (long long)ub);
+        prev = ub;
+        if (un.owner(ua) != g || un.owner(ub - 1) != g)
+            return fail(Q4K_EINVAL, "check: owner() disagrees with begin() at workgroup %d", g);
+        const int64_t ft = ua / un.upt, lt = (ub - 1) / un.upt;
+        const int64_t tl[2] = {ft, lt};
+        for (int slot = 0; slot < (ft == lt ? 1 : 2); ++slot) {
+            const int64_t t = tl[slot];
+            const int64_t t0u = t * un.upt, t1u = t0u + un.upt - 1;
+            const bool cut = un.owner(t0u) != un.owner(t1u);
+            if ((((int64_t)g * 2 + slot) * nvk + nvk) * 64 > (int64_t)partial_floats)
+                return fail(Q4K_EINVAL, "check: partial slot of workgroup %d outside", g);
+            if (!cut) continue;
+            const int gf = un.owner(t0u), gl = un.owner(t1u);
+            for (int w = gf; w <= gl; ++w)
+                if (un.begin(w) > t1u || un.begin(w + 1) <= t0u)
+                    return fail(Q4K_EINVAL, "check: workgroup %d holds none of cut tile %lld", w,
+                                (long long)t);
+            if (g == gf && ++first_of[gf] > 1)
+                return fail(Q4K_EINVAL, "check: workgroup %d first-contributes to two cut tiles", gf);
+        }
+        for (int64_t u : {ua, ub - 1}) {
+            const int64_t t = u / un.upt, k = u % un.upt, j0 = k * bpu;
+            const int64_t rmax = std::min<int64_t>(rows - 1, M - 1 - t * rows);
+            const int64_t valid = std::min<int64_t>(bpu, nb - j0) * block_bytes;
+            const int64_t base = t * rows * row_bytes + j0 * block_bytes;
+            const int64_t lane_max = rmax * row_bytes + valid;  // one past the last byte
+            if (rmax < 0 || valid <= 0 || base + lane_max > M * row_bytes)
+                return fail(Q4K_EINVAL, "check: unit %lld fetches outside the matrix",
+                            (long long)u);
+            if (lane_max > ((int64_t)1 << 32))
+                return fail(Q4K_EINVAL, "check: 32-bit lane offset wraps at unit %lld",
+                            (long long)u);
+        }
+    }
+    if (prev != un.U) return fail(Q4K_EINVAL, "check: ranges end at %lld of %lld units",
+                                  (long long)prev, (long long)un.U);
+    return Q4K_OK;
+}
+}  // namespace
+
+int check_gemv_partition(int64_t M, int64_t K, int nv, int nmat, int groups) {
+    if (M <= 0 || K <= 0 || K % 256 != 0 || (nmat != 1 && nmat != 2) || nv < 1)
+        return fail(Q4K_EINVAL, "check: bad arguments");
+    GemvLaunch L = choose_gemv_launch(M, K, nv, nmat, nmat == 2 ? EPI_SWIGLU : EPI_PLAIN);
+    if (groups > 0) L.ks = groups;
+    const int nvk = nmat == 2 ? 1 : nv >= 16 ? 16 : nv >= 8 ? 8 : nv >= 4 ? 4 : nv >= 2 ? 2 : 1;
+    return check_units(M, K / 256, kBlockBytes, WK, nmat, nvk, L.ks);
+}
+
+int check_gemv_q8_partition(int64_t M, int64_t K, int groups) {
+    if (M <= 0 || K <= 0 || K % 32 != 0) return fail(Q4K_EINVAL, "check: bad arguments");
+    GemvLaunch L = choose_gemv_q8_launch(M, K);
+    if (groups > 0) L.ks = groups;
+    return check_units(M, K / 32, Q8_BB, Q8_UNIT_BLOCKS, 1, 1, L.ks);
+}
+
+int check_gemv_q6_partition(int64_t M, int64_t K, int groups) {
+    if (M <= 0 || K <= 0 || K % 1024 != 0) return fail(Q4K_EINVAL, "check: bad arguments");
+    GemvLaunch L = choose_gemv_q6_launch(M, K);
+    if (groups > 0) L.ks = groups;
+    return check_units(M, K / 256, Q6_BB, WK, 1, 1, L.ks);
+}
 
 int launch_gemv(const GemvParams &p, int nv, int nmat, int epi, const GemvLaunch &L,
                 hipStream_t stream) {
@@ -1292,11 +1392,7 @@ GemvLaunch choose_gemv_q8_launch(int64_t M, int64_t K) {
 
 int launch_gemv_q8(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     const int64_t tiles = (p.M + 63) / 64;
-    Units un;
-    un.upt = (p.nb + Q8_UNIT_BLOCKS - 1) / Q8_UNIT_BLOCKS;
-    un.U = tiles * un.upt;
-    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
-    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    const Units un = make_units(p.M, p.nb, 1, L.ks, Q8_UNIT_BLOCKS);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL(gemv_q8_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
     Q4K_HIP(hipGetLastError());
@@ -1323,11 +1419,7 @@ GemvLaunch choose_gemv_q6_launch(int64_t M, int64_t K) {
 int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     const int64_t tiles = (p.M + 63) / 64;
     if (p.nb % WK != 0) return fail(Q4K_ESHAPE, "gemv_q6_k: K must be a multiple of 1024");
-    Units un;
-    un.upt = p.nb / WK;
-    un.U = tiles * un.upt;
-    un.G = (int)std::max<int64_t>(1, std::min<int64_t>(L.ks, un.U));
-    un.small = (un.U + 1) * (int64_t)un.G + un.U < ((int64_t)1 << 32);
+    const Units un = make_units(p.M, p.nb, 1, L.ks);  // nb is a multiple of WK
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     hipLaunchKernelGGL(gemv_q6_kernel, dim3((unsigned)un.G), dim3(64 * WK), 0, stream, p, un);
     Q4K_HIP(hipGetLastError());

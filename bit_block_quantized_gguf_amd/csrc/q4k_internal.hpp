@@ -159,6 +159,15 @@ struct GemmLaunch {
     int r;   // 32-token groups per tile (tile = 256 W rows x 32r tokens)
 };
 GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P);
+
+// Host-side checks of the work partitions (q4k_check_partition): the
+// kernels' own range arithmetic run for every workgroup, against the
+// workspace a launch reserves and the bounds of its operands.  groups or
+// tile_tokens 0: the launch heuristics' choice.
+int check_gemv_partition(int64_t M, int64_t K, int nv, int nmat, int groups);
+int check_gemv_q8_partition(int64_t M, int64_t K, int groups);
+int check_gemv_q6_partition(int64_t M, int64_t K, int groups);
+int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int groups);
 // Workspace: split partials (rounded up to 64 floats) followed by the bf16 copy of X.
 size_t gemm_partial_floats(const GemmLaunch &L, int64_t M, int64_t P);
 size_t gemm_xb_floats(int64_t K, int64_t P);

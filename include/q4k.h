@@ -451,6 +451,25 @@ int q4k_decode_stack_nodes(q4k_stack *s, int64_t *n_nodes);
 void q4k_decode_stack_destroy(q4k_stack *s);
 
 /* ------------------------------------------------------------------------
+ * Self-check of the work partitions (host only, no device needed).
+ * ---------------------------------------------------------------------- */
+
+/* Runs, on the host, the range / owner / cut-tile arithmetic that the
+ * kernels of `op` (Q4K_OP_GEMV, _GEMV_BATCH with N vectors, _MLP with M =
+ * intermediate and K = hidden, _GEMM with P = N tokens, _GEMV_Q8_0,
+ * _GEMV_Q6_K) would receive for an M x K matrix over `workgroups`
+ * workgroups (0: the count the launch heuristics pick; the GEMM tile width
+ * follows q4k_tune_gemm), for every workgroup, and checks that the ranges
+ * cover the work exactly once, that every tile cut between workgroups has
+ * consecutive contributors which all hold part of it, that every partial-sum
+ * slot and arrival counter the kernels index lies inside the workspace
+ * q4k_workspace_size reserves, and that every weight or activation byte a
+ * fetch forms lies inside its operand (with 32-bit lane offsets that do not
+ * wrap).  Q4K_OK, or Q4K_EINVAL naming the first violation in
+ * q4k_last_error; Q4K_ESHAPE for shapes the entry points refuse. */
+int q4k_check_partition(int32_t op, int64_t M, int64_t K, int64_t N, int32_t workgroups);
+
+/* ------------------------------------------------------------------------
  * Launch-shape reporting and benchmark knobs.
  * ---------------------------------------------------------------------- */
 
