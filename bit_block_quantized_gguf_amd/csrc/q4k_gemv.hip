@@ -609,6 +609,181 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
 }
 
 // ---------------------------------------------------------------------------
+// Batched GEMV on the matrix cores (four, eight or sixteen vectors).  Same
+// units, ranges, LDS staging and cut-tile finishing as gemv_kernel: lane l
+// reads row l of the wave's block from LDS and forms each of its 256 weights
+// exactly (one v_fma_mix_f32: d*sc*q - dmin*m).  The products go to
+// v_mfma_f32_4x4x1_16b_f32, sixteen independent 4x4 outer products per
+// instruction: product block b = l / 4 takes the weights of rows 4b .. 4b+3
+// (lane 4b + i supplies row i) and the activations of four vectors at the
+// same column (lane 4b + j supplies vector j), so one instruction applies one
+// column of the 64 rows to four vectors and accumulates W[row][k] * X[vec][k]
+// in f32 (an exact weight times an f32 activation).  Lane 4b + j ends with
+// rows 4b + i (register i) of vector j: no cross-lane reduction is needed.
+// The unit's activations (NV vectors x 1024 columns) are staged in LDS next
+// to its weights, loaded and committed with them; a lane reads them as
+// float4 runs of four columns (four distinct addresses per instruction).
+// Four accumulator chains per 4-vector group (low/high nibbles, even/odd
+// byte) keep consecutive MFMAs independent.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <int NV>
+__global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(const GemvParams p, const Units un) {
+    static_assert(NV == 4 || NV == 8 || NV == 16, "four, eight or sixteen vectors");
+    constexpr int VG = NV / 4;  // 4-vector groups
+    constexpr int XQ = NV;      // float4s of activations per thread per unit
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * SEGP];
+    __shared__ __attribute__((aligned(16))) float xs[NV][256 * WK];
+    __shared__ float red[WK][NV][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x;
+    const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
+
+    int coff[CH_THREAD], crow[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;
+        crow[i] = q / CH_ROW;
+        coff[i] = 16 * (q - crow[i] * CH_ROW);
+    }
+    uint4 reg[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    float4 xreg[XQ];
+    auto fetch = [&](int t, int k) {
+        const int j0 = k * WK;
+        const uint8_t *b0 = p.w0 + (int64_t)t * 64 * p.row_bytes + (int64_t)j0 * kBlockBytes;
+        const int valid = min(WK, p.nb - j0) * kBlockBytes;
+        const int rmax = min(63, p.M - 1 - t * 64);
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i) {
+            const int co = coff[i] < valid ? coff[i] : 0;
+            reg[i] = ldg16(b0 + (uint32_t)min(crow[i], rmax) * (uint32_t)p.row_bytes + (uint32_t)co);
+        }
+        // activations of the unit's columns: float4 q = tid + 256 m is vector
+        // q / 256, columns 4 (q % 256) .. +3 of the unit (zero past K)
+#pragma unroll
+        for (int m = 0; m < XQ; ++m) {
+            const int q = tid + 256 * m;
+            const int col = 256 * j0 + 4 * (q & 255);
+            xreg[m] = col < p.K ? *reinterpret_cast<const float4 *>(
+                                      p.x + (int64_t)(q >> 8) * p.x_stride + col)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i)
+            *reinterpret_cast<uint4 *>(&stage[crow[i] * SEGP + coff[i]]) = reg[i];
+#pragma unroll
+        for (int m = 0; m < XQ; ++m) {
+            const int q = tid + 256 * m;
+            *reinterpret_cast<float4 *>(&xs[q >> 8][4 * (q & 255)]) = xreg[m];
+        }
+    };
+
+    // acc[v][c]: vector group v, chain c (bit 0: high nibbles, bit 1: odd byte)
+    f4v acc[VG][4];
+#pragma unroll
+    for (int v = 0; v < VG; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[v][c] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);
+    fetch(t, k);
+    commit();
+    __syncthreads();
+    bool seg_first = k == 0;
+    for (int64_t u = ua; u < ub; ++u) {
+        const int j = k * WK + wave;
+        const bool last_of_tile = k + 1 == un.upt;
+        const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
+        const bool more = u + 1 < ub;
+        if (more) fetch(tn, kn);
+        if (j < p.nb) {
+            const uint8_t *lp = &stage[lane * SEGP + wave * kBlockBytes];
+            uint4 b[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) b[i] = *reinterpret_cast<const uint4 *>(lp + 16 * i);
+            const float d = half_lo(b[0].x), ndm = -half_hi(b[0].x);
+            const float d24 = d * 16777216.0f, d20 = d * 1048576.0f;
+            const Scales sc = unpack_scales(b[0].y, b[0].z, b[0].w);
+            const float *xr[VG];
+#pragma unroll
+            for (int v = 0; v < VG; ++v) xr[v] = &xs[4 * v + (lane & 3)][256 * wave];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const GroupF f = group_factors(sc, gq, d24, d20, ndm);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const WordQ q = word_unpack(word_of(b[1 + 2 * gq + (i >> 2)], i & 3));
+                    float4 xl[VG], xh[VG];
+#pragma unroll
+                    for (int v = 0; v < VG; ++v) {
+                        xl[v] = *reinterpret_cast<const float4 *>(xr[v] + 64 * gq + 4 * i);
+                        xh[v] = *reinterpret_cast<const float4 *>(xr[v] + 64 * gq + 32 + 4 * i);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const half2v ql = (e & 1) ? q.l13 : q.l02, qh = (e & 1) ? q.h13 : q.h02;
+                        const float wl = fmaf((e & 2) ? (float)ql.y : (float)ql.x, f.al, f.bl);
+                        const float wh = fmaf((e & 2) ? (float)qh.y : (float)qh.x, f.ah, f.bh);
+#pragma unroll
+                        for (int v = 0; v < VG; ++v) {
+                            const float xle = e == 0 ? xl[v].x : e == 1 ? xl[v].y : e == 2 ? xl[v].z : xl[v].w;
+                            const float xhe = e == 0 ? xh[v].x : e == 1 ? xh[v].y : e == 2 ? xh[v].z : xh[v].w;
+                            acc[v][2 * (e & 1)] = __builtin_amdgcn_mfma_f32_4x4x1f32(
+                                wl, xle, acc[v][2 * (e & 1)], 0, 0, 0);
+                            acc[v][2 * (e & 1) + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(
+                                wh, xhe, acc[v][2 * (e & 1) + 1], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        const bool seg_end = !more || last_of_tile;
+        if (seg_end) {
+            // lane 4b + j holds rows 4b + i (register i) of vector 4v + j
+#pragma unroll
+            for (int v = 0; v < VG; ++v) {
+                const f4v s = (acc[v][0] + acc[v][1]) + (acc[v][2] + acc[v][3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    red[wave][4 * v + (lane & 3)][(lane & ~3) + i] = s[i];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[v][c] = f4v{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        __syncthreads();
+        if (seg_end && wave == 0) {
+            float tot[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                float s = red[0][n][lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) s += red[w][n][lane];
+                tot[n] = s;
+            }
+            if (seg_first && last_of_tile)
+                epilogue<NV, 1, EPI_PLAIN>(p, t * 64, lane, tot, 1.f);
+            else
+                finish_split_tile<NV, 1, EPI_PLAIN>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot,
+                                                    1.f);
+        }
+        if (seg_end) seg_first = true;
+        t = tn;
+        k = kn;
+        if (more) commit();
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Persistent decode kernel: the whole per-token chain of GEMV nodes in one
 // launch ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4: one submission per
 // token with the activation resident).  Every workgroup walks the node list;
@@ -1189,13 +1364,23 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
 // slower than 512; on the 715 MB lm_head two per CU took 134.6 us against
 // 138.0 at three and 152.7 at four (interleaved runs).  One tile per
 // workgroup (no cut tiles) was slower still.
+// Four, eight and sixteen plain vectors run on the matrix cores.
+template <int NV, int NMAT, int EPI>
+constexpr bool kMfma = NMAT == 1 && EPI == EPI_PLAIN && (NV == 4 || NV == 8 || NV == 16);
+
+template <int NV, int NMAT, int EPI>
+const void *gemv_fn() {
+    if constexpr (kMfma<NV, NMAT, EPI>) return (const void *)gemv_mfma_kernel<NV>;
+    else return (const void *)gemv_kernel<NV, NMAT, EPI>;
+}
+
 template <int NV, int NMAT, int EPI>
 int groups_for(int64_t M, int64_t K, int *G) {
     int res = 0, cus = 0;
     const int o = g_override_groups.load();
     int64_t g = o;
     if (o <= 0) {
-        int rc = resident_groups((const void *)gemv_kernel<NV, NMAT, EPI>, &res, &cus);
+        int rc = resident_groups(gemv_fn<NV, NMAT, EPI>(), &res, &cus);
         if (rc) return rc;
         g = std::min(res, 2 * cus);
     }
@@ -1222,8 +1407,12 @@ int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     const int64_t tiles = (p.M + ROWS - 1) / ROWS;
     const Units un = make_units(p.M, p.nb, NMAT, L.ks);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
-    hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
-                       stream, p, un);
+    if constexpr (kMfma<NV, NMAT, EPI>)
+        hipLaunchKernelGGL((gemv_mfma_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0, stream,
+                           p, un);
+    else
+        hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
+                           stream, p, un);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }
