@@ -260,6 +260,20 @@ def test_gemm_prefill_sampled(q4k, shape, P):
     _check_gemm(Y, w, X, M, K, rows, toks, "prefill %dx%d P=%d" % (M, K, P))
 
 
+@pytest.mark.parametrize("shape", wl.PREFILL_SHAPES, ids=["17408x5120", "5120x17408"])
+def test_gemm_prefill_every_element(q4k, shape):
+    """P = 256 at full size, every one of the 4.5 million outputs against both
+    references (the oracle computes all of them: 45.6 GFLOP in double, a few
+    seconds on the host threads)."""
+    M, K = shape
+    P = wl.PREFILL_P[0]
+    w = synth.q4k_weight(synth.key(5, wl.PREFILL_SHAPES.index(shape)), M, K)
+    X = synth.activations(5, P, K)
+    note("gemm prefill every element %dx%d P=%d" % (M, K, P))
+    Y = down(q4k.gemm(up(w), up(X), M=M, K=K))
+    _check_gemm(Y, w, X, M, K, None, np.arange(P), "prefill all %dx%d P=%d" % (M, K, P))
+
+
 @pytest.mark.parametrize("P", [1, 16, 22, 27, 64])
 def test_gemm_short_prompt_sampled(q4k, P):
     """Short prompts (the 22- and 27-token prompts among them) on the MLP
