@@ -207,7 +207,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="gemv,batch,small,q8,q6,gemm,stack,cpu",
+    ap.add_argument("--sections", default="gemv,batch,small,q8,q6,gemm,stack,mixers,cpu",
                     help="comma list of gemv,batch,small,gemm,stack,cpu (and copy: the "
                          "256 MiB device copy that calibrates the PMC traffic counters)")
     ap.add_argument("--copies", type=int, default=12, help="cold-rotation copies per MLP matrix")
@@ -646,8 +646,107 @@ def main():
             "wait_timeouts": pst.status()}
         log("persistent stack: %.1f us/token, logits equal to the graph plan's: %s" % (pmed, same))
         pst.close()
+        # the same weights with the real token mixers (GDN step / gated
+        # attention), positions 0 .. tokens-1 from zero states
+        kinds = [1 if wl.is_attention(l) else 0 for l in range(L)]
+        mixers = []
+        for l in range(L):
+            if kinds[l] == 0:
+                C = (2 * 16 + 48) * 128
+                mixers.append({"conv_w": upload((0.5 * synth.normal(synth.key(6, 10 * l), 4 * C)).astype(np.float32)),
+                               "a_log": upload((0.5 * synth.normal(synth.key(6, 10 * l + 1), 48)).astype(np.float32)),
+                               "dt_bias": upload((0.5 * synth.normal(synth.key(6, 10 * l + 2), 48)).astype(np.float32)),
+                               "norm_w": upload((1 + 0.1 * synth.normal(synth.key(6, 10 * l + 3), 128)).astype(np.float32))})
+            else:
+                mixers.append({"q_norm_w": upload((0.2 * synth.normal(synth.key(6, 10 * l + 4), 256)).astype(np.float32)),
+                               "k_norm_w": upload((0.2 * synth.normal(synth.key(6, 10 * l + 5), 256)).astype(np.float32))})
+        ntok = max(args.stack_tokens, 4)
+        mst = q4k.DecodeStack(layers, lm, hidden=wl.HIDDEN, kinds=kinds, mixers=mixers,
+                              attn_capacity=ntok + 8)
+        for _ in range(3):
+            mst(h0, logits)
+        torch.cuda.synchronize()
+        mst.reset()
+        pairs = []
+        for _ in range(ntok):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            mst(h0, logits)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        mmed = float(np.median(ts))
+        state_bytes = 48 * (2 * 48 * 128 * 128 * 4)  # every GDN layer reads and writes its state
+        out["decode_stack_mixers"] = {
+            "us_per_token_median": mmed, "us_per_token_mean": float(np.mean(ts)),
+            "tokens": ntok, "positions": "0..%d" % (ntok - 1), "graph_nodes": mst.nodes(),
+            "bytes_per_token": tot + state_bytes,
+            "roofline_us": (tot + state_bytes) / HBM_PEAK_GBS / 1e3,
+            "frac_roofline": (tot + state_bytes) / HBM_PEAK_GBS / 1e3 / mmed,
+            "logits_finite": bool(torch.isfinite(logits).all())}
+        log("stack with mixers: %.1f us/token" % mmed)
+        mst.close()
         del layers, lm
         torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ token mixers
+    if "mixers" in sections:
+        # One decode step of each mixer at the model's sizes, timed as a
+        # replayed graph of 20 calls (the form it takes inside the decode
+        # graph); bytes are the state (GDN) or the K/V cache (attention) that
+        # one call must read and write.
+        def graph_time(fn, calls=20, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            res = []
+            for _ in range(reps):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) * 1e3 / calls)
+            del g
+            return float(np.median(res))
+
+        Hk, Hv, D = 16, 48, 128
+        C = (2 * Hk + Hv) * D
+        nrm = lambda k, n, sc: upload((sc * synth.normal(synth.key(6, k), n)).astype(np.float32))
+        gu = nrm(100, C + Hv * D + 2 * Hv, 1.0)
+        gp = dict(conv_w=nrm(101, 4 * C, 0.5), a_log=nrm(102, Hv, 0.5), dt_bias=nrm(103, Hv, 0.5),
+                  norm_w=upload((1 + 0.1 * synth.normal(synth.key(6, 104), D)).astype(np.float32)))
+        cs, S = nrm(105, 3 * C, 1.0), nrm(106, Hv * D * D, 0.05)
+        gout = torch.empty(Hv * D, device=dev)
+        gws = q4k.Workspace(q4k.workspace_size(q4k.OP_GDN_STEP, Hk, Hv, 0))
+        t_gdn = graph_time(lambda: q4k.gdn_step(gu, gp["conv_w"], gp["a_log"], gp["dt_bias"],
+                                                gp["norm_w"], cs, S, gout, ws=gws))
+        gdn_bytes = 2 * Hv * D * D * 4 + 2 * 3 * C * 4 + (C + Hv * D + 2 * Hv) * 4 + Hv * D * 4
+        res = {"gdn_step": {"us": t_gdn, "bytes": gdn_bytes, "GBps": gdn_bytes / t_gdn / 1e3,
+                            "frac_hbm": gdn_bytes / t_gdn / 1e3 / HBM_PEAK_GBS,
+                            "kernels": 2, "heads": [Hk, Hv, D]}}
+        Hq, Hkv, AD, cap = 24, 4, 256, 4096
+        au = nrm(110, Hq * 2 * AD + 2 * Hkv * AD, 1.0)
+        qw, kw = nrm(111, AD, 0.2), nrm(112, AD, 0.2)
+        kc = nrm(113, Hkv * cap * AD, 1.0).view(Hkv, cap, AD)
+        vc = nrm(114, Hkv * cap * AD, 1.0).view(Hkv, cap, AD)
+        aout = torch.empty(Hq * AD, device=dev)
+        aws = q4k.Workspace(q4k.workspace_size(q4k.OP_ATTN_STEP, Hq, Hkv, cap))
+        res["attn_step"] = []
+        for pos in (1023, 4095):
+            t_a = graph_time(lambda: q4k.attn_step(au, qw, kw, kc, vc, pos, aout, ws=aws))
+            ab = 2 * Hkv * (pos + 1) * AD * 4 + (Hq * 2 * AD + 2 * Hkv * AD + Hq * AD) * 4
+            res["attn_step"].append({"pos": pos, "us": t_a, "bytes": ab,
+                                     "GBps": ab / t_a / 1e3, "frac_hbm": ab / t_a / 1e3 / HBM_PEAK_GBS})
+        out["mixers"] = res
+        log("mixers: gdn %.2f us, attn %s" % (t_gdn, [(r["pos"], round(r["us"], 2)) for r in res["attn_step"]]))
+        del kc, vc, S
 
     # ------------------------------------------------------------ counter calibration
     if "copy" in sections:

@@ -39,7 +39,8 @@ EXPORTS = (
     "q4k_decode_stack_reset", "q4k_decode_stack_position", "q4k_decode_stack_status",
     "q4k_check_partition",
 )
-OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP = range(7)
+(OP_GEMV, OP_GEMV_BATCH, OP_GEMM, OP_GEMV_Q8_0, OP_GEMV_Q6_K, OP_MLP, OP_GDN_STEP,
+ OP_ATTN_STEP) = range(8)
 
 _lib = None
 
@@ -117,7 +118,7 @@ def load(path: str | None = None):
     L.q4k_gemv_noalloc.restype = ctypes.c_int
     L.q4k_gdn_step.argtypes = [ctypes.POINTER(GdnParams), p, p, p, p, p, sz, p]
     L.q4k_gdn_step.restype = ctypes.c_int
-    L.q4k_attn_step.argtypes = [ctypes.POINTER(AttnParams), p, p, p, i64, i64, p, p]
+    L.q4k_attn_step.argtypes = [ctypes.POINTER(AttnParams), p, p, p, i64, i64, p, p, sz, p]
     L.q4k_attn_step.restype = ctypes.c_int
     L.q4k_gemv_q6_k.argtypes = [p, p, p, i64, i64, p, sz, p]
     L.q4k_decode_stack_create.argtypes = [ctypes.POINTER(StackDesc), p, ctypes.POINTER(p)]
@@ -461,7 +462,7 @@ def gdn_step(u, conv_w, a_log, dt_bias, norm_w, conv_state, state, out=None, key
 
 
 def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos: int, out=None, q_heads=24,
-              kv_heads=4, rope_dim=64, rope_theta: float = 1e7, eps: float = 1e-6):
+              kv_heads=4, rope_dim=64, rope_theta: float = 1e7, eps: float = 1e-6, ws=None):
     """One gated full-attention token at position pos (q4k_attn_step): writes
     position pos of k_cache/v_cache [Hkv, capacity, 256], returns out [Hq*256]."""
     torch = _torch()
@@ -478,10 +479,12 @@ def attn_step(u, q_norm_w, k_norm_w, k_cache, v_cache, pos: int, out=None, q_hea
         out = torch.empty(q_heads * D, dtype=f32, device=u.device)
     _tensor(out, f32, "out", q_heads * D)
     _on_gpu(u=u, q_norm_w=q_norm_w, k_norm_w=k_norm_w, k_cache=k_cache, v_cache=v_cache, out=out)
+    ws = _ws(OP_ATTN_STEP, q_heads, kv_heads, cap, ws)
     prm = AttnParams(q_heads, kv_heads, D, rope_dim, float(rope_theta), float(eps),
                      q_norm_w.data_ptr(), k_norm_w.data_ptr())
     check(load().q4k_attn_step(ctypes.byref(prm), u.data_ptr(), k_cache.data_ptr(),
-                               v_cache.data_ptr(), cap, int(pos), out.data_ptr(), _stream()))
+                               v_cache.data_ptr(), cap, int(pos), out.data_ptr(), ws.ptr,
+                               ws.nbytes, _stream()))
     return out
 
 

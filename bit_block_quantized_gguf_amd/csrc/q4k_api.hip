@@ -201,6 +201,11 @@ size_t gdn_ws_bytes(int Hk, int Hv) {
     return region_bytes((size_t)(2 * Hk + Hv) * 128 + 2 * (size_t)Hv);
 }
 
+// Attention step workspace: [counter region, unused][split-KV partials]
+size_t attn_ws_bytes(int Hq, int Hkv, int64_t cap) {
+    return region_bytes(attn_scratch_floats(Hq, Hkv, cap));
+}
+
 // The caller has checked the workspace against gemv_ws_bytes(M, K, N).
 int gemv_multi(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
                void *wsp, size_t ws_bytes, hipStream_t stream) {
@@ -282,6 +287,14 @@ int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *byte
                 return fail(Q4K_ESHAPE, "gdn: key heads %lld, value heads %lld", (long long)M,
                             (long long)K);
             *bytes = gdn_ws_bytes((int)M, (int)K);
+            return Q4K_OK;
+        case Q4K_OP_ATTN_STEP:
+            if (M <= 0 || K <= 0 || M % K != 0 || M > 65536)
+                return fail(Q4K_ESHAPE, "attention: query heads %lld, kv heads %lld", (long long)M,
+                            (long long)K);
+            if (N <= 0 || N > ((int64_t)1 << 40) / 256 / K)
+                return fail(Q4K_ESHAPE, "attention: capacity %lld", (long long)N);
+            *bytes = attn_ws_bytes((int)M, (int)K, N);
             return Q4K_OK;
         default:
             return fail(Q4K_EINVAL, "unknown op %d", op);
@@ -503,7 +516,8 @@ int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, flo
 }
 
 int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, float *v_cache,
-                  int64_t capacity, int64_t pos, float *out, void *stream) {
+                  int64_t capacity, int64_t pos, float *out, void *ws, size_t ws_bytes,
+                  void *stream) {
     clear_error();
     if (!p) return fail(Q4K_EINVAL, "NULL parameters");
     if (p->head_dim != 256) return fail(Q4K_ESHAPE, "attention: head dimension must be 256");
@@ -525,10 +539,12 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
     Q4K_TRY(check_ptr(out, "out"));
     Q4K_TRY(check_ptr(p->q_norm_w, "q_norm_w"));
     Q4K_TRY(check_ptr(p->k_norm_w, "k_norm_w"));
+    Q4K_TRY(check_ws(ws, ws_bytes, attn_ws_bytes(p->q_heads, p->kv_heads, capacity), "attn_step"));
     Q4K_TRY(check_device());
     AttnShape sh{p->q_heads, p->kv_heads, p->rope_dim, p->rope_theta, p->eps};
+    float *scratch = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
     return launch_attn_step(sh, u, p->q_norm_w, p->k_norm_w, k_cache, v_cache, capacity, pos,
-                            nullptr, out, (hipStream_t)stream);
+                            nullptr, out, scratch, (hipStream_t)stream);
 }
 
 int q4k_check_partition(int32_t op, int64_t M, int64_t K, int64_t N, int32_t workgroups) {

@@ -29,14 +29,16 @@
 //                       contiguous state, and each row's dot products reduce
 //                       over the 32 lanes that hold it.
 // Gated attention step (position pos; u = [per head: q | gate] x Hq, k, v):
-//   attn_step_kernel  — one workgroup per query head: (1 + w) RMSNorm of q
-//                       and of its key/value head's k, rotary on the first R
-//                       dims (angles in double), k and v written to the cache
-//                       at pos by the head's first query head, then an online
-//                       softmax over positions 0..pos (four waves, positions
-//                       t = w mod 4, 4 dims per lane) and the sigmoid gate.
+//   attn_chunk_kernel   — (1 + w) RMSNorm and rotary (first R dims, angles in
+//                         double) of q and k, k and v written to the cache at
+//                         pos, then a split-KV online softmax over chunks of
+//                         positions, each key/value row read once per group
+//                         of query heads that share it;
+//   attn_combine_kernel — merges the chunks per query head, sigmoid gate.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
+
+#include <algorithm>
 
 #include <math.h>
 
@@ -54,6 +56,12 @@ __device__ __forceinline__ float wave_sum64(float v) {
     v += __shfl_xor(v, 4);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 1);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
 
@@ -171,95 +179,301 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const float *__restrict_
 
 constexpr int AD = 256;  // attention head dimension
 
-// (1 + w) RMSNorm and rotary of one 256-vector, one element per thread;
-// returns this thread's element.  buf: 256 floats of LDS, red: 4.
-__device__ __forceinline__ float norm_rope(float x, const float *__restrict__ w, float eps, int R,
-                                           double theta, int64_t pos, float *buf, float *red) {
-    const int d = threadIdx.x;
-    const float ss = block_sum256(x * x, red);
-    const float n = x / sqrtf(ss / (float)AD + eps) * (1.0f + w[d]);
-    buf[d] = n;
-    __syncthreads();
-    float r = n;
-    if (d < R) {
-        const int half = R / 2, i = d < half ? d : d - half;
-        const double ang = (double)pos * pow(theta, -2.0 * i / R);
-        const float cs = (float)cos(ang), sn = (float)sin(ang);
-        r = d < half ? n * cs - buf[d + half] * sn : n * cs + buf[d - half] * sn;
-    }
-    __syncthreads();
-    return r;
-}
+// Split-KV decode attention, two kernels.
+//
+// attn_chunk_kernel: the positions 0..pos are cut into chunks of ACH;
+// workgroup (g, head group, w) takes chunks w, w + nw, ... of key/value head
+// g for up to AHG of the query heads that read it, so every key and value row
+// is read once per head group rather than once per query head.
+//   set-up: (1 + w) RMSNorm and rotary of the group's queries into LDS (the
+//           rotary angles, in double, once per thread for all heads); the
+//           workgroup whose chunks hold pos also forms that position's key
+//           and value (the first head group writes them to the caches) and
+//           uses its own copy wherever the chunk reads row pos, so no other
+//           workgroup depends on that write;
+//   scores: wave v takes the chunk's positions 16v .. 16v+15; one load
+//           instruction covers 8 whole 1 KB key rows (8 lanes per row, 16 B
+//           each) and 16 of them cover the wave's rows; 8-lane sums finish
+//           the dot products;
+//   softmax: wave v keeps the running max and sum of heads v and v + 4
+//           (lane i position i);
+//   values: lane l holds dims 4l .. 4l+3, wave v positions 16v .. 16v+15
+//           (a value row is one 1 KB load), loaded together with the keys;
+//           outputs rescaled whenever the running max moves.
+// It writes (output, max, sum) per head, or nothing if it had no chunk.
+// attn_combine_kernel: one workgroup per query head merges the chunk
+// workgroups in index order and applies the sigmoid gate.  Deterministic:
+// fixed chunk assignment and merge order.
+constexpr int ACH = 64;  // positions per chunk
+constexpr int AHG = 8;   // query heads per chunk workgroup
+constexpr int APS = AD + 4;  // partial record: 256 outputs, max, sum, 2 pad (16 B rows)
 
-__global__ __launch_bounds__(256) void attn_step_kernel(
+__global__ __launch_bounds__(256) void attn_chunk_kernel(
     const float *__restrict__ u, const float *__restrict__ qw, const float *__restrict__ kw,
     float *__restrict__ kc, float *__restrict__ vc, int64_t cap, int64_t pos_val,
-    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int R, float theta, float eps,
-    float *__restrict__ out) {
-    __shared__ float qs[AD], ks[AD], buf[AD];
-    __shared__ float red[4];
-    __shared__ float wm[4], wl[4];
-    __shared__ float wacc[4][AD];
-    const int h = blockIdx.x, d = threadIdx.x;
-    const int g = h / (Hq / Hkv);
+    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int R, float theta, float eps, int nw,
+    float *__restrict__ part) {
+    __shared__ __attribute__((aligned(16))) float qs[AHG][AD];
+    __shared__ __attribute__((aligned(16))) float kn[AD];
+    __shared__ __attribute__((aligned(16))) float vn[AD];
+    __shared__ float sc[AHG][ACH];
+    __shared__ float pr[AHG][ACH];
+    __shared__ float red[AHG + 1][4];
+    __shared__ float ms[AHG], ls[AHG], rs[AHG];
+    __shared__ __attribute__((aligned(16))) float oacc[4][AHG][AD];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
+    const int wi = blockIdx.x % nw, gg = blockIdx.x / nw;  // gg = g * hg + head group
+    const int g = gg / hg, hgi = gg % hg;
+    const int h0 = g * rep + hgi * AHG, nh = min(AHG, rep - hgi * AHG);
     const int64_t pos = pos_dev ? *pos_dev : pos_val;
     if (pos < 0 || pos >= cap) return;  // the callers keep pos inside the cache
-    const float *uq = u + (int64_t)h * 2 * AD;
-    const float *uk = u + (int64_t)Hq * 2 * AD + (int64_t)g * AD;
-    const float *uv = u + (int64_t)Hq * 2 * AD + (int64_t)Hkv * AD + (int64_t)g * AD;
-    const float gate = uq[AD + d];
-    qs[d] = norm_rope(uq[d], qw, eps, R, (double)theta, pos, buf, red);
-    const float kn = norm_rope(uk[d], kw, eps, R, (double)theta, pos, buf, red);
-    const float vn = uv[d];
-    ks[d] = kn;
-    if (h % (Hq / Hkv) == 0) {  // the key/value head's first query head fills the cache
-        kc[((int64_t)g * cap + pos) * AD + d] = kn;
-        vc[((int64_t)g * cap + pos) * AD + d] = vn;
-    }
-    __shared__ float vs[AD];
-    vs[d] = vn;
-    __syncthreads();
-    // online softmax over positions t = w mod 4 (position pos from LDS)
-    const int w = d >> 6, lane = d & 63;
-    const float4 q4 = *reinterpret_cast<const float4 *>(&qs[4 * lane]);
-    const float scale = 1.0f / sqrtf((float)AD);
-    float m = -INFINITY, l = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t nchunks = pos / ACH + 1, cpos = pos / ACH;
+    if (wi >= nchunks) return;  // no chunk: the merge reads min(nw, nchunks) partials
+    const bool own_pos = cpos % nw == wi;
+
     const float *kg = kc + (int64_t)g * cap * AD, *vg = vc + (int64_t)g * cap * AD;
-    for (int64_t t = w; t <= pos; t += 4) {
-        const float4 k4 = t == pos ? *reinterpret_cast<const float4 *>(&ks[4 * lane])
-                                   : *reinterpret_cast<const float4 *>(kg + t * AD + 4 * lane);
-        const float4 v4 = t == pos ? *reinterpret_cast<const float4 *>(&vs[4 * lane])
-                                   : *reinterpret_cast<const float4 *>(vg + t * AD + 4 * lane);
-        float s = fmaf(q4.x, k4.x, fmaf(q4.y, k4.y, fmaf(q4.z, k4.z, q4.w * k4.w)));
-        s = wave_sum64(s) * scale;
-        const float mn = fmaxf(m, s);
-        const float c = expf(m - mn), e = expf(s - mn);
-        l = fmaf(l, c, e);
-        acc.x = fmaf(acc.x, c, e * v4.x);
-        acc.y = fmaf(acc.y, c, e * v4.y);
-        acc.z = fmaf(acc.z, c, e * v4.z);
-        acc.w = fmaf(acc.w, c, e * v4.w);
-        m = mn;
+    const int sub = lane & 7, rsub = lane >> 3;  // 16 B piece, row within 8
+    // every key and value load of the wave's 16 rows of chunk c: key row
+    // tw + 8 (j & 1) + rsub, dims 32 (j >> 1) + 4 sub .. +3; value row tw + i,
+    // dims 4 lane .. +3 (rows past pos read row pos, replaced below)
+    float4 k4[16], v4[16];
+    auto issue = [&](int64_t c) {
+        const int64_t tw = c * ACH + 16 * wv;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t t = tw + 8 * (j & 1) + rsub;
+            k4[j] = *reinterpret_cast<const float4 *>(kg + min(t, pos) * AD + 32 * (j >> 1) +
+                                                      4 * sub);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v4[i] = *reinterpret_cast<const float4 *>(vg + min(tw + i, pos) * AD + 4 * lane);
+    };
+    issue(wi);  // the first chunk's loads fly during the set-up
+
+    // ---- set-up: normed, rotated queries (and key, value at pos)
+    {
+        const int d = tid;
+        float cs = 1.f, sn = 0.f;
+        const int half = R / 2;
+        if (d < R) {
+            const int i = d < half ? d : d - half;
+            const double ang = (double)pos * pow((double)theta, -2.0 * i / R);
+            cs = (float)cos(ang);
+            sn = (float)sin(ang);
+        }
+        const int64_t ko = (int64_t)Hq * 2 * AD + (int64_t)g * AD;
+        const int64_t vo = (int64_t)Hq * 2 * AD + (int64_t)Hkv * AD + (int64_t)g * AD;
+        float x[AHG + 1];
+#pragma unroll
+        for (int hh = 0; hh < AHG; ++hh) x[hh] = hh < nh ? u[(int64_t)(h0 + hh) * 2 * AD + d] : 0.f;
+        x[AHG] = own_pos ? u[ko + d] : 0.f;
+#pragma unroll
+        for (int hh = 0; hh <= AHG; ++hh) {
+            const float ssq = wave_sum64(x[hh] * x[hh]);
+            if (lane == 0) red[hh][wv] = ssq;
+        }
+        __syncthreads();
+        float n[AHG + 1];
+#pragma unroll
+        for (int hh = 0; hh <= AHG; ++hh) {
+            const float ss = (red[hh][0] + red[hh][1]) + (red[hh][2] + red[hh][3]);
+            const float wgt = hh < AHG ? qw[d] : kw[d];
+            n[hh] = x[hh] / sqrtf(ss / (float)AD + eps) * (1.0f + wgt);
+            if (hh < AHG) qs[hh][d] = n[hh];
+            else kn[d] = n[hh];
+        }
+        __syncthreads();
+        float r[AHG + 1];
+#pragma unroll
+        for (int hh = 0; hh <= AHG; ++hh) {
+            const float *row = hh < AHG ? qs[hh] : kn;
+            r[hh] = n[hh];
+            if (d < R) r[hh] = d < half ? n[hh] * cs - row[d + half] * sn
+                                        : n[hh] * cs + row[d - half] * sn;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hh = 0; hh < AHG; ++hh) qs[hh][d] = r[hh];
+        if (own_pos) {
+            const float v = u[vo + d];
+            kn[d] = r[AHG];
+            vn[d] = v;
+            if (hgi == 0) {
+                kc[((int64_t)g * cap + pos) * AD + d] = r[AHG];
+                vc[((int64_t)g * cap + pos) * AD + d] = v;
+            }
+        }
+        if (tid < AHG) {
+            ms[tid] = -INFINITY;
+            ls[tid] = 0.f;
+        }
+        __syncthreads();
     }
-    if (lane == 0) {
-        wm[w] = m;
-        wl[w] = l;
+
+    float o[AHG][4];
+#pragma unroll
+    for (int hh = 0; hh < AHG; ++hh) o[hh][0] = o[hh][1] = o[hh][2] = o[hh][3] = 0.f;
+    const float scale = 1.0f / sqrtf((float)AD);
+    for (int64_t c = wi;;) {
+        const int64_t tw = c * ACH + 16 * wv;  // this wave's first position
+        // rows at or past pos: the key and value formed above (past pos the
+        // score is masked and the weight is zero, so they only have to be finite)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t t = tw + 8 * (j & 1) + rsub;
+            if (t >= pos) k4[j] = *reinterpret_cast<const float4 *>(&kn[32 * (j >> 1) + 4 * sub]);
+        }
+        // scores: lane (rsub, sub) sums dims 32 m + 4 sub .. +3 (m = 0..7) of
+        // rows tw + rsub and tw + 8 + rsub, then 8-lane sums
+#pragma unroll
+        for (int hh = 0; hh < AHG; ++hh) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 q4 = *reinterpret_cast<const float4 *>(&qs[hh][32 * m + 4 * sub]);
+                const float4 ka = k4[2 * m], kb = k4[2 * m + 1];
+                a0 = fmaf(q4.x, ka.x, fmaf(q4.y, ka.y, fmaf(q4.z, ka.z, fmaf(q4.w, ka.w, a0))));
+                a1 = fmaf(q4.x, kb.x, fmaf(q4.y, kb.y, fmaf(q4.z, kb.z, fmaf(q4.w, kb.w, a1))));
+            }
+            a0 += __shfl_xor(a0, 4);
+            a1 += __shfl_xor(a1, 4);
+            a0 += __shfl_xor(a0, 2);
+            a1 += __shfl_xor(a1, 2);
+            a0 += __shfl_xor(a0, 1);
+            a1 += __shfl_xor(a1, 1);
+            if (sub == 0) {
+                sc[hh][16 * wv + rsub] = a0;
+                sc[hh][16 * wv + 8 + rsub] = a1;
+            }
+        }
+        __syncthreads();
+        // online softmax: wave wv takes heads wv and wv + 4, lane = position
+        const int64_t t0 = c * ACH;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int hh = wv + 4 * k2;
+            if (hh < nh) {
+                const bool ok = t0 + lane <= pos;
+                const float s = ok ? sc[hh][lane] * scale : -INFINITY;
+                const float mo = ms[hh];
+                const float mn = fmaxf(mo, wave_max64(s));
+                const float pv = ok ? expf(s - mn) : 0.f;
+                const float ssum = wave_sum64(pv);
+                pr[hh][lane] = pv;
+                if (lane == 0) {
+                    const float rr = expf(mo - mn);  // 0 while nothing was seen (mo = -inf)
+                    rs[hh] = rr;
+                    ms[hh] = mn;
+                    ls[hh] = fmaf(ls[hh], rr, ssum);
+                }
+            } else {
+                pr[hh][lane] = 0.f;
+                if (lane == 0) rs[hh] = 1.f;
+            }
+        }
+        __syncthreads();
+        // values: rescale, then add this wave's 16 rows
+        if (tw + 15 >= pos) {
+            const float4 vp = *reinterpret_cast<const float4 *>(&vn[4 * lane]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (tw + i >= pos) v4[i] = vp;
+        }
+#pragma unroll
+        for (int hh = 0; hh < AHG; ++hh) {
+            const float rr = rs[hh];
+            o[hh][0] *= rr;
+            o[hh][1] *= rr;
+            o[hh][2] *= rr;
+            o[hh][3] *= rr;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = pr[hh][16 * wv + i];
+                o[hh][0] = fmaf(pv, v4[i].x, o[hh][0]);
+                o[hh][1] = fmaf(pv, v4[i].y, o[hh][1]);
+                o[hh][2] = fmaf(pv, v4[i].z, o[hh][2]);
+                o[hh][3] = fmaf(pv, v4[i].w, o[hh][3]);
+            }
+        }
+        __syncthreads();  // sc, pr and rs are rewritten by the next chunk
+        c += nw;
+        if (c >= nchunks) break;
+        issue(c);
     }
-    *reinterpret_cast<float4 *>(&wacc[w][4 * lane]) = acc;
+    // the four waves' outputs, then (output, max, sum) per head
+#pragma unroll
+    for (int hh = 0; hh < AHG; ++hh)
+        *reinterpret_cast<float4 *>(&oacc[wv][hh][4 * lane]) =
+            make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
     __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) M = fmaxf(M, wm[i]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (wm[i] == -INFINITY) continue;  // a wave that saw no position
-        const float c = expf(wm[i] - M);
-        num = fmaf(wacc[i][d], c, num);
-        den = fmaf(wl[i], c, den);
+    float *pw = part + (int64_t)blockIdx.x * AHG * APS;
+    for (int hh = 0; hh < nh; ++hh) {
+        pw[hh * APS + tid] = (oacc[0][hh][tid] + oacc[1][hh][tid]) +
+                             (oacc[2][hh][tid] + oacc[3][hh][tid]);
+        if (tid == 0) {
+            pw[hh * APS + AD] = ms[hh];
+            pw[hh * APS + AD + 1] = ls[hh];
+        }
     }
-    out[(int64_t)h * AD + d] = num / den * sigmoidf_(gate);
+}
+
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    const float *__restrict__ u, const float *__restrict__ part, int64_t cap, int64_t pos_val,
+    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int nw, float *__restrict__ out) {
+    __shared__ float cw[64];
+    __shared__ float den_s;
+    __shared__ __attribute__((aligned(16))) float acc[4][AD];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t pos = pos_dev ? *pos_dev : pos_val;
+    if (pos < 0 || pos >= cap) return;
+    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
+    const int g = h / rep, hr = h - g * rep, hgi = hr / AHG, hh = hr - hgi * AHG;
+    const int nact = (int)min<int64_t>(nw, pos / ACH + 1);  // nw <= 64
+    const float *pb = part + ((int64_t)(g * hg + hgi) * nw * AHG + hh) * APS;
+    const int64_t stride = (int64_t)AHG * APS;  // one chunk workgroup
+    // outputs first: wave wv loads chunk workgroups wv, wv + 4, ... (lane l
+    // dims 4l .. 4l+3), all loads in flight together
+    float4 ov[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int w = wv + 4 * i;
+        ov[i] = w < nact ? *reinterpret_cast<const float4 *>(pb + w * stride + 4 * lane)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // merge weights exp(m_w - M) and the denominator, lane w of wave 0
+    if (wv == 0) {
+        const bool ok = lane < nact;
+        const float m = ok ? pb[lane * stride + AD] : -INFINITY;
+        const float l = ok ? pb[lane * stride + AD + 1] : 0.f;
+        const float M = wave_max64(m);
+        const float c = ok ? expf(m - M) : 0.f;
+        cw[lane] = c;
+        const float den = wave_sum64(c * l);
+        if (lane == 0) den_s = den;
+    }
+    __syncthreads();
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int w = wv + 4 * i;
+        if (w < nact) {
+            const float c = cw[w];
+            a.x = fmaf(c, ov[i].x, a.x);
+            a.y = fmaf(c, ov[i].y, a.y);
+            a.z = fmaf(c, ov[i].z, a.z);
+            a.w = fmaf(c, ov[i].w, a.w);
+        }
+    }
+    *reinterpret_cast<float4 *>(&acc[wv][4 * lane]) = a;
+    __syncthreads();
+    const int d = tid;
+    const float num = (acc[0][d] + acc[1][d]) + (acc[2][d] + acc[3][d]);
+    const float gate = u[(int64_t)h * 2 * AD + AD + d];
+    out[(int64_t)h * AD + d] = num / den_s * sigmoidf_(gate);
 }
 
 }  // namespace
@@ -278,12 +492,28 @@ int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, cons
     return Q4K_OK;
 }
 
+size_t attn_chunk_groups(int Hq, int Hkv, int64_t cap) {
+    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
+    const int64_t nw = std::max<int64_t>(1, std::min<int64_t>(64, (cap + ACH - 1) / ACH));
+    return (size_t)Hkv * hg * nw;
+}
+
+size_t attn_scratch_floats(int Hq, int Hkv, int64_t cap) {
+    return attn_chunk_groups(Hq, Hkv, cap) * AHG * APS;
+}
+
 int launch_attn_step(const AttnShape &s, const float *u, const float *q_norm_w,
                      const float *k_norm_w, float *k_cache, float *v_cache, int64_t cap,
-                     int64_t pos, const int64_t *pos_dev, float *out, hipStream_t stream) {
-    hipLaunchKernelGGL(attn_step_kernel, dim3((unsigned)s.Hq), dim3(256), 0, stream, u, q_norm_w,
-                       k_norm_w, k_cache, v_cache, cap, pos, pos_dev, s.Hq, s.Hkv, s.R, s.theta,
-                       s.eps, out);
+                     int64_t pos, const int64_t *pos_dev, float *out, float *scratch,
+                     hipStream_t stream) {
+    const int rep = s.Hq / s.Hkv, hg = (rep + AHG - 1) / AHG;
+    const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(64, (cap + ACH - 1) / ACH));
+    hipLaunchKernelGGL(attn_chunk_kernel, dim3((unsigned)(s.Hkv * hg * nw)), dim3(256), 0, stream,
+                       u, q_norm_w, k_norm_w, k_cache, v_cache, cap, pos, pos_dev, s.Hq, s.Hkv,
+                       s.R, s.theta, s.eps, nw, scratch);
+    Q4K_HIP(hipGetLastError());
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)s.Hq), dim3(256), 0, stream, u, scratch,
+                       cap, pos, pos_dev, s.Hq, s.Hkv, nw, out);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }

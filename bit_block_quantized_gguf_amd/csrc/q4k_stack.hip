@@ -65,7 +65,7 @@ struct q4k_stack {
     float *states = nullptr;          // every layer's conv state, S or K/V caches
     size_t state_floats = 0;
     std::vector<int64_t> st_a, st_b;  // per layer: conv state / K cache, S / V cache
-    float *mix_scratch = nullptr;     // GDN conv outputs and gates
+    float *mix_scratch = nullptr;     // GDN conv outputs and gates; attention partials
     int64_t *pos_dev = nullptr;       // device-side position
     int64_t host_pos = 0;             // tokens launched since creation or reset
     // persistent plan
@@ -205,9 +205,9 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint
                                    m.attn.rope_theta, m.attn.eps};
                 if ((rc = launch_attn_step(sh, A + s->off_u[l], m.attn.q_norm_w, m.attn.k_norm_w,
                                            s->states + s->st_a[l], s->states + s->st_b[l], s->cap,
-                                           0, s->pos_dev, o, cs)))
+                                           0, s->pos_dev, o, s->mix_scratch, cs)))
                     return rc;
-                ++n;
+                n += 3;
             }
             if ((rc = launch_sumsq(o, L.mix_out.K, SQ + s->sq_o[l], cs))) return rc;
             ++n;
@@ -409,9 +409,11 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
             s->st_b.push_back(take(sto, (int64_t)g.value_heads * MD * MD));
             scratch = std::max(scratch, (size_t)(C + 2 * g.value_heads));
         } else if (mixers) {
-            const int64_t n = (int64_t)s->mix[l].attn.kv_heads * s->cap * AHD;
+            const q4k_attn_params &a = s->mix[l].attn;
+            const int64_t n = (int64_t)a.kv_heads * s->cap * AHD;
             s->st_a.push_back(take(sto, n));
             s->st_b.push_back(take(sto, n));
+            scratch = std::max(scratch, attn_scratch_floats(a.q_heads, a.kv_heads, s->cap));
         } else {
             s->st_a.push_back(-1);
             s->st_b.push_back(-1);

@@ -126,13 +126,14 @@ int q4k_dequant(const void *w, float *out, int64_t M, int64_t K, void *stream);
  *   Q4K_OP_GEMV_BATCH: M x K matrix, N vectors;
  *   Q4K_OP_GEMM: M x K matrix, P = N tokens;
  *   Q4K_OP_MLP: M = inter, K = hidden (N ignored);
- *   Q4K_OP_GDN_STEP: M = key heads, K = value heads (N ignored).
+ *   Q4K_OP_GDN_STEP: M = key heads, K = value heads (N ignored);
+ *   Q4K_OP_ATTN_STEP: M = query heads, K = kv heads, N = cache capacity.
  * Writes *bytes (a multiple of 256, possibly 0).  Errors: Q4K_EINVAL for an
  * unknown op or NULL bytes, and the shape errors of the call itself.
  */
 enum {
     Q4K_OP_GEMV = 0, Q4K_OP_GEMV_BATCH = 1, Q4K_OP_GEMM = 2, Q4K_OP_GEMV_Q8_0 = 3,
-    Q4K_OP_GEMV_Q6_K = 4, Q4K_OP_MLP = 5, Q4K_OP_GDN_STEP = 6
+    Q4K_OP_GEMV_Q6_K = 4, Q4K_OP_MLP = 5, Q4K_OP_GDN_STEP = 6, Q4K_OP_ATTN_STEP = 7
 };
 int q4k_workspace_size(int32_t op, int64_t M, int64_t K, int64_t N, size_t *bytes);
 
@@ -302,16 +303,21 @@ int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, flo
  * rope_dim dims (pairs i, i + rope_dim/2; angle pos * theta^(-2i/rope_dim));
  * query head h attends with key/value head h / (Hq/Hkv):
  * out_h = softmax(q . k_t / 16) v over t = 0..pos, times sigmoid(gate_h).
- * Needs no workspace.  Errors: Q4K_EINVAL (NULL), Q4K_ESHAPE (head_dim not
- * 256, Hq not a multiple of Hkv, rope_dim odd or above 256, pos outside
- * 0..capacity-1), Q4K_EALIGN. */
+ * Split-KV: the positions are cut into chunks of 64 spread over up to 64
+ * workgroups per (kv head, group of 8 query heads), each key and value row
+ * read once per group, then merged per query head in a fixed order.
+ * Workspace: q4k_workspace_size(Q4K_OP_ATTN_STEP, Hq, Hkv, capacity)
+ * (per-chunk partials).  Errors: Q4K_EINVAL (NULL,
+ * small workspace), Q4K_ESHAPE (head_dim not 256, Hq not a multiple of Hkv,
+ * rope_dim odd or above 256, pos outside 0..capacity-1), Q4K_EALIGN. */
 typedef struct {
     int32_t q_heads, kv_heads, head_dim, rope_dim; /* head_dim must be 256 */
     float rope_theta, eps;                          /* e.g. 1e7, 1e-6 */
     const float *q_norm_w, *k_norm_w;
 } q4k_attn_params;
 int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, float *v_cache,
-                  int64_t capacity, int64_t pos, float *out, void *stream);
+                  int64_t capacity, int64_t pos, float *out, void *ws, size_t ws_bytes,
+                  void *stream);
 
 /* ------------------------------------------------------------------------
  * Decode stack: the per-token chain of projection and MLP GEMVs of a

@@ -328,16 +328,29 @@ def test_gdn_step_validation(lib):
 def test_attn_step_validation(lib):
     ok = dict(q_heads=24, kv_heads=4, head_dim=256, rope_dim=64, rope_theta=1e7, eps=1e-6,
               q_norm_w=P, k_norm_w=P)
+    need = q4k.workspace_size(q4k.OP_ATTN_STEP, 24, 4, 64)
+    # one partial (256 outputs, max, sum) per head slot of every chunk
+    # workgroup: 4 kv heads x 8 query-head slots at one chunk (capacity 64)
+    assert need >= 4 * 8 * 258 * 4
+    # the split-KV partials grow with the capacity until 64 chunk workgroups
+    assert q4k.workspace_size(q4k.OP_ATTN_STEP, 24, 4, 4096) > need
+    assert (q4k.workspace_size(q4k.OP_ATTN_STEP, 24, 4, 4096)
+            == q4k.workspace_size(q4k.OP_ATTN_STEP, 24, 4, 1 << 20))
+    for M, K, N in ((25, 4, 64), (24, 0, 64), (24, 4, 0)):
+        with pytest.raises(q4k.Q4KError):
+            q4k.workspace_size(q4k.OP_ATTN_STEP, M, K, N)
 
-    def call(cap=64, pos=3, u=P, kc=P, **kw):
+    def call(cap=64, pos=3, u=P, kc=P, ws=WS, nbytes=need, **kw):
         prm = q4k.AttnParams(**dict(ok, **kw))
-        return lib.q4k_attn_step(ctypes.byref(prm), u, kc, P, cap, pos, P, None)
+        return lib.q4k_attn_step(ctypes.byref(prm), u, kc, P, cap, pos, P, ws, nbytes, None)
 
-    assert lib.q4k_attn_step(None, P, P, P, 64, 0, P, None) == -1
+    assert lib.q4k_attn_step(None, P, P, P, 64, 0, P, WS, need, None) == -1
     for kw, code in (({"head_dim": 128}, -2), ({"q_heads": 25}, -2), ({"kv_heads": 0}, -2),
                      ({"rope_dim": 63}, -2), ({"rope_dim": 258}, -2), ({"pos": 64}, -2),
                      ({"pos": -1}, -2), ({"cap": 0}, -2), ({"rope_theta": 0.0}, -1),
-                     ({"u": None}, -1), ({"kc": P + 4}, -3), ({"q_norm_w": None}, -1)):
+                     ({"u": None}, -1), ({"kc": P + 4}, -3), ({"q_norm_w": None}, -1),
+                     ({"ws": None}, -1), ({"nbytes": need - 256}, -1), ({"ws": WS + 16}, -3),
+                     ({"cap": 4096, "pos": 5}, -1)):
         assert call(**kw) == code, kw
         assert lib.q4k_last_error()
     assert call() not in (-1, -2, -3)

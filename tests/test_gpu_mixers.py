@@ -166,3 +166,44 @@ def test_attn_deterministic(q4k, torch):
             o = q4k.attn_step(u, up(prm["qw"]), up(prm["kw"]), kc, vc, pos)
         outs.append(down(o).copy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("pos", [63, 64, 4160, 8199])
+def test_attn_split_kv_chunks(q4k, torch, pos):
+    """Capacity 8200 gives 64 chunk workgroups over up to 129 chunks of 64
+    positions: one partial chunk (63), a chunk of one position (64), two
+    chunks for the first workgroups (4160), three with a ragged tail (8199)."""
+    prm = _attn_params()
+    cap = 8200
+    kc_h = _n(600, Hkv * cap * AD).reshape(Hkv, cap, AD)
+    vc_h = _n(601, Hkv * cap * AD).reshape(Hkv, cap, AD)
+    kc, vc = up(kc_h), up(vc_h)
+    u = _n(602 + pos, NA)
+    note("attention split-KV at position %d of %d" % (pos, cap))
+    out = down(q4k.attn_step(up(u), up(prm["qw"]), up(prm["kw"]), kc, vc, pos))
+    ref, kc_ref, vc_ref = oracle.attn_step(u, prm["qw"], prm["kw"], kc_h, vc_h, pos)
+    _heads(out, ref, Hq, 2e-4, "attn out pos %d" % pos)
+    _close(down(kc)[:, pos], kc_ref[:, pos], 2e-5, "k cache pos %d" % pos)
+    assert np.array_equal(down(vc)[:, pos], vc_ref[:, pos].astype(np.float32))
+    # rows other than pos are untouched
+    kd = down(kc)
+    assert np.array_equal(np.delete(kd, pos, axis=1),
+                          np.delete(kc_h.astype(np.float32), pos, axis=1))
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2), (40, 2)])
+def test_attn_head_groups(q4k, torch, hq, hkv):
+    """Query heads per key/value head of 1, exactly one group of 8, and 20
+    (groups of 8, 8 and 4)."""
+    prm = _attn_params()
+    cap, pos = 330, 321
+    na = hq * 2 * AD + 2 * hkv * AD
+    kc_h = _n(700, hkv * cap * AD).reshape(hkv, cap, AD)
+    vc_h = _n(701, hkv * cap * AD).reshape(hkv, cap, AD)
+    kc, vc = up(kc_h), up(vc_h)
+    u = _n(702, na)
+    note("attention %d query heads over %d kv heads" % (hq, hkv))
+    out = down(q4k.attn_step(up(u), up(prm["qw"]), up(prm["kw"]), kc, vc, pos, q_heads=hq,
+                             kv_heads=hkv))
+    ref, _, _ = oracle.attn_step(u, prm["qw"], prm["kw"], kc_h, vc_h, pos, Hq=hq, Hkv=hkv)
+    _heads(out, ref, hq, 2e-4, "attn out %dx%d" % (hq, hkv))
