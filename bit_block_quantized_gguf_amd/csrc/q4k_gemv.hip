@@ -784,6 +784,198 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(const GemvParams p, 
 }
 
 // ---------------------------------------------------------------------------
+// Batched GEMV for sixteen vectors on v_mfma_f32_16x16x4_f32: one
+// instruction takes 16 rows x 4 columns of W against 4 columns x 16 vectors
+// of X (1,024 multiply-adds in 32 cycles, the rate of four 4x4x1
+// instructions), so each weight formed in a lane feeds one instruction.
+// Same units, staging, ranges and cut-tile finishing as
+// gemv_mfma_kernel.  Wave w computes block w of the unit for the 64 rows as
+// four row groups of 16; lane l = 16 kk + r supplies row r of a group (A)
+// and vector r (B, vector r mod NV when NV < 16: those output columns are
+// never read) at column offset kk:
+//   * it reads quant dwords 2 kk and 2 kk + 1 of each 32-byte group of its
+//     row (one 8-byte LDS read), so the four column offsets of one MFMA are
+//     8 kk + 4 i + e (i = 0, 1; e = byte), and the activations as float4
+//     runs at those offsets;
+//   * each weight is formed exactly (one v_fma_mix_f32, as in gemv_kernel)
+//     from the row's scale and min, which the lane unpacks itself for each
+//     of its four rows;
+//   * lane 16 kk + j ends with rows 4 kk + r (register r) of each group for
+//     vector j; two accumulator chains per group (low and high nibbles).
+template <int NV>
+__global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p,
+                                                               const Units un) {
+    static_assert(NV == 4 || NV == 8 || NV == 16, "four, eight or sixteen vectors");
+    constexpr int XQ = NV;  // float4s of activations per thread per unit
+    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * SEGP];
+    __shared__ __attribute__((aligned(16))) float xs[NV][256 * WK];
+    __shared__ float red[WK][NV][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x;
+    const int64_t ua = un.begin(g), ub = un.begin(g + 1);
+    if (ua >= ub) return;
+    const int first_tile = un.small ? (int)((uint32_t)ua / (uint32_t)un.upt) : (int)(ua / un.upt);
+
+    int coff[CH_THREAD], crow[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) {
+        const int q = i * 64 * WK + tid;
+        crow[i] = q / CH_ROW;
+        coff[i] = 16 * (q - crow[i] * CH_ROW);
+    }
+    uint4 reg[CH_THREAD];
+#pragma unroll
+    for (int i = 0; i < CH_THREAD; ++i) reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    float4 xreg[XQ];
+    auto fetch = [&](int t, int k) {
+        const int j0 = k * WK;
+        const uint8_t *b0 = p.w0 + (int64_t)t * 64 * p.row_bytes + (int64_t)j0 * kBlockBytes;
+        const int valid = min(WK, p.nb - j0) * kBlockBytes;
+        const int rmax = min(63, p.M - 1 - t * 64);
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i) {
+            const int co = coff[i] < valid ? coff[i] : 0;
+            reg[i] = ldg16(b0 + (uint32_t)min(crow[i], rmax) * (uint32_t)p.row_bytes + (uint32_t)co);
+        }
+        // activations of the unit's columns: float4 q = tid + 256 m is vector
+        // q / 256, columns 4 (q % 256) .. +3 of the unit (zero past K)
+#pragma unroll
+        for (int m = 0; m < XQ; ++m) {
+            const int q = tid + 256 * m;
+            const int col = 256 * j0 + 4 * (q & 255);
+            xreg[m] = col < p.K ? *reinterpret_cast<const float4 *>(
+                                      p.x + (int64_t)(q >> 8) * p.x_stride + col)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < CH_THREAD; ++i)
+            *reinterpret_cast<uint4 *>(&stage[crow[i] * SEGP + coff[i]]) = reg[i];
+#pragma unroll
+        for (int m = 0; m < XQ; ++m) {
+            const int q = tid + 256 * m;
+            *reinterpret_cast<float4 *>(&xs[q >> 8][4 * (q & 255)]) = xreg[m];
+        }
+    };
+
+    const int r16 = lane & 15, kk = lane >> 4;
+    f4v acc[4][2];  // row group, low / high nibbles
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    int t = first_tile, k = (int)(ua - (int64_t)first_tile * un.upt);
+    fetch(t, k);
+    commit();
+    __syncthreads();
+    bool seg_first = k == 0;
+    for (int64_t u = ua; u < ub; ++u) {
+        const int j = k * WK + wave;
+        const bool last_of_tile = k + 1 == un.upt;
+        const int tn = last_of_tile ? t + 1 : t, kn = last_of_tile ? 0 : k + 1;
+        const bool more = u + 1 < ub;
+        if (more) fetch(tn, kn);
+        if (j < p.nb) {
+            // the scale and min of this lane's row in each row group
+            const uint8_t *blk = &stage[r16 * SEGP + wave * kBlockBytes];
+            Scales sc[4];
+            float d24[4], d20[4], ndm[4];
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const uint4 h = *reinterpret_cast<const uint4 *>(blk + 16 * rg * SEGP);
+                const float d = half_lo(h.x);
+                ndm[rg] = -half_hi(h.x);
+                d24[rg] = d * 16777216.0f;
+                d20[rg] = d * 1048576.0f;
+                sc[rg] = unpack_scales(h.y, h.z, h.w);
+            }
+            const float *xrow = &xs[r16 % NV][256 * wave + 8 * kk];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                float4 xv[2][2];  // [dword i][low / high nibbles]
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        xv[i][hf] = *reinterpret_cast<const float4 *>(xrow + 64 * gq + 32 * hf + 4 * i);
+                GroupF f[4];
+                uint2 qd[4];
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    f[rg] = group_factors(sc[rg], gq, d24[rg], d20[rg], ndm[rg]);
+                    qd[rg] = *reinterpret_cast<const uint2 *>(blk + 16 * rg * SEGP + 16 + 32 * gq +
+                                                              8 * kk);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    WordQ q[4];
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) q[rg] = word_unpack(i ? qd[rg].y : qd[rg].x);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float xle = e == 0 ? xv[i][0].x : e == 1 ? xv[i][0].y
+                                        : e == 2 ? xv[i][0].z : xv[i][0].w;
+                        const float xhe = e == 0 ? xv[i][1].x : e == 1 ? xv[i][1].y
+                                        : e == 2 ? xv[i][1].z : xv[i][1].w;
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const half2v ql = (e & 1) ? q[rg].l13 : q[rg].l02;
+                            const half2v qh = (e & 1) ? q[rg].h13 : q[rg].h02;
+                            const float wl =
+                                fmaf((e & 2) ? (float)ql.y : (float)ql.x, f[rg].al, f[rg].bl);
+                            const float wh =
+                                fmaf((e & 2) ? (float)qh.y : (float)qh.x, f[rg].ah, f[rg].bh);
+                            acc[rg][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(wl, xle, acc[rg][0],
+                                                                             0, 0, 0);
+                            acc[rg][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wh, xhe, acc[rg][1],
+                                                                             0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        const bool seg_end = !more || last_of_tile;
+        if (seg_end) {
+            // lane 16 kk + j holds rows 16 rg + 4 kk + r (register r) of vector j
+            if (r16 < NV) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const f4v s = acc[rg][0] + acc[rg][1];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[wave][r16][16 * rg + 4 * kk + r] = s[r];
+                }
+            }
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f4v{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        if (seg_end && wave == 0) {
+            float tot[NV];
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                float s = red[0][n][lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) s += red[w][n][lane];
+                tot[n] = s;
+            }
+            if (seg_first && last_of_tile)
+                epilogue<NV, 1, EPI_PLAIN>(p, t * 64, lane, tot, 1.f);
+            else
+                finish_split_tile<NV, 1, EPI_PLAIN>(p, un, g, t, t == first_tile ? 0 : 1, lane, tot,
+                                                    1.f);
+        }
+        if (seg_end) seg_first = true;
+        t = tn;
+        k = kn;
+        if (more) commit();
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Persistent decode kernel: the whole per-token chain of GEMV nodes in one
 // launch ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4: one submission per
 // token with the activation resident).  Every workgroup walks the node list;
@@ -1364,14 +1556,23 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
 // slower than 512; on the 715 MB lm_head two per CU took 134.6 us against
 // 138.0 at three and 152.7 at four (interleaved runs).  One tile per
 // workgroup (no cut tiles) was slower still.
-// Four, eight and sixteen plain vectors run on the matrix cores.
+// Four, eight and sixteen plain vectors run on the matrix cores: four and
+// eight on the 4x4x1 form, sixteen on the 16x16x4 form, which uses all of
+// its sixteen vector columns there (17408x5120: 60.0 against 68.0 us; for
+// eight vectors half its columns would idle: 48.8 against 37.9 us).
 template <int NV, int NMAT, int EPI>
 constexpr bool kMfma = NMAT == 1 && EPI == EPI_PLAIN && (NV == 4 || NV == 8 || NV == 16);
+template <int NV>
+constexpr bool kMfma16 = NV == 16;
 
 template <int NV, int NMAT, int EPI>
 const void *gemv_fn() {
-    if constexpr (kMfma<NV, NMAT, EPI>) return (const void *)gemv_mfma_kernel<NV>;
-    else return (const void *)gemv_kernel<NV, NMAT, EPI>;
+    if constexpr (kMfma<NV, NMAT, EPI>) {
+        if constexpr (kMfma16<NV>) return (const void *)gemv_mfma16_kernel<NV>;
+        else return (const void *)gemv_mfma_kernel<NV>;
+    } else {
+        return (const void *)gemv_kernel<NV, NMAT, EPI>;
+    }
 }
 
 template <int NV, int NMAT, int EPI>
@@ -1407,10 +1608,14 @@ int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     const int64_t tiles = (p.M + ROWS - 1) / ROWS;
     const Units un = make_units(p.M, p.nb, NMAT, L.ks);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
-    if constexpr (kMfma<NV, NMAT, EPI>)
-        hipLaunchKernelGGL((gemv_mfma_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0, stream,
-                           p, un);
-    else
+    if constexpr (kMfma<NV, NMAT, EPI>) {
+        if constexpr (kMfma16<NV>)
+            hipLaunchKernelGGL((gemv_mfma16_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0,
+                               stream, p, un);
+        else
+            hipLaunchKernelGGL((gemv_mfma_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0,
+                               stream, p, un);
+    } else
         hipLaunchKernelGGL((gemv_kernel<NV, NMAT, EPI>), dim3((unsigned)un.G), dim3(64 * WK), 0,
                            stream, p, un);
     Q4K_HIP(hipGetLastError());
