@@ -196,10 +196,9 @@ size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t P) {
     return region_bytes(gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P));
 }
 
-// GDN step workspace: [counter region, unused][conv outputs, beta, alpha]
-size_t gdn_ws_bytes(int Hk, int Hv) {
-    return region_bytes((size_t)(2 * Hk + Hv) * 128 + 2 * (size_t)Hv);
-}
+// GDN step workspace: [counter region: per-head arrival counters][conv
+// outputs, beta and alpha, head outputs before their norm]
+size_t gdn_ws_bytes(int Hk, int Hv) { return region_bytes(gdn_scratch_floats(Hk, Hv)); }
 
 // Attention step workspace: [counter region, unused][split-KV partials]
 size_t attn_ws_bytes(int Hq, int Hkv, int64_t cap) {
@@ -511,8 +510,10 @@ int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, flo
     Q4K_TRY(check_device());
     GdnShape sh{p->key_heads, p->value_heads, p->eps};
     float *scratch = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
+    static_assert(kMaxCounters >= 4096, "a counter per value head");
     return launch_gdn_step(sh, u, p->conv_w, p->a_log, p->dt_bias, p->norm_w, conv_state, state,
-                           out, scratch, (hipStream_t)stream);
+                           out, nullptr, scratch, static_cast<unsigned *>(ws),
+                           (hipStream_t)stream);
 }
 
 int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, float *v_cache,
@@ -544,7 +545,7 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
     AttnShape sh{p->q_heads, p->kv_heads, p->rope_dim, p->rope_theta, p->eps};
     float *scratch = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
     return launch_attn_step(sh, u, p->q_norm_w, p->k_norm_w, k_cache, v_cache, capacity, pos,
-                            nullptr, out, scratch, (hipStream_t)stream);
+                            nullptr, out, nullptr, scratch, (hipStream_t)stream);
 }
 
 int q4k_check_partition(int32_t op, int64_t M, int64_t K, int64_t N, int32_t workgroups) {

@@ -141,18 +141,24 @@ struct AttnShape {
     int Hq, Hkv, R;  // query heads, key/value heads (head dimension 256), rotary dims
     float theta, eps;
 };
-// scratch: (2*Hk + Hv) * 128 + 2*Hv floats (conv outputs, beta and alpha)
+// scratch: gdn_scratch_floats(Hk, Hv) floats (conv outputs, beta and alpha,
+// the heads' outputs before their norm); cnt: Hv arrival counters, zero
+// before the call and after it.  out_sq (may be null): per-32-element sums of
+// squares of out.
+size_t gdn_scratch_floats(int Hk, int Hv);
 int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, const float *a_log,
                     const float *dt_bias, const float *norm_w, float *conv_state, float *S,
-                    float *out, float *scratch, hipStream_t stream);
+                    float *out, float *out_sq, float *scratch, unsigned *cnt,
+                    hipStream_t stream);
 // pos_dev, when not null, holds the position (read on the device); else pos.
 // Attention step scratch: the split-KV partials
 // (floats; depends on the cache capacity through the chunk count).
 size_t attn_scratch_floats(int Hq, int Hkv, int64_t cap);
+// out_sq (may be null): per-32-element sums of squares of out.
 int launch_attn_step(const AttnShape &s, const float *u, const float *q_norm_w,
                      const float *k_norm_w, float *k_cache, float *v_cache, int64_t cap,
-                     int64_t pos, const int64_t *pos_dev, float *out, float *scratch,
-                     hipStream_t stream);
+                     int64_t pos, const int64_t *pos_dev, float *out, float *out_sq,
+                     float *scratch, hipStream_t stream);
 
 // ---------------------------------------------------------------- dequant
 int launch_dequant(const uint8_t *w, float *out, int64_t M, int64_t K, hipStream_t stream);

@@ -59,10 +59,37 @@ __device__ __forceinline__ float wave_sum64(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Cross-lane steps through DPP (no LDS round trip, unlike __shfl_xor):
+// quad_perm [1,0,3,2] = lane ^ 1, [2,3,0,1] = lane ^ 2, row_half_mirror =
+// lane 7 - i within each 8 lanes, row_mirror = lane 15 - i within each 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// sum over each group of 8 lanes (8i .. 8i+7), in every lane of the group
+__device__ __forceinline__ float sum8_dpp(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
     return v;
+}
+// sum / maximum over the wave, in every lane: groups of 16 by DPP, then the
+// four groups' values read out in a fixed order
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = sum8_dpp(v);
+    v += dpp_f<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // sum over the 32 lanes of each half-wave (every lane ends with its half's sum)
@@ -75,13 +102,20 @@ __device__ __forceinline__ float half_sum32(float v) {
     return v;
 }
 
+// Workgroup barrier for hand-offs through LDS only: it waits for this
+// wave's LDS (and scalar) operations, not for its global loads in flight,
+// which __syncthreads() would also drain.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Block (256 threads) sum; every thread gets the total.  red: 4 floats of LDS.
 __device__ __forceinline__ float block_sum256(float v, float *red) {
     v = wave_sum64(v);
     const int w = threadIdx.x >> 6;
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
+    lds_barrier();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
@@ -114,20 +148,36 @@ __global__ __launch_bounds__(256) void gdn_conv_kernel(const float *__restrict__
     }
 }
 
-__global__ __launch_bounds__(256) void gdn_state_kernel(const float *__restrict__ c_out,
-                                                        const float *__restrict__ gates,
-                                                        const float *__restrict__ u, int Hk,
-                                                        int Hv, const float *__restrict__ norm_w,
-                                                        float eps, float *__restrict__ S,
-                                                        float *__restrict__ out) {
+// The recurrence of one value head is independent per row dv of its state,
+// so each head's 128 rows are split over GRS workgroups (GRR rows each, 16 KB
+// of state), which spreads the 64 KB per head over four times as many CUs.
+// The gated RMSNorm needs all 128 outputs of the head: each workgroup
+// publishes its rows' outputs with device-coherent stores, waits until they
+// have completed and counts itself in on the head's arrival counter; the
+// last of the GRS applies the norm (the same additions in the same order,
+// whichever arrives last) and resets the counter to zero.
+constexpr int GRS = 4;         // workgroups per value head
+constexpr int GRR = GD / GRS;  // state rows per workgroup
+
+__global__ __launch_bounds__(256) void gdn_state_kernel(
+    const float *__restrict__ c_out, const float *__restrict__ gates, const float *__restrict__ u,
+    int Hk, int Hv, const float *__restrict__ norm_w, float eps, float *__restrict__ S,
+    float *__restrict__ out, float *__restrict__ out_sq, float *obuf, unsigned *cnt) {
     __shared__ float kq[2][GD];
-    __shared__ float ov[GD];
+    __shared__ float ov[GRR];
     __shared__ float red[4];
-    const int h = blockIdx.x, t = threadIdx.x;
+    __shared__ unsigned last_s;
+    const int h = blockIdx.x / GRS, part = blockIdx.x - h * GRS, t = threadIdx.x;
     const int j = h / (Hv / Hk);  // key head of this value head
     const int64_t nq = (int64_t)Hk * GD;
     const float *q = c_out + (int64_t)j * GD, *k = c_out + nq + (int64_t)j * GD;
-    const float *v = c_out + 2 * nq + (int64_t)h * GD;
+    const float *v = c_out + 2 * nq + (int64_t)h * GD + part * GRR;
+    // this workgroup's state rows: their loads fly while q and k are normed
+    float4 *Sh = reinterpret_cast<float4 *>(S + ((int64_t)h * GD + part * GRR) * GD);
+    constexpr int NM = GRR / 8;  // rows per thread slot
+    float4 s[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) s[m] = Sh[t + 256 * m];
     // L2 norms of q and k (threads 0..127: q, 128..255: k)
     const float qk = t < GD ? q[t] : k[t - GD];
     float ssq = t < GD ? qk * qk : 0.f, ssk = t < GD ? 0.f : qk * qk;
@@ -135,18 +185,14 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const float *__restrict_
     ssk = block_sum256(ssk, red);
     if (t < GD) kq[1][t] = qk / sqrtf(ssq + eps) / sqrtf((float)GD);
     else kq[0][t - GD] = qk / sqrtf(ssk + eps);
-    __syncthreads();
+    lds_barrier();
     const float alpha = gates[Hv + h], beta = gates[h];
     const int lane32 = t & 31, row0 = t >> 5;
     const float4 kk = *reinterpret_cast<const float4 *>(&kq[0][4 * lane32]);
     const float4 qq = *reinterpret_cast<const float4 *>(&kq[1][4 * lane32]);
-    float4 *Sh = reinterpret_cast<float4 *>(S + (int64_t)h * GD * GD);
-    float4 s[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) s[m] = Sh[t + 256 * m];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int dv = row0 + 8 * m;
+    for (int m = 0; m < NM; ++m) {
+        const int dv = row0 + 8 * m;  // row within this workgroup's slice
         float4 r = s[m];
         r.x *= alpha;
         r.y *= alpha;
@@ -165,15 +211,34 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const float *__restrict_
         s[m] = r;
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) Sh[t + 256 * m] = s[m];
-    __syncthreads();
+    for (int m = 0; m < NM; ++m) Sh[t + 256 * m] = s[m];
+    lds_barrier();
+    float *ob = obuf + (int64_t)h * GD;
+    if (t < GRR)
+        __hip_atomic_store(&ob[part * GRR + t], ov[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+    lds_barrier();
+    if (t == 0)
+        last_s = __hip_atomic_fetch_add(&cnt[h], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (unsigned)(GRS - 1);
+    lds_barrier();
+    if (!last_s) return;
+    if (t == 0) __hip_atomic_store(&cnt[h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // gated RMSNorm of the head's output
-    const float o = t < GD ? ov[t] : 0.f;
+    const float o = t < GD ? __hip_atomic_load(&ob[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
     const float ms = block_sum256(o * o, red);
     if (t < GD) {
         const float inv = 1.0f / sqrtf(ms / (float)GD + eps);
         const int64_t zo = 2 * nq + (int64_t)Hv * GD + (int64_t)h * GD + t;  // z after q, k, v
-        out[(int64_t)h * GD + t] = norm_w[t] * (o * inv) * siluf_(u[zo]);
+        const float val = norm_w[t] * (o * inv) * siluf_(u[zo]);
+        out[(int64_t)h * GD + t] = val;
+        if (out_sq) {
+            // sums of squares of 32-element granules, added as the plain
+            // sum-of-squares kernel adds them
+            const float sq = half_sum32(val * val);
+            if (lane32 == 0) out_sq[(int64_t)h * (GD / 32) + (t >> 5)] = sq;
+        }
     }
 }
 
@@ -183,36 +248,53 @@ constexpr int AD = 256;  // attention head dimension
 //
 // attn_chunk_kernel: the positions 0..pos are cut into chunks of ACH;
 // workgroup (g, head group, w) takes chunks w, w + nw, ... of key/value head
-// g for up to AHG of the query heads that read it, so every key and value row
-// is read once per head group rather than once per query head.
+// g for a group of the query heads that read it (at most AHG, evened out),
+// so every key and value row is read once per head group rather than once
+// per query head.
 //   set-up: (1 + w) RMSNorm and rotary of the group's queries into LDS (the
-//           rotary angles, in double, once per thread for all heads); the
+//           rotary angle once per thread for all heads: frequency from the
+//           host, product and reduction modulo 2 pi in double); the
 //           workgroup whose chunks hold pos also forms that position's key
 //           and value (the first head group writes them to the caches) and
 //           uses its own copy wherever the chunk reads row pos, so no other
 //           workgroup depends on that write;
 //   scores: wave v takes the chunk's positions 16v .. 16v+15; one load
 //           instruction covers 8 whole 1 KB key rows (8 lanes per row, 16 B
-//           each) and 16 of them cover the wave's rows; 8-lane sums finish
+//           each) and 16 of them cover the wave's rows; 8-lane DPP sums finish
 //           the dot products;
-//   softmax: wave v keeps the running max and sum of heads v and v + 4
-//           (lane i position i);
+//   softmax: wave v keeps the running max and sum of head v (lane i
+//           position i);
 //   values: lane l holds dims 4l .. 4l+3, wave v positions 16v .. 16v+15
-//           (a value row is one 1 KB load), loaded together with the keys;
+//           (a value row is one 1 KB load), issued before the scores so
+//           they arrive during the scores and the softmax;
 //           outputs rescaled whenever the running max moves.
 // It writes (output, max, sum) per head, or nothing if it had no chunk.
 // attn_combine_kernel: one workgroup per query head merges the chunk
 // workgroups in index order and applies the sigmoid gate.  Deterministic:
 // fixed chunk assignment and merge order.
 constexpr int ACH = 64;  // positions per chunk
-constexpr int AHG = 8;   // query heads per chunk workgroup
+constexpr int AHG = 4;   // at most this many query heads per chunk workgroup
+
+// Query heads of a key/value head split into hg groups of hpw (the last may
+// be smaller): as few groups of at most AHG heads as possible, evened out
+// (6 heads: two groups of 3).
+__host__ __device__ inline void attn_head_groups(int rep, int &hpw, int &hg) {
+    const int ng = (rep + AHG - 1) / AHG;
+    hpw = (rep + ng - 1) / ng;
+    hg = (rep + hpw - 1) / hpw;
+}
 constexpr int APS = AD + 4;  // partial record: 256 outputs, max, sum, 2 pad (16 B rows)
+
+// Rotary frequencies theta^(-2i/R), i < R/2, computed on the host in double.
+struct RopeTable {
+    double f[AD / 2];
+};
 
 __global__ __launch_bounds__(256) void attn_chunk_kernel(
     const float *__restrict__ u, const float *__restrict__ qw, const float *__restrict__ kw,
     float *__restrict__ kc, float *__restrict__ vc, int64_t cap, int64_t pos_val,
-    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int R, float theta, float eps, int nw,
-    float *__restrict__ part) {
+    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int R, const RopeTable rope, float eps,
+    int nw, float *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) float qs[AHG][AD];
     __shared__ __attribute__((aligned(16))) float kn[AD];
     __shared__ __attribute__((aligned(16))) float vn[AD];
@@ -223,10 +305,12 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     __shared__ __attribute__((aligned(16))) float oacc[4][AHG][AD];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
+    const int rep = Hq / Hkv;
+    int hpw, hg;
+    attn_head_groups(rep, hpw, hg);
     const int wi = blockIdx.x % nw, gg = blockIdx.x / nw;  // gg = g * hg + head group
     const int g = gg / hg, hgi = gg % hg;
-    const int h0 = g * rep + hgi * AHG, nh = min(AHG, rep - hgi * AHG);
+    const int h0 = g * rep + hgi * hpw, nh = min(hpw, rep - hgi * hpw);
     const int64_t pos = pos_dev ? *pos_dev : pos_val;
     if (pos < 0 || pos >= cap) return;  // the callers keep pos inside the cache
     const int64_t nchunks = pos / ACH + 1, cpos = pos / ACH;
@@ -239,7 +323,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     // tw + 8 (j & 1) + rsub, dims 32 (j >> 1) + 4 sub .. +3; value row tw + i,
     // dims 4 lane .. +3 (rows past pos read row pos, replaced below)
     float4 k4[16], v4[16];
-    auto issue = [&](int64_t c) {
+    auto issue_k = [&](int64_t c) {
         const int64_t tw = c * ACH + 16 * wv;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -247,35 +331,43 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
             k4[j] = *reinterpret_cast<const float4 *>(kg + min(t, pos) * AD + 32 * (j >> 1) +
                                                       4 * sub);
         }
+    };
+    auto issue_v = [&](int64_t c) {
+        const int64_t tw = c * ACH + 16 * wv;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             v4[i] = *reinterpret_cast<const float4 *>(vg + min(tw + i, pos) * AD + 4 * lane);
     };
-    issue(wi);  // the first chunk's loads fly during the set-up
+    issue_k(wi);  // the first chunk's keys fly during the set-up
 
     // ---- set-up: normed, rotated queries (and key, value at pos)
     {
         const int d = tid;
-        float cs = 1.f, sn = 0.f;
-        const int half = R / 2;
-        if (d < R) {
-            const int i = d < half ? d : d - half;
-            const double ang = (double)pos * pow((double)theta, -2.0 * i / R);
-            cs = (float)cos(ang);
-            sn = (float)sin(ang);
-        }
         const int64_t ko = (int64_t)Hq * 2 * AD + (int64_t)g * AD;
         const int64_t vo = (int64_t)Hq * 2 * AD + (int64_t)Hkv * AD + (int64_t)g * AD;
         float x[AHG + 1];
 #pragma unroll
         for (int hh = 0; hh < AHG; ++hh) x[hh] = hh < nh ? u[(int64_t)(h0 + hh) * 2 * AD + d] : 0.f;
         x[AHG] = own_pos ? u[ko + d] : 0.f;
+        // rotary angle pos * theta^(-2i/R) in double (the frequencies come
+        // from the host), reduced modulo 2 pi in double, then sine and cosine
+        // of the reduced angle in single precision
+        float cs = 1.f, sn = 0.f;
+        const int half = R / 2;
+        if (d < R) {
+            const int i = d < half ? d : d - half;
+            const double ang = (double)pos * rope.f[i];
+            const double nt = rint(ang * 0.15915494309189535);         // turns: ang / (2 pi)
+            double red2 = fma(-nt, 6.283185307179586, ang);            // 2 pi, leading part
+            red2 = fma(-nt, 2.4492935982947064e-16, red2);             // 2 pi, the rest
+            sincosf((float)red2, &sn, &cs);
+        }
 #pragma unroll
         for (int hh = 0; hh <= AHG; ++hh) {
-            const float ssq = wave_sum64(x[hh] * x[hh]);
+            const float ssq = wave_sum_dpp(x[hh] * x[hh]);
             if (lane == 0) red[hh][wv] = ssq;
         }
-        __syncthreads();
+        lds_barrier();
         float n[AHG + 1];
 #pragma unroll
         for (int hh = 0; hh <= AHG; ++hh) {
@@ -285,7 +377,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
             if (hh < AHG) qs[hh][d] = n[hh];
             else kn[d] = n[hh];
         }
-        __syncthreads();
+        lds_barrier();
         float r[AHG + 1];
 #pragma unroll
         for (int hh = 0; hh <= AHG; ++hh) {
@@ -294,7 +386,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
             if (d < R) r[hh] = d < half ? n[hh] * cs - row[d + half] * sn
                                         : n[hh] * cs + row[d - half] * sn;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int hh = 0; hh < AHG; ++hh) qs[hh][d] = r[hh];
         if (own_pos) {
@@ -310,7 +402,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
             ms[tid] = -INFINITY;
             ls[tid] = 0.f;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     float o[AHG][4];
@@ -319,6 +411,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     const float scale = 1.0f / sqrtf((float)AD);
     for (int64_t c = wi;;) {
         const int64_t tw = c * ACH + 16 * wv;  // this wave's first position
+        issue_v(c);  // the values fly during the scores and the softmax
         // rows at or past pos: the key and value formed above (past pos the
         // score is masked and the weight is zero, so they only have to be finite)
 #pragma unroll
@@ -338,30 +431,27 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
                 a0 = fmaf(q4.x, ka.x, fmaf(q4.y, ka.y, fmaf(q4.z, ka.z, fmaf(q4.w, ka.w, a0))));
                 a1 = fmaf(q4.x, kb.x, fmaf(q4.y, kb.y, fmaf(q4.z, kb.z, fmaf(q4.w, kb.w, a1))));
             }
-            a0 += __shfl_xor(a0, 4);
-            a1 += __shfl_xor(a1, 4);
-            a0 += __shfl_xor(a0, 2);
-            a1 += __shfl_xor(a1, 2);
-            a0 += __shfl_xor(a0, 1);
-            a1 += __shfl_xor(a1, 1);
+            a0 = sum8_dpp(a0);
+            a1 = sum8_dpp(a1);
             if (sub == 0) {
                 sc[hh][16 * wv + rsub] = a0;
                 sc[hh][16 * wv + 8 + rsub] = a1;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // online softmax: wave wv takes heads wv and wv + 4, lane = position
         const int64_t t0 = c * ACH;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < (AHG + 3) / 4; ++k2) {
             const int hh = wv + 4 * k2;
+            if (hh >= AHG) break;
             if (hh < nh) {
                 const bool ok = t0 + lane <= pos;
                 const float s = ok ? sc[hh][lane] * scale : -INFINITY;
                 const float mo = ms[hh];
-                const float mn = fmaxf(mo, wave_max64(s));
+                const float mn = fmaxf(mo, wave_max_dpp(s));
                 const float pv = ok ? expf(s - mn) : 0.f;
-                const float ssum = wave_sum64(pv);
+                const float ssum = wave_sum_dpp(pv);
                 pr[hh][lane] = pv;
                 if (lane == 0) {
                     const float rr = expf(mo - mn);  // 0 while nothing was seen (mo = -inf)
@@ -374,7 +464,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
                 if (lane == 0) rs[hh] = 1.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // values: rescale, then add this wave's 16 rows
         if (tw + 15 >= pos) {
             const float4 vp = *reinterpret_cast<const float4 *>(&vn[4 * lane]);
@@ -398,31 +488,35 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
                 o[hh][3] = fmaf(pv, v4[i].w, o[hh][3]);
             }
         }
-        __syncthreads();  // sc, pr and rs are rewritten by the next chunk
+        lds_barrier();  // sc, pr and rs are rewritten by the next chunk
         c += nw;
         if (c >= nchunks) break;
-        issue(c);
+        issue_k(c);
     }
     // the four waves' outputs, then (output, max, sum) per head
 #pragma unroll
     for (int hh = 0; hh < AHG; ++hh)
         *reinterpret_cast<float4 *>(&oacc[wv][hh][4 * lane]) =
             make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
-    __syncthreads();
+    lds_barrier();
     float *pw = part + (int64_t)blockIdx.x * AHG * APS;
-    for (int hh = 0; hh < nh; ++hh) {
-        pw[hh * APS + tid] = (oacc[0][hh][tid] + oacc[1][hh][tid]) +
-                             (oacc[2][hh][tid] + oacc[3][hh][tid]);
-        if (tid == 0) {
-            pw[hh * APS + AD] = ms[hh];
-            pw[hh * APS + AD + 1] = ls[hh];
+#pragma unroll
+    for (int hh = 0; hh < AHG; ++hh) {
+        if (hh < nh) {
+            pw[hh * APS + tid] = (oacc[0][hh][tid] + oacc[1][hh][tid]) +
+                                 (oacc[2][hh][tid] + oacc[3][hh][tid]);
+            if (tid == 0) {
+                pw[hh * APS + AD] = ms[hh];
+                pw[hh * APS + AD + 1] = ls[hh];
+            }
         }
     }
 }
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const float *__restrict__ u, const float *__restrict__ part, int64_t cap, int64_t pos_val,
-    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int nw, float *__restrict__ out) {
+    const int64_t *__restrict__ pos_dev, int Hq, int Hkv, int nw, float *__restrict__ out,
+    float *__restrict__ out_sq) {
     __shared__ float cw[64];
     __shared__ float den_s;
     __shared__ __attribute__((aligned(16))) float acc[4][AD];
@@ -430,8 +524,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t pos = pos_dev ? *pos_dev : pos_val;
     if (pos < 0 || pos >= cap) return;
-    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
-    const int g = h / rep, hr = h - g * rep, hgi = hr / AHG, hh = hr - hgi * AHG;
+    const int rep = Hq / Hkv;
+    int hpw, hg;
+    attn_head_groups(rep, hpw, hg);
+    const int g = h / rep, hr = h - g * rep, hgi = hr / hpw, hh = hr - hgi * hpw;
     const int nact = (int)min<int64_t>(nw, pos / ACH + 1);  // nw <= 64
     const float *pb = part + ((int64_t)(g * hg + hgi) * nw * AHG + hh) * APS;
     const int64_t stride = (int64_t)AHG * APS;  // one chunk workgroup
@@ -449,13 +545,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         const bool ok = lane < nact;
         const float m = ok ? pb[lane * stride + AD] : -INFINITY;
         const float l = ok ? pb[lane * stride + AD + 1] : 0.f;
-        const float M = wave_max64(m);
+        const float M = wave_max_dpp(m);
         const float c = ok ? expf(m - M) : 0.f;
         cw[lane] = c;
-        const float den = wave_sum64(c * l);
+        const float den = wave_sum_dpp(c * l);
         if (lane == 0) den_s = den;
     }
-    __syncthreads();
+    lds_barrier();
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -469,31 +565,44 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         }
     }
     *reinterpret_cast<float4 *>(&acc[wv][4 * lane]) = a;
-    __syncthreads();
+    lds_barrier();
     const int d = tid;
     const float num = (acc[0][d] + acc[1][d]) + (acc[2][d] + acc[3][d]);
     const float gate = u[(int64_t)h * 2 * AD + AD + d];
-    out[(int64_t)h * AD + d] = num / den_s * sigmoidf_(gate);
+    const float val = num / den_s * sigmoidf_(gate);
+    out[(int64_t)h * AD + d] = val;
+    if (out_sq) {
+        // sums of squares of 32-element granules, added as the plain
+        // sum-of-squares kernel adds them
+        const float sq = half_sum32(val * val);
+        if ((d & 31) == 0) out_sq[(int64_t)h * (AD / 32) + (d >> 5)] = sq;
+    }
 }
 
 }  // namespace
 
 int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, const float *a_log,
                     const float *dt_bias, const float *norm_w, float *conv_state, float *S,
-                    float *out, float *scratch, hipStream_t stream) {
+                    float *out, float *out_sq, float *scratch, unsigned *cnt,
+                    hipStream_t stream) {
     const int C = 2 * s.Hk * GD + s.Hv * GD;
-    float *c_out = scratch, *gates = scratch + C;
+    float *c_out = scratch, *gates = scratch + C, *obuf = scratch + C + 2 * s.Hv;
     hipLaunchKernelGGL(gdn_conv_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, stream, u,
                        conv_w, conv_state, C, s.Hv, a_log, dt_bias, c_out, gates);
     Q4K_HIP(hipGetLastError());
-    hipLaunchKernelGGL(gdn_state_kernel, dim3((unsigned)s.Hv), dim3(256), 0, stream, c_out, gates,
-                       u, s.Hk, s.Hv, norm_w, s.eps, S, out);
+    hipLaunchKernelGGL(gdn_state_kernel, dim3((unsigned)(s.Hv * GRS)), dim3(256), 0, stream, c_out,
+                       gates, u, s.Hk, s.Hv, norm_w, s.eps, S, out, out_sq, obuf, cnt);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }
 
+size_t gdn_scratch_floats(int Hk, int Hv) {
+    return (size_t)(2 * Hk + Hv) * GD + 2 * (size_t)Hv + (size_t)Hv * GD;
+}
+
 size_t attn_chunk_groups(int Hq, int Hkv, int64_t cap) {
-    const int rep = Hq / Hkv, hg = (rep + AHG - 1) / AHG;
+    int hpw, hg;
+    attn_head_groups(Hq / Hkv, hpw, hg);
     const int64_t nw = std::max<int64_t>(1, std::min<int64_t>(64, (cap + ACH - 1) / ACH));
     return (size_t)Hkv * hg * nw;
 }
@@ -504,16 +613,19 @@ size_t attn_scratch_floats(int Hq, int Hkv, int64_t cap) {
 
 int launch_attn_step(const AttnShape &s, const float *u, const float *q_norm_w,
                      const float *k_norm_w, float *k_cache, float *v_cache, int64_t cap,
-                     int64_t pos, const int64_t *pos_dev, float *out, float *scratch,
-                     hipStream_t stream) {
-    const int rep = s.Hq / s.Hkv, hg = (rep + AHG - 1) / AHG;
+                     int64_t pos, const int64_t *pos_dev, float *out, float *out_sq,
+                     float *scratch, hipStream_t stream) {
+    int hpw, hg;
+    attn_head_groups(s.Hq / s.Hkv, hpw, hg);
     const int nw = (int)std::max<int64_t>(1, std::min<int64_t>(64, (cap + ACH - 1) / ACH));
+    RopeTable rope = {};
+    for (int i = 0; i < s.R / 2; ++i) rope.f[i] = pow((double)s.theta, -2.0 * i / s.R);
     hipLaunchKernelGGL(attn_chunk_kernel, dim3((unsigned)(s.Hkv * hg * nw)), dim3(256), 0, stream,
                        u, q_norm_w, k_norm_w, k_cache, v_cache, cap, pos, pos_dev, s.Hq, s.Hkv,
-                       s.R, s.theta, s.eps, nw, scratch);
+                       s.R, rope, s.eps, nw, scratch);
     Q4K_HIP(hipGetLastError());
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)s.Hq), dim3(256), 0, stream, u, scratch,
-                       cap, pos, pos_dev, s.Hq, s.Hkv, nw, out);
+                       cap, pos, pos_dev, s.Hq, s.Hkv, nw, out, out_sq);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }

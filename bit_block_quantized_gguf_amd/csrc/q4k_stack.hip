@@ -65,7 +65,8 @@ struct q4k_stack {
     float *states = nullptr;          // every layer's conv state, S or K/V caches
     size_t state_floats = 0;
     std::vector<int64_t> st_a, st_b;  // per layer: conv state / K cache, S / V cache
-    float *mix_scratch = nullptr;     // GDN conv outputs and gates; attention partials
+    float *mix_scratch = nullptr;     // GDN conv outputs, gates, head outputs; attention partials
+    unsigned *mix_cnt = nullptr;      // GDN per-head arrival counters (zero between calls)
     int64_t *pos_dev = nullptr;       // device-side position
     int64_t host_pos = 0;             // tokens launched since creation or reset
     // persistent plan
@@ -80,6 +81,7 @@ struct q4k_stack {
 namespace {
 
 constexpr int MD = 128;   // GDN head dimension
+constexpr size_t kMixCounters = 4096;  // GDN arrival counters: one per value head (<= 4096)
 constexpr int AHD = 256;  // attention head dimension
 
 int check_mat(const q4k_mat &m, const char *name, int layer) {
@@ -197,7 +199,8 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint
                 const GdnShape sh{m.gdn.key_heads, m.gdn.value_heads, m.gdn.eps};
                 if ((rc = launch_gdn_step(sh, A + s->off_u[l], m.gdn.conv_w, m.gdn.a_log,
                                           m.gdn.dt_bias, m.gdn.norm_w, s->states + s->st_a[l],
-                                          s->states + s->st_b[l], o, s->mix_scratch, cs)))
+                                          s->states + s->st_b[l], o, SQ + s->sq_o[l],
+                                          s->mix_scratch, s->mix_cnt, cs)))
                     return rc;
                 n += 2;
             } else {
@@ -205,12 +208,11 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint
                                    m.attn.rope_theta, m.attn.eps};
                 if ((rc = launch_attn_step(sh, A + s->off_u[l], m.attn.q_norm_w, m.attn.k_norm_w,
                                            s->states + s->st_a[l], s->states + s->st_b[l], s->cap,
-                                           0, s->pos_dev, o, s->mix_scratch, cs)))
+                                           0, s->pos_dev, o, SQ + s->sq_o[l], s->mix_scratch,
+                                           cs)))
                     return rc;
                 n += 3;
             }
-            if ((rc = launch_sumsq(o, L.mix_out.K, SQ + s->sq_o[l], cs))) return rc;
-            ++n;
             mo = o;
             mo_sq = SQ + s->sq_o[l];
         }
@@ -273,6 +275,7 @@ void release(q4k_stack *s) {
     if (s->sq) (void)hipFree(s->sq);
     if (s->states) (void)hipFree(s->states);
     if (s->mix_scratch) (void)hipFree(s->mix_scratch);
+    if (s->mix_cnt) (void)hipFree(s->mix_cnt);
     if (s->pos_dev) (void)hipFree(s->pos_dev);
     if (s->pnodes) (void)hipFree(s->pnodes);
     if (s->psync) (void)hipFree(s->psync);
@@ -290,6 +293,11 @@ int zero_states(q4k_stack *s, hipStream_t st) {
     // the position too, by a kernel (a plan may be reset inside a captured graph)
     hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float *>(s->pos_dev),
                        (int64_t)(sizeof(int64_t) / sizeof(float)));
+    Q4K_HIP(hipGetLastError());
+    // and the GDN arrival counters (zero after every complete token; cleared
+    // here in case a token did not run to completion)
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((kMixCounters + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<float *>(s->mix_cnt), (int64_t)kMixCounters);
     Q4K_HIP(hipGetLastError());
     s->host_pos = 0;
     return Q4K_OK;
@@ -407,7 +415,7 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
             const int64_t C = (int64_t)(2 * g.key_heads + g.value_heads) * MD;
             s->st_a.push_back(take(sto, 3 * C));
             s->st_b.push_back(take(sto, (int64_t)g.value_heads * MD * MD));
-            scratch = std::max(scratch, (size_t)(C + 2 * g.value_heads));
+            scratch = std::max(scratch, gdn_scratch_floats(g.key_heads, g.value_heads));
         } else if (mixers) {
             const q4k_attn_params &a = s->mix[l].attn;
             const int64_t n = (int64_t)a.kv_heads * s->cap * AHD;
@@ -436,6 +444,7 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         ok = (sto == 0 || hipMalloc(&s->states, sto * sizeof(float)) == hipSuccess) &&
              hipMalloc(&s->mix_scratch, std::max<size_t>(scratch, 64) * sizeof(float)) ==
                  hipSuccess &&
+             hipMalloc(&s->mix_cnt, kMixCounters * sizeof(unsigned)) == hipSuccess &&
              hipMalloc(&s->pos_dev, sizeof(int64_t)) == hipSuccess;
     }
     if (!ok) {
@@ -451,6 +460,7 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
         hipMemset(s->sq, 0, sqo * sizeof(float)) != hipSuccess ||
         (s->states && hipMemset(s->states, 0, sto * sizeof(float)) != hipSuccess) ||
         (s->pos_dev && hipMemset(s->pos_dev, 0, sizeof(int64_t)) != hipSuccess) ||
+        (s->mix_cnt && hipMemset(s->mix_cnt, 0, kMixCounters * sizeof(unsigned)) != hipSuccess) ||
         hipDeviceSynchronize() != hipSuccess) {
         release(s);
         return fail(Q4K_EHIP, "decode stack: arena clear failed");

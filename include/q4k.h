@@ -280,8 +280,12 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
  * beta = sigmoid(b), alpha = exp(-exp(a_log) * softplus(a + dt_bias));
  * S <- alpha S; S <- S + k (beta (v - S^T k))^T; o = S^T q;
  * out = norm_w * o / sqrt(mean(o^2) + eps) * silu(z).
- * Workspace: q4k_workspace_size(Q4K_OP_GDN_STEP, Hk, Hv, 0).  Two kernels;
- * the state is read and written once (64 KB per value head).  Errors:
+ * Workspace: q4k_workspace_size(Q4K_OP_GDN_STEP, Hk, Hv, 0).  Two kernels:
+ * the convolution and gates, then the recurrence with each head's 128 state
+ * rows split over four workgroups (the state is read and written once, 64 KB
+ * per value head); the last of a head's workgroups to finish applies the
+ * norm, counted in on an arrival counter in the workspace's counter region
+ * that the call leaves at zero.  Errors:
  * Q4K_EINVAL (NULL, bad eps, small workspace), Q4K_ESHAPE (Hk, Hv not
  * positive or Hv not a multiple of Hk, key_dim or value_dim not 128),
  * Q4K_EALIGN. */
@@ -304,8 +308,9 @@ int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, flo
  * query head h attends with key/value head h / (Hq/Hkv):
  * out_h = softmax(q . k_t / 16) v over t = 0..pos, times sigmoid(gate_h).
  * Split-KV: the positions are cut into chunks of 64 spread over up to 64
- * workgroups per (kv head, group of 8 query heads), each key and value row
- * read once per group, then merged per query head in a fixed order.
+ * workgroups per (kv head, group of query heads: at most 4, evened out), each
+ * key and value row read once per group, then merged per query head in a
+ * fixed order.
  * Workspace: q4k_workspace_size(Q4K_OP_ATTN_STEP, Hq, Hkv, capacity)
  * (per-chunk partials).  Errors: Q4K_EINVAL (NULL,
  * small workspace), Q4K_ESHAPE (head_dim not 256, Hq not a multiple of Hkv,

@@ -92,6 +92,29 @@ def test_gdn_steps_match_oracle(q4k, steps):
     _heads(out, free, Hv, 2e-3, "gdn out after %d free-running steps" % steps)
 
 
+def test_gdn_deterministic_and_counters_cleared(q4k, torch):
+    """A head's 128 state rows are split over four workgroups and the last
+    to arrive applies the norm: two runs of the same steps give the same
+    bits, and every call leaves the workspace's arrival counters at zero."""
+    prm = _gdn_params()
+    dprm = {k: up(v) for k, v in prm.items()}
+    ws = q4k.Workspace(q4k.workspace_size(q4k.OP_GDN_STEP, Hk, Hv, 0))
+    runs = []
+    for _ in range(2):
+        cs_d, S_d = up(_n(5, 3 * C)), up(_n(6, Hv * D * D, 0.05))
+        outs = []
+        for t in range(3):
+            o = q4k.gdn_step(up(_n(100 + t, NU)), dprm["conv_w"], dprm["a_log"],
+                             dprm["dt_bias"], dprm["norm_w"], cs_d, S_d, ws=ws)
+            outs.append(down(o).copy())
+            cnt = ws.tensor[:4 * Hv].cpu().numpy()
+            assert not cnt.any(), "arrival counters left non-zero"
+        runs.append((outs, down(S_d).copy()))
+    for a, b in zip(runs[0][0], runs[1][0]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+
+
 def test_gdn_zero_state_first_token(q4k):
     """From a zero state and zero conv state the first token's state is the
     rank-1 beta k v^T of every head."""
