@@ -304,6 +304,10 @@ def test_gemm_bf16_exact_inputs(q4k):
 
 
 def test_gemm_split_k_variants_agree(q4k):
+    """Stream-K partitions from one workgroup to more than the CUs, at both
+    tile widths: every one gives the reference within the bars, repeated
+    calls give the same bits, and each call leaves the workspace's counter
+    region at zero."""
     M, K, P = 5120, 17408, 256
     w = synth.q4k_weight(synth.key(5, 1), M, K)
     X = synth.activations(5, P, K)
@@ -316,10 +320,12 @@ def test_gemm_split_k_variants_agree(q4k):
                        (128, 256), (128, 511), (256, 1), (256, 5), (256, 256), (256, 1000)):
             q4k.tune_gemm(tt, wg)
             note("gemm tile=%d wg=%d" % (tt, wg))
-            Y = down(q4k.gemm(wd, Xd, M=M, K=K))
+            ws = q4k.Workspace(q4k.workspace_size(q4k.OP_GEMM, M, K, P))
+            Y = down(q4k.gemm(wd, Xd, M=M, K=K, ws=ws))
+            assert not ws.tensor[:4 * 16384].cpu().numpy().any(), "counters left non-zero"
             _check_gemm(Y, w, X, M, K, rows, toks, "tile=%d wg=%d" % (tt, wg))
             outs.append(Y)
-        Y2 = down(q4k.gemm(wd, Xd, M=M, K=K))
-        assert np.array_equal(bits(Y2), bits(outs[-1]))          # deterministic
+            Y2 = down(q4k.gemm(wd, Xd, M=M, K=K, ws=ws))
+            assert np.array_equal(bits(Y2), bits(Y))                 # deterministic
     finally:
         q4k.tune_gemm(0, 0)
