@@ -211,7 +211,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint
                                            0, s->pos_dev, o, SQ + s->sq_o[l], s->mix_scratch,
                                            cs)))
                     return rc;
-                n += 3;
+                n += 2;
             }
             mo = o;
             mo_sq = SQ + s->sq_o[l];
