@@ -196,8 +196,8 @@ size_t gemm_ws_bytes(int64_t M, int64_t K, int64_t P) {
     return region_bytes(gemm_partial_floats(L, M, P) + gemm_xb_floats(K, P));
 }
 
-// GDN step workspace: [counter region: per-head arrival counters][conv
-// outputs, beta and alpha, head outputs before their norm]
+// GDN step workspace: [counter region: per-value-head and per-key-head
+// arrival counters][head outputs before their norm]
 size_t gdn_ws_bytes(int Hk, int Hv) { return region_bytes(gdn_scratch_floats(Hk, Hv)); }
 
 // Attention step workspace: [counter region, unused][split-KV partials]
@@ -510,7 +510,7 @@ int q4k_gdn_step(const q4k_gdn_params *p, const float *u, float *conv_state, flo
     Q4K_TRY(check_device());
     GdnShape sh{p->key_heads, p->value_heads, p->eps};
     float *scratch = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
-    static_assert(kMaxCounters >= 4096, "a counter per value head");
+    static_assert(kMaxCounters >= 8192, "a counter per value head and per key head");
     return launch_gdn_step(sh, u, p->conv_w, p->a_log, p->dt_bias, p->norm_w, conv_state, state,
                            out, nullptr, scratch, static_cast<unsigned *>(ws),
                            (hipStream_t)stream);

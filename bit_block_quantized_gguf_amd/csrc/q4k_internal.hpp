@@ -141,10 +141,10 @@ struct AttnShape {
     int Hq, Hkv, R;  // query heads, key/value heads (head dimension 256), rotary dims
     float theta, eps;
 };
-// scratch: gdn_scratch_floats(Hk, Hv) floats (conv outputs, beta and alpha,
-// the heads' outputs before their norm); cnt: Hv arrival counters, zero
-// before the call and after it.  out_sq (may be null): per-32-element sums of
-// squares of out.
+// scratch: gdn_scratch_floats(Hk, Hv) floats (the heads' outputs before
+// their norm); cnt: Hv + Hk arrival counters (value heads, then key heads),
+// zero before the call and after it.  out_sq (may be null): per-32-element
+// sums of squares of out.
 size_t gdn_scratch_floats(int Hk, int Hv);
 int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, const float *a_log,
                     const float *dt_bias, const float *norm_w, float *conv_state, float *S,

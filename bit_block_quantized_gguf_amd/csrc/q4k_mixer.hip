@@ -11,26 +11,27 @@
 // attention, conv, norms and gates at 6.8%; §4 asks for them on the device so
 // that a token is one submission.
 //
-// Gated DeltaNet step (per token; u = [q | k | v | z | b | a]):
-//   gdn_conv_kernel   — one thread per channel of [q|k|v]: silu of the
-//                       4-tap causal conv over (state, input), state shifted;
-//                       the first threads also form beta = sigmoid(b) and
-//                       alpha = exp(-exp(A_log) softplus(a + dt_bias)).
-//   gdn_state_kernel  — one workgroup per value head: q and k of its key
-//                       head L2-normalised (q also by 1/sqrt(128)), then on
-//                       the head's 128 x 128 state (value-dimension major,
-//                       S[dv][dk], 64 KB) S <- alpha S,
-//                       delta = beta (v - S^T k), S <- S + k delta^T,
-//                       o = S^T q, and the gated norm
-//                       out = norm_w * o / rms(o) * silu(z).
-//                       Thread t holds float4 t + 256 m (m = 0..15) of the
-//                       state: rows t/32 + 8m, key dims 4 (t%32) .. +3, so
-//                       every load and store instruction moves 4 KB of
-//                       contiguous state, and each row's dot products reduce
-//                       over the 32 lanes that hold it.
+// Gated DeltaNet step (per token; u = [q | k | v | z | b | a]), one kernel,
+// gdn_step_kernel, four workgroups per value head:
+//   conv         — silu of the 4-tap causal conv over (state, input) of the
+//                  q and k channels of the head's key head and of the v
+//                  channels of the workgroup's rows, the conv state shifted
+//                  once per channel; beta = sigmoid(b) and
+//                  alpha = exp(-exp(A_log) softplus(a + dt_bias));
+//   recurrence   — q and k L2-normalised (q also by 1/sqrt(128)); on the
+//                  workgroup's 32 rows of the head's 128 x 128 state
+//                  (value-dimension major, S[dv][dk]) S <- alpha S,
+//                  delta = beta (v - S^T k), S <- S + k delta^T, o = S^T q.
+//                  Thread t holds float4 t + 256 m of the slice: rows
+//                  t/32 + 8m, key dims 4 (t%32) .. +3, so every load and
+//                  store instruction moves 4 KB of contiguous state and each
+//                  row's dot products reduce over the 32 lanes that hold it;
+//   gated norm   — out = norm_w * o / rms(o) * silu(z) over the head's 128
+//                  outputs, by the last of its four workgroups.
 // Gated attention step (position pos; u = [per head: q | gate] x Hq, k, v):
-//   attn_chunk_kernel   — (1 + w) RMSNorm and rotary (first R dims, angles in
-//                         double) of q and k, k and v written to the cache at
+//   attn_chunk_kernel   — (1 + w) RMSNorm and rotary (first R dims, angle
+//                         and its reduction in double) of q and k, k and v
+//                         written to the cache at
 //                         pos, then a split-KV online softmax over chunks of
 //                         positions, each key/value row read once per group
 //                         of query heads that share it;
@@ -48,16 +49,6 @@ namespace {
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
 __device__ __forceinline__ float softplusf_(float x) { return x > 30.f ? x : log1pf(expf(x)); }
-
-__device__ __forceinline__ float wave_sum64(float v) {
-    v += __shfl_xor(v, 32);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    return v;
-}
 
 // Cross-lane steps through DPP (no LDS round trip, unlike __shfl_xor):
 // quad_perm [1,0,3,2] = lane ^ 1, [2,3,0,1] = lane ^ 2, row_half_mirror =
@@ -111,7 +102,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Block (256 threads) sum; every thread gets the total.  red: 4 floats of LDS.
 __device__ __forceinline__ float block_sum256(float v, float *red) {
-    v = wave_sum64(v);
+    v = wave_sum_dpp(v);
     const int w = threadIdx.x >> 6;
     lds_barrier();
     if ((threadIdx.x & 63) == 0) red[w] = v;
@@ -121,109 +112,161 @@ __device__ __forceinline__ float block_sum256(float v, float *red) {
 
 constexpr int GD = 128;  // key and value head dimension of the recurrence
 
-__global__ __launch_bounds__(256) void gdn_conv_kernel(const float *__restrict__ u,
-                                                       const float *__restrict__ conv_w,
-                                                       float *__restrict__ conv_state, int C,
-                                                       int Hv, const float *__restrict__ a_log,
-                                                       const float *__restrict__ dt_bias,
-                                                       float *__restrict__ c_out,
-                                                       float *__restrict__ gates) {
-    const int ch = blockIdx.x * 256 + threadIdx.x;
-    if (ch < C) {
-        float *st = conv_state + 3 * (int64_t)ch;
-        const float4 w = *reinterpret_cast<const float4 *>(conv_w + 4 * (int64_t)ch);
-        const float s0 = st[0], s1 = st[1], s2 = st[2], x = u[ch];
-        const float s = fmaf(w.w, x, fmaf(w.z, s2, fmaf(w.y, s1, w.x * s0)));
-        c_out[ch] = siluf_(s);
-        st[0] = s1;
-        st[1] = s2;
-        st[2] = x;
-    }
-    if (blockIdx.x == 0 && threadIdx.x < Hv) {
-        const int h = threadIdx.x;
-        const int64_t off = (int64_t)C + (int64_t)Hv * GD;  // b after q, k, v and z
-        const float b = u[off + h], a = u[off + Hv + h];
-        gates[h] = sigmoidf_(b);
-        gates[Hv + h] = expf(-expf(a_log[h]) * softplusf_(a + dt_bias[h]));
-    }
-}
-
-// The recurrence of one value head is independent per row dv of its state,
-// so each head's 128 rows are split over GRS workgroups (GRR rows each, 16 KB
-// of state), which spreads the 64 KB per head over four times as many CUs.
-// The gated RMSNorm needs all 128 outputs of the head: each workgroup
-// publishes its rows' outputs with device-coherent stores, waits until they
-// have completed and counts itself in on the head's arrival counter; the
-// last of the GRS applies the norm (the same additions in the same order,
-// whichever arrives last) and resets the counter to zero.
+// One GDN decode step in one kernel.  The recurrence of a value head is
+// independent per row dv of its state, so each head's 128 rows are split over
+// GRS workgroups (GRR rows each, 16 KB of state): 4 x 48 = 192 workgroups for
+// the model's 48 heads.  Each workgroup
+//   * issues its state loads first;
+//   * forms the causal conv + SiLU of the q and k channels of its key head
+//     (256 channels, one per thread) and of the v channels of its rows from
+//     the old conv state, and beta and the decay of its head;
+//   * L2-normalises q and k and runs the delta rule on its rows;
+//   * publishes its rows' outputs with device-coherent stores and counts
+//     itself in on the head's arrival counter; the last of the GRS applies
+//     the gated RMSNorm (in a fixed order, whoever arrives last) and resets
+//     the counter.
+// Conv state: a v channel is read by one workgroup only, which shifts it in
+// place.  A q or k channel is read by the GRS workgroups of every value head
+// of its key head; each counts itself in on the key head's counter after its
+// reads have returned, and the last one shifts those 256 channels' state and
+// resets the counter, so no workgroup reads a state another has shifted.
 constexpr int GRS = 4;         // workgroups per value head
 constexpr int GRR = GD / GRS;  // state rows per workgroup
 
-__global__ __launch_bounds__(256) void gdn_state_kernel(
-    const float *__restrict__ c_out, const float *__restrict__ gates, const float *__restrict__ u,
-    int Hk, int Hv, const float *__restrict__ norm_w, float eps, float *__restrict__ S,
-    float *__restrict__ out, float *__restrict__ out_sq, float *obuf, unsigned *cnt) {
+__device__ __forceinline__ float conv4(const float4 w, float s0, float s1, float s2, float x) {
+    return siluf_(fmaf(w.w, x, fmaf(w.z, s2, fmaf(w.y, s1, w.x * s0))));
+}
+
+__global__ __launch_bounds__(256) void gdn_step_kernel(
+    const float *__restrict__ u, const float *__restrict__ conv_w, float *conv_state, int Hk,
+    int Hv, const float *__restrict__ a_log, const float *__restrict__ dt_bias,
+    const float *__restrict__ norm_w, float eps, float *__restrict__ S, float *__restrict__ out,
+    float *__restrict__ out_sq, float *obuf, unsigned *cnt_v, unsigned *cnt_k) {
     __shared__ float kq[2][GD];
+    __shared__ float vv[GRR];
     __shared__ float ov[GRR];
+    __shared__ float gab[2];
     __shared__ float red[4];
     __shared__ unsigned last_s;
     const int h = blockIdx.x / GRS, part = blockIdx.x - h * GRS, t = threadIdx.x;
-    const int j = h / (Hv / Hk);  // key head of this value head
+    const int rep = Hv / Hk, j = h / rep;  // key head of this value head
     const int64_t nq = (int64_t)Hk * GD;
-    const float *q = c_out + (int64_t)j * GD, *k = c_out + nq + (int64_t)j * GD;
-    const float *v = c_out + 2 * nq + (int64_t)h * GD + part * GRR;
-    // this workgroup's state rows: their loads fly while q and k are normed
+    // this workgroup's state rows: their loads fly while the inputs are formed
+    // thread t holds key dims 8 (t % 16) .. +7 of rows t / 16 + 16 m of the
+    // slice (two float4 per row): every load instruction pair moves 2 KB of
+    // contiguous state, and a row's dot products reduce over 16 lanes
     float4 *Sh = reinterpret_cast<float4 *>(S + ((int64_t)h * GD + part * GRR) * GD);
-    constexpr int NM = GRR / 8;  // rows per thread slot
-    float4 s[NM];
+    constexpr int NM = GRR / 16;  // rows per thread
+    float4 s[NM][2];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) s[m] = Sh[t + 256 * m];
-    // L2 norms of q and k (threads 0..127: q, 128..255: k)
-    const float qk = t < GD ? q[t] : k[t - GD];
+    for (int m = 0; m < NM; ++m) {
+        s[m][0] = Sh[2 * t + 512 * m];
+        s[m][1] = Sh[2 * t + 1 + 512 * m];
+    }
+    // conv of the q (threads 0..127) and k (128..255) channels of key head j
+    const int64_t chqk = t < GD ? (int64_t)j * GD + t : nq + (int64_t)j * GD + (t - GD);
+    const float4 wqk = *reinterpret_cast<const float4 *>(conv_w + 4 * chqk);
+    const float q0 = conv_state[3 * chqk], q1 = conv_state[3 * chqk + 1],
+                q2 = conv_state[3 * chqk + 2], xqk = u[chqk];
+    const float qk = conv4(wqk, q0, q1, q2, xqk);
+    // conv of the v channels of this workgroup's rows (their only reader)
+    if (t < GRR) {
+        const int64_t ch = 2 * nq + (int64_t)h * GD + part * GRR + t;
+        const float4 w = *reinterpret_cast<const float4 *>(conv_w + 4 * ch);
+        float *st = conv_state + 3 * ch;
+        const float v0 = st[0], v1 = st[1], v2 = st[2], x = u[ch];
+        vv[t] = conv4(w, v0, v1, v2, x);
+        st[0] = v1;
+        st[1] = v2;
+        st[2] = x;
+    }
+    if (t == 0) {
+        const int64_t off = 2 * nq + 2 * (int64_t)Hv * GD;  // b after q, k, v and z
+        const float b = u[off + h], a = u[off + Hv + h];
+        gab[0] = sigmoidf_(b);
+        gab[1] = expf(-expf(a_log[h]) * softplusf_(a + dt_bias[h]));
+    }
+    // L2 norms of q and k
     float ssq = t < GD ? qk * qk : 0.f, ssk = t < GD ? 0.f : qk * qk;
     ssq = block_sum256(ssq, red);
     ssk = block_sum256(ssk, red);
     if (t < GD) kq[1][t] = qk / sqrtf(ssq + eps) / sqrtf((float)GD);
     else kq[0][t - GD] = qk / sqrtf(ssk + eps);
     lds_barrier();
-    const float alpha = gates[Hv + h], beta = gates[h];
-    const int lane32 = t & 31, row0 = t >> 5;
-    const float4 kk = *reinterpret_cast<const float4 *>(&kq[0][4 * lane32]);
-    const float4 qq = *reinterpret_cast<const float4 *>(&kq[1][4 * lane32]);
+    // every thread's conv-state reads have returned (their values are used
+    // above): count in on the key head now; the answer (is this the last
+    // reader, which shifts the state?) is only needed at the end
+    unsigned k_old = 0;
+    if (t == 0)
+        k_old = __hip_atomic_fetch_add(&cnt_k[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float alpha = gab[1], beta = gab[0];
+    const int lane16 = t & 15, row0 = t >> 4;
+    const float4 k0 = *reinterpret_cast<const float4 *>(&kq[0][8 * lane16]);
+    const float4 k1 = *reinterpret_cast<const float4 *>(&kq[0][8 * lane16 + 4]);
+    const float4 q0v = *reinterpret_cast<const float4 *>(&kq[1][8 * lane16]);
+    const float4 q1v = *reinterpret_cast<const float4 *>(&kq[1][8 * lane16 + 4]);
+    auto dot8 = [](const float4 &a0, const float4 &a1, const float4 &b0, const float4 &b1) {
+        return fmaf(a0.x, b0.x, fmaf(a0.y, b0.y, fmaf(a0.z, b0.z, fmaf(a0.w, b0.w,
+               fmaf(a1.x, b1.x, fmaf(a1.y, b1.y, fmaf(a1.z, b1.z, a1.w * b1.w)))))));
+    };
+    auto axpy4 = [](float4 &r, const float4 &k, float d) {
+        r.x = fmaf(k.x, d, r.x);
+        r.y = fmaf(k.y, d, r.y);
+        r.z = fmaf(k.z, d, r.z);
+        r.w = fmaf(k.w, d, r.w);
+    };
+    auto scale4 = [](float4 &r, float a) {
+        r.x *= a;
+        r.y *= a;
+        r.z *= a;
+        r.w *= a;
+    };
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const int dv = row0 + 8 * m;  // row within this workgroup's slice
-        float4 r = s[m];
-        r.x *= alpha;
-        r.y *= alpha;
-        r.z *= alpha;
-        r.w *= alpha;
-        float kv = fmaf(r.x, kk.x, fmaf(r.y, kk.y, fmaf(r.z, kk.z, r.w * kk.w)));
-        kv = half_sum32(kv);
-        const float delta = beta * (v[dv] - kv);
-        r.x = fmaf(kk.x, delta, r.x);
-        r.y = fmaf(kk.y, delta, r.y);
-        r.z = fmaf(kk.z, delta, r.z);
-        r.w = fmaf(kk.w, delta, r.w);
-        float o = fmaf(r.x, qq.x, fmaf(r.y, qq.y, fmaf(r.z, qq.z, r.w * qq.w)));
-        o = half_sum32(o);
-        if (lane32 == 0) ov[dv] = o;
-        s[m] = r;
+        const int dv = row0 + 16 * m;  // row within this workgroup's slice
+        float4 r0 = s[m][0], r1 = s[m][1];
+        scale4(r0, alpha);
+        scale4(r1, alpha);
+        float kv = dot8(r0, r1, k0, k1);
+        kv = sum8_dpp(kv);
+        kv += dpp_f<0x140>(kv);  // sum over the row's 16 lanes
+        const float delta = beta * (vv[dv] - kv);
+        axpy4(r0, k0, delta);
+        axpy4(r1, k1, delta);
+        float o = dot8(r0, r1, q0v, q1v);
+        o = sum8_dpp(o);
+        o += dpp_f<0x140>(o);
+        if (lane16 == 0) ov[dv] = o;
+        s[m][0] = r0;
+        s[m][1] = r1;
     }
 #pragma unroll
-    for (int m = 0; m < NM; ++m) Sh[t + 256 * m] = s[m];
+    for (int m = 0; m < NM; ++m) {
+        Sh[2 * t + 512 * m] = s[m][0];
+        Sh[2 * t + 1 + 512 * m] = s[m][1];
+    }
     lds_barrier();
     float *ob = obuf + (int64_t)h * GD;
     if (t < GRR)
         __hip_atomic_store(&ob[part * GRR + t], ov[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
     lds_barrier();
-    if (t == 0)
-        last_s = __hip_atomic_fetch_add(&cnt[h], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 (unsigned)(GRS - 1);
+    if (t == 0) {
+        const bool v_last = __hip_atomic_fetch_add(&cnt_v[h], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(GRS - 1);
+        const bool k_last = k_old == (unsigned)(rep * GRS - 1);
+        last_s = (v_last ? 1u : 0u) | (k_last ? 2u : 0u);
+    }
     lds_barrier();
-    if (!last_s) return;
-    if (t == 0) __hip_atomic_store(&cnt[h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last_s & 2u) {  // the last reader of key head j's q and k channels
+        float *st = conv_state + 3 * chqk;
+        st[0] = q1;
+        st[1] = q2;
+        st[2] = xqk;
+        if (t == 0) __hip_atomic_store(&cnt_k[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!(last_s & 1u)) return;
+    if (t == 0) __hip_atomic_store(&cnt_v[h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // gated RMSNorm of the head's output
     const float o = t < GD ? __hip_atomic_load(&ob[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                            : 0.f;
@@ -237,7 +280,7 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(
             // sums of squares of 32-element granules, added as the plain
             // sum-of-squares kernel adds them
             const float sq = half_sum32(val * val);
-            if (lane32 == 0) out_sq[(int64_t)h * (GD / 32) + (t >> 5)] = sq;
+            if ((t & 31) == 0) out_sq[(int64_t)h * (GD / 32) + (t >> 5)] = sq;
         }
     }
 }
@@ -585,19 +628,16 @@ int launch_gdn_step(const GdnShape &s, const float *u, const float *conv_w, cons
                     const float *dt_bias, const float *norm_w, float *conv_state, float *S,
                     float *out, float *out_sq, float *scratch, unsigned *cnt,
                     hipStream_t stream) {
-    const int C = 2 * s.Hk * GD + s.Hv * GD;
-    float *c_out = scratch, *gates = scratch + C, *obuf = scratch + C + 2 * s.Hv;
-    hipLaunchKernelGGL(gdn_conv_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, stream, u,
-                       conv_w, conv_state, C, s.Hv, a_log, dt_bias, c_out, gates);
-    Q4K_HIP(hipGetLastError());
-    hipLaunchKernelGGL(gdn_state_kernel, dim3((unsigned)(s.Hv * GRS)), dim3(256), 0, stream, c_out,
-                       gates, u, s.Hk, s.Hv, norm_w, s.eps, S, out, out_sq, obuf, cnt);
+    hipLaunchKernelGGL(gdn_step_kernel, dim3((unsigned)(s.Hv * GRS)), dim3(256), 0, stream, u,
+                       conv_w, conv_state, s.Hk, s.Hv, a_log, dt_bias, norm_w, s.eps, S, out,
+                       out_sq, scratch, cnt, cnt + s.Hv);
     Q4K_HIP(hipGetLastError());
     return Q4K_OK;
 }
 
 size_t gdn_scratch_floats(int Hk, int Hv) {
-    return (size_t)(2 * Hk + Hv) * GD + 2 * (size_t)Hv + (size_t)Hv * GD;
+    (void)Hk;
+    return (size_t)Hv * GD;
 }
 
 size_t attn_chunk_groups(int Hq, int Hkv, int64_t cap) {

@@ -65,8 +65,8 @@ struct q4k_stack {
     float *states = nullptr;          // every layer's conv state, S or K/V caches
     size_t state_floats = 0;
     std::vector<int64_t> st_a, st_b;  // per layer: conv state / K cache, S / V cache
-    float *mix_scratch = nullptr;     // GDN conv outputs, gates, head outputs; attention partials
-    unsigned *mix_cnt = nullptr;      // GDN per-head arrival counters (zero between calls)
+    float *mix_scratch = nullptr;     // GDN head outputs; attention partials
+    unsigned *mix_cnt = nullptr;      // GDN arrival counters (zero between calls)
     int64_t *pos_dev = nullptr;       // device-side position
     int64_t host_pos = 0;             // tokens launched since creation or reset
     // persistent plan
@@ -81,7 +81,7 @@ struct q4k_stack {
 namespace {
 
 constexpr int MD = 128;   // GDN head dimension
-constexpr size_t kMixCounters = 4096;  // GDN arrival counters: one per value head (<= 4096)
+constexpr size_t kMixCounters = 8192;  // GDN arrival counters: per value head and key head
 constexpr int AHD = 256;  // attention head dimension
 
 int check_mat(const q4k_mat &m, const char *name, int layer) {

@@ -280,12 +280,13 @@ int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int6
  * beta = sigmoid(b), alpha = exp(-exp(a_log) * softplus(a + dt_bias));
  * S <- alpha S; S <- S + k (beta (v - S^T k))^T; o = S^T q;
  * out = norm_w * o / sqrt(mean(o^2) + eps) * silu(z).
- * Workspace: q4k_workspace_size(Q4K_OP_GDN_STEP, Hk, Hv, 0).  Two kernels:
- * the convolution and gates, then the recurrence with each head's 128 state
- * rows split over four workgroups (the state is read and written once, 64 KB
- * per value head); the last of a head's workgroups to finish applies the
- * norm, counted in on an arrival counter in the workspace's counter region
- * that the call leaves at zero.  Errors:
+ * Workspace: q4k_workspace_size(Q4K_OP_GDN_STEP, Hk, Hv, 0).  One kernel,
+ * four workgroups per value head, each taking 32 of the head's 128 state
+ * rows (the state is read and written once, 64 KB per value head) and
+ * forming the conv of the channels it reads; the last of a head's
+ * workgroups applies the norm, and the last reader of a key head's q and k
+ * channels shifts their conv state, each counted in on arrival counters in
+ * the workspace's counter region that the call leaves at zero.  Errors:
  * Q4K_EINVAL (NULL, bad eps, small workspace), Q4K_ESHAPE (Hk, Hv not
  * positive or Hv not a multiple of Hk, key_dim or value_dim not 128),
  * Q4K_EALIGN. */

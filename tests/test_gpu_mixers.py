@@ -93,9 +93,11 @@ def test_gdn_steps_match_oracle(q4k, steps):
 
 
 def test_gdn_deterministic_and_counters_cleared(q4k, torch):
-    """A head's 128 state rows are split over four workgroups and the last
-    to arrive applies the norm: two runs of the same steps give the same
-    bits, and every call leaves the workspace's arrival counters at zero."""
+    """A head's 128 state rows are split over four workgroups; the last to
+    arrive applies the norm, and the last reader of a key head's q and k
+    channels shifts their conv state: two runs of the same steps give the
+    same bits, and every call leaves the workspace's arrival counters at
+    zero."""
     prm = _gdn_params()
     dprm = {k: up(v) for k, v in prm.items()}
     ws = q4k.Workspace(q4k.workspace_size(q4k.OP_GDN_STEP, Hk, Hv, 0))
@@ -107,7 +109,7 @@ def test_gdn_deterministic_and_counters_cleared(q4k, torch):
             o = q4k.gdn_step(up(_n(100 + t, NU)), dprm["conv_w"], dprm["a_log"],
                              dprm["dt_bias"], dprm["norm_w"], cs_d, S_d, ws=ws)
             outs.append(down(o).copy())
-            cnt = ws.tensor[:4 * Hv].cpu().numpy()
+            cnt = ws.tensor[:4 * (Hv + Hk)].cpu().numpy()
             assert not cnt.any(), "arrival counters left non-zero"
         runs.append((outs, down(S_d).copy()))
     for a, b in zip(runs[0][0], runs[1][0]):
