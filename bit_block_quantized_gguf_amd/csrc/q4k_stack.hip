@@ -202,7 +202,7 @@ int enqueue_token(q4k_stack *s, hipStream_t cs, int64_t *nodes, std::vector<uint
                                           s->states + s->st_b[l], o, SQ + s->sq_o[l],
                                           s->mix_scratch, s->mix_cnt, cs)))
                     return rc;
-                n += 2;
+                n += 1;
             } else {
                 const AttnShape sh{m.attn.q_heads, m.attn.kv_heads, m.attn.rope_dim,
                                    m.attn.rope_theta, m.attn.eps};

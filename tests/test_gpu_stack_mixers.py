@@ -92,11 +92,11 @@ def test_stack_with_real_mixers(q4k, torch):
     mats.append(lm)
     shapes.append((V, H))
     stack = q4k.DecodeStack(dev, up(lm), hidden=H, kinds=KINDS, mixers=dmix, attn_capacity=CAP)
-    # per layer four GEMVs and two mixer kernels (each mixer also writes the
-    # sums of squares the out-projection needs), then the lm_head and the
-    # position update
+    # per layer four GEMVs and the mixer's kernels (GDN one, attention two;
+    # each mixer also writes the sums of squares the out-projection needs),
+    # then the lm_head and the position update
     L = len(KINDS)
-    assert stack.nodes() == 4 * L + 2 * L + 2
+    assert stack.nodes() == 4 * L + sum(1 if k == 0 else 2 for k in KINDS) + 2
     get = lambda l, b: down(stack.buffer(l, b)).astype(np.float64)
     # oracle states for the free-running chain
     ostates = []
