@@ -232,3 +232,48 @@ def test_attn_head_groups(q4k, torch, hq, hkv):
                              kv_heads=hkv))
     ref, _, _ = oracle.attn_step(u, prm["qw"], prm["kw"], kc_h, vc_h, pos, Hq=hq, Hkv=hkv)
     _heads(out, ref, hq, 2e-4, "attn out %dx%d" % (hq, hkv))
+
+
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (1, 12)])
+def test_gdn_head_ratios(q4k, hk, hv):
+    """Value heads per key head of 1, 4 and 12 (the conv state of a key
+    head's q and k channels is read by 4, 16 and 48 workgroups; the last one
+    shifts it), two steps, state and conv state and outputs against the
+    oracle."""
+    C = (2 * hk + hv) * D
+    nu = C + hv * D + 2 * hv
+    prm = dict(conv_w=_n(31, 4 * C, 0.5), a_log=_n(32, hv, 0.5), dt_bias=_n(33, hv, 0.5),
+               norm_w=(1.0 + 0.1 * _n(34, D)).astype(np.float32))
+    dprm = {k: up(v) for k, v in prm.items()}
+    cs, S = _n(35, 3 * C), _n(36, hv * D * D, 0.05)
+    cs_d, S_d = up(cs), up(S)
+    note("gdn heads %d/%d" % (hk, hv))
+    for t in range(2):
+        u = _n(800 + t, nu)
+        cs_prev, S_prev = down(cs_d).copy(), down(S_d).copy()
+        out = down(q4k.gdn_step(up(u), dprm["conv_w"], dprm["a_log"], dprm["dt_bias"],
+                                dprm["norm_w"], cs_d, S_d, key_heads=hk, value_heads=hv))
+        ref, cs_ref, S_ref = oracle.gdn_step(u, prm["conv_w"], prm["a_log"], prm["dt_bias"],
+                                             prm["norm_w"], cs_prev, S_prev, Hk=hk, Hv=hv)
+        _close(down(cs_d), cs_ref, 0.0, "conv state %d/%d step %d" % (hk, hv, t))
+        _close(down(S_d), S_ref, 2e-5, "state %d/%d step %d" % (hk, hv, t))
+        _heads(out, ref, hv, 2e-4, "gdn out %d/%d step %d" % (hk, hv, t))
+
+
+@pytest.mark.parametrize("rope_dim", [0, 2, 256])
+def test_attn_rope_extremes(q4k, torch, rope_dim):
+    """No rotary, one rotated pair, and every dimension rotated, at a position
+    whose angles wrap many times (pos 4000 of 4096: the angle reduction
+    modulo 2 pi in double)."""
+    prm = _attn_params()
+    cap, pos = 4096, 4000
+    kc_h = _n(900, Hkv * cap * AD).reshape(Hkv, cap, AD)
+    vc_h = _n(901, Hkv * cap * AD).reshape(Hkv, cap, AD)
+    kc, vc = up(kc_h), up(vc_h)
+    u = _n(902 + rope_dim, NA)
+    note("attention rope_dim %d at position %d" % (rope_dim, pos))
+    out = down(q4k.attn_step(up(u), up(prm["qw"]), up(prm["kw"]), kc, vc, pos,
+                             rope_dim=rope_dim))
+    ref, kc_ref, _ = oracle.attn_step(u, prm["qw"], prm["kw"], kc_h, vc_h, pos, R=rope_dim)
+    _heads(out, ref, Hq, 2e-4, "attn out rope_dim %d" % rope_dim)
+    _close(down(kc)[:, pos], kc_ref[:, pos], 2e-5, "k cache rope_dim %d" % rope_dim)
