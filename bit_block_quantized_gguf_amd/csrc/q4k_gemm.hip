@@ -262,6 +262,9 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
         bf16x8 A[2][T], B[2][2];
         load_a(0, A[0]);
         make_b(0, B[0]);
+        // Block 0's LDS reads issue together: left to itself the scheduler
+        // sinks each next to its MFMA and waits for them one at a time.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             const int c = b & 1;
@@ -278,13 +281,13 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
                 acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[c][ti], B[c][1], acc[1][ti], 0, 0, 0);
             }
             if (b < 7) {
-                // interleave: each MFMA pair carries one LDS read and a share of the VALU
+                // interleave: the next block's T LDS reads ride on the first T
+                // MFMAs (so they land before the block ends) and every MFMA
+                // carries a share of the VALU
 #pragma unroll
-                for (int ti = 0; ti < T; ++ti) {
+                for (int i = 0; i < 2 * T; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                    __builtin_amdgcn_sched_group_barrier(0x002, 24 / T + 1, 0);  // VALU
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    if (i < T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                     __builtin_amdgcn_sched_group_barrier(0x002, 24 / T + 1, 0);  // VALU
                 }
             }
@@ -337,6 +340,26 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
                        : p.ws + ((int64_t)g * 2 + slot) * (BM * BN);
     const int ld = whole ? p.M : BM;
     const int cmax = whole ? p.M - row0 : BM, tmax = whole ? p.P - tok0 : BN;
+    if (cmax >= BM && tmax >= BN) {
+        // Every element of the tile is in range (partial slots always are):
+        // no per-element conditions.  Each store takes a wave-uniform token row
+        // base (scalar adds) plus the lane's fixed 32-bit byte offset (its
+        // column, and 4 token rows further for the upper half-wave); the
+        // condition-guarded form below spends a branch, a 64-bit multiply and
+        // an exec-mask spill on every store.
+        const uint32_t lofs = (uint32_t)((4 * h * ld + 64 * wave + (lane & 31)) * 4);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ti = 0; ti < T; ++ti)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tu = 32 * ti + 8 * (v >> 2) + (v & 3);  // uniform token row
+                    char *rowp = reinterpret_cast<char *>(out + (int64_t)tu * ld + 32 * r);
+                    *reinterpret_cast<float *>(rowp + lofs) = acc[r][ti][v];
+                }
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int cl = 64 * wave + 32 * r + (lane & 31);  // W row = Y column
