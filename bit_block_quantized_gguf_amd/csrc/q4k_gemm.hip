@@ -79,18 +79,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Stream-K partition: the (tile, super-block) work items, tile-major, are
-// split into G equal contiguous ranges, one per workgroup.  Tile t covers W
-// rows 256 (t mod rtiles) .. +255 and tokens BN (t div rtiles) .. +BN-1.
+// Partition of the (tile, super-block) work items, tile-major.  Tile t covers
+// W rows 256 (t mod rtiles) .. +255 and tokens BN (t div rtiles) .. +BN-1.
+// With at least G tiles and a remainder, the first dp * G tiles are handed out
+// whole (round r gives workgroup g tile r * G + g: written straight to Y), and
+// only the rest, items [U0, U), is split into G equal contiguous stream-K
+// ranges.  Otherwise dp = 0, U0 = 0 and all items are split.  Either way every
+// workgroup gets the same number of super-blocks, and at most two partial
+// tiles (its stream-K range's first and last).
 struct SKUnits {
     int nb;       // super-blocks per row (work items per tile)
     int rtiles;   // 256-row tiles
     int64_t U;    // total work items = tiles * nb
     int G;        // workgroups
-    __host__ __device__ __forceinline__ int64_t begin(int g) const { return (int64_t)g * U / G; }
-    // workgroup whose range contains item u
+    int dp;       // whole-tile rounds before the stream-K part
+    int64_t U0;   // first stream-K item = dp * G * nb
+    __host__ __device__ __forceinline__ int64_t begin(int g) const {
+        return U0 + (int64_t)g * (U - U0) / G;
+    }
+    // workgroup whose stream-K range contains item u (U0 <= u < U)
     __host__ __device__ __forceinline__ int owner(int64_t u) const {
-        return (int)(((u + 1) * (int64_t)G + U - 1) / U - 1);
+        const int64_t n = U - U0;
+        return (int)(((u - U0 + 1) * (int64_t)G + n - 1) / n - 1);
     }
 };
 
@@ -379,17 +389,29 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const 
     // buffer `half` holds X columns [256j + 128 half, +128) of the tile's tokens
     __shared__ __attribute__((aligned(1024))) __bf16 xs[2][32 * T * KS];
     const int g = blockIdx.x;
+    // the whole tiles of the data-parallel rounds, then the stream-K range's
+    // segments; one call site, so the segment body is inlined once
     const int64_t ua = su.begin(g), ub = su.begin(g + 1);
-    if (ua >= ub) return;
     const int first_tile = (int)(ua / su.nb);
+    int r = 0;
     int64_t u = ua;
-    while (u < ub) {
-        const int tile = (int)(u / su.nb);
-        const int64_t tb = (int64_t)tile * su.nb;
-        const int jb = (int)(u - tb);
-        const int je = (int)((ub < tb + su.nb ? ub : tb + su.nb) - tb);
+    while (true) {
+        int tile, jb, je;
+        if (r < su.dp) {
+            tile = r * su.G + g;
+            jb = 0;
+            je = su.nb;
+            ++r;
+        } else if (u < ub) {
+            tile = (int)(u / su.nb);
+            const int64_t tb = (int64_t)tile * su.nb;
+            jb = (int)(u - tb);
+            je = (int)((ub < tb + su.nb ? ub : tb + su.nb) - tb);
+            u = tb + je;
+        } else {
+            break;
+        }
         gemm_segment<T>(p, su, g, tile, jb, je, tile == first_tile ? 0 : 1, xs);
-        u = tb + je;
     }
 }
 
@@ -473,12 +495,21 @@ SKUnits sk_units(int64_t M, int64_t K, int64_t P, int t, int G) {
     const int64_t tiles = (int64_t)su.rtiles * ((P + 32 * t - 1) / (32 * t));
     su.U = tiles * su.nb;
     su.G = (int)std::max<int64_t>(1, std::min<int64_t>(G, su.U));
+    su.dp = 0;
+    su.U0 = 0;
+    // whole-tile rounds when there are at least G tiles, a remainder, and
+    // enough remaining items to give every workgroup one (no empty ranges)
+    const int64_t rem = tiles % su.G;
+    if (tiles > su.G && rem != 0 && rem * su.nb >= su.G && tiles / su.G <= 0x7FFFFFFF) {
+        su.dp = (int)(tiles / su.G);
+        su.U0 = (int64_t)su.dp * su.G * su.nb;
+    }
     return su;
 }
 
 // A range boundary falls inside a tile unless every range is whole tiles.
 bool has_split_tiles(const SKUnits &su) {
-    const int64_t tiles = su.U / su.nb;
+    const int64_t tiles = (su.U - su.U0) / su.nb;
     return !(tiles % su.G == 0);
 }
 }  // namespace
@@ -490,7 +521,7 @@ static void split_pieces(const SKUnits &su, int64_t &pieces, int64_t &split_tile
     split_tiles = 0;
     int64_t last_split = -1;
     for (int g = 0; g < su.G; ++g) {
-        const int64_t ua = (int64_t)g * su.U / su.G, ub = (int64_t)(g + 1) * su.U / su.G;
+        const int64_t ua = su.begin(g), ub = su.begin(g + 1);
         if (ua >= ub) continue;
         const int64_t t0 = ua / su.nb, t1 = (ub - 1) / su.nb;
         const bool cut0 = ua % su.nb != 0 || (t0 == t1 && ub % su.nb != 0);
@@ -507,12 +538,14 @@ static void split_pieces(const SKUnits &su, int64_t &pieces, int64_t &split_tile
 }
 
 // Tile width and workgroup count.  Every workgroup holds a CU to itself (LDS
-// and register file).  The cost model takes the longest range (work items
-// times the measured time of one super-block of one tile at that width),
-// plus, when some tile is cut, the partial tiles a workgroup writes (at about
-// 32 GB/s per CU with every CU writing) and the fix-up launch with its
-// traffic (partials read, Y written; about 12 TB/s measured, the partials
-// being still in cache).
+// and register file).  The cost model takes the longest range (work items,
+// whole-tile rounds included, times the time of one super-block of one tile
+// at that width), plus, when some tile is cut, the partial tiles a workgroup
+// writes (about 48 GB/s per CU with every CU writing) and the fix-up launch
+// with its traffic (partials read, Y written; about 12 TB/s, the partials
+// being still in cache).  The constants are a least-squares fit to measured
+// calls at 128 and 256 tokens on both MLP shapes at P = 256, 512 and 1024,
+// constrained to rank the two widths as the measurements do.
 GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P) {
     const int ot = g_override_t.load(), og = g_override_ks.load();
     const int G = og > 0 ? og : device_cus();
@@ -523,14 +556,14 @@ GemmLaunch choose_gemm_launch(int64_t M, int64_t K, int64_t P) {
         const SKUnits su = sk_units(M, K, P, t, G);
         // one super-block of one tile (measured): the dequantisation costs the
         // same at every width, the MFMA work grows with it
-        const double item_us = t == 8 ? 8.4 : t == 4 ? 5.0 : t == 2 ? GEMM_T2_US : GEMM_T1_US;
-        const int64_t per = (su.U + su.G - 1) / su.G;
+        const double item_us = t == 8 ? 6.9 : t == 4 ? 4.2 : t == 2 ? GEMM_T2_US : GEMM_T1_US;
+        const int64_t per = (int64_t)su.dp * su.nb + (su.U - su.U0 + su.G - 1) / su.G;
         double cost = per * item_us;
         if (has_split_tiles(su)) {
             int64_t pieces, split_tiles;
             split_pieces(su, pieces, split_tiles);
             const double tile_bytes = (double)BM * 32 * t * 4;
-            cost += (double)(pieces + su.G - 1) / su.G * tile_bytes / 32.0e3 + 3.0 +
+            cost += (double)(pieces + su.G - 1) / su.G * tile_bytes / 48.0e3 + 3.0 +
                     (double)(pieces + split_tiles) * tile_bytes / 12.0e6;
         }
         if (cost < best_cost - 1e-9) {
@@ -629,7 +662,22 @@ int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int g
     const int64_t ptok = padded_tokens(P);
     if ((int64_t)gemm_xb_floats(K, P) * 2 < ptok * K)
         return fail(Q4K_EINVAL, "check: bf16 X copy smaller than its padded tokens");
-    int64_t prev = 0;
+    if (su.U0 != (int64_t)su.dp * su.G * su.nb || su.U0 > su.U || su.U0 % su.nb != 0)
+        return fail(Q4K_EINVAL, "check: %d whole-tile rounds do not end at item %lld",
+                    su.dp, (long long)su.U0);
+    // whole tiles r * G + g of the data-parallel rounds: in range, tokens
+    // inside the padded copy, written straight to Y (no partial slot)
+    for (int r = 0; r < su.dp; ++r)
+        for (int g = 0; g < su.G; ++g) {
+            const int64_t tile = (int64_t)r * su.G + g;
+            if ((tile + 1) * su.nb > su.U0)
+                return fail(Q4K_EINVAL, "check: round %d tile %lld past the rounds", r,
+                            (long long)tile);
+            if ((tile / su.rtiles + 1) * BN > ptok)
+                return fail(Q4K_EINVAL, "check: tile %lld reads tokens past the padded copy",
+                            (long long)tile);
+        }
+    int64_t prev = su.U0;
     for (int g = 0; g < su.G; ++g) {
         const int64_t ua = su.begin(g), ub = su.begin(g + 1);
         if (ua != prev || ub <= ua)

@@ -216,15 +216,17 @@ def _check_gemm(Y, w, X, M, K, rows, toks, what):
         assert c >= COS_MIN, "%s token %d cosine %.9f" % (what, t, c)
 
 
-@pytest.mark.parametrize("tile,wg", [(0, 0), (32, 1), (32, 5), (64, 2), (64, 9), (128, 1), (128, 3),
-                                     (256, 1), (256, 2), (256, 7)])
+@pytest.mark.parametrize("tile,wg", [(0, 0), (32, 1), (32, 4), (32, 5), (64, 2), (64, 9), (128, 1),
+                                     (128, 3), (256, 1), (256, 2), (256, 7)])
 @pytest.mark.parametrize("M,K,P", [(300, 512, 1), (300, 512, 7), (128, 256, 128), (129, 768, 130),
                                    (520, 1024, 200), (64, 4096, 33), (257, 2048, 257),
                                    (256, 1280, 128)])
 def test_gemm_small(q4k, M, K, P, tile, wg):
     """Ragged rows and tokens around both tile widths; stream-K grids of one
-    workgroup (everything in one range), and a few workgroups whose ranges
-    cut tiles at odd super-block offsets (0: automatic)."""
+    workgroup (everything in one range), a few workgroups whose ranges cut
+    tiles at odd super-block offsets, and grids with fewer workgroups than
+    tiles, where whole-tile rounds come before the stream-K ranges (32 tokens
+    on 4 workgroups; 0: automatic)."""
     w, _ = _case(5, M + P, M, K)
     X = synth.activations(5, P, K, first=M)
     note("gemm %dx%d P=%d tile=%d wg=%d" % (M, K, P, tile, wg))
