@@ -416,20 +416,31 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const 
 }
 
 // Cut tiles: Y = sum of the contributors' partial tiles, in workgroup order
-// (ascending K).  blockIdx.x + 1 = range boundary b; the tile it falls in is
-// fixed up by the first boundary that cuts it, so whole tiles launch nothing
-// and no tile is done twice.  blockIdx.y: FT tokens of the tile; thread:
-// one column, FT independent loads per contributor.
+// (ascending K).  by_tile: blockIdx.x is a tile of the stream-K part (fewer
+// such tiles than range boundaries), and a tile inside one range exits.
+// Otherwise blockIdx.x + 1 = range boundary b; the tile it falls in is fixed
+// up by the first boundary that cuts it.  Either way whole tiles do nothing
+// and no tile is done twice.  blockIdx.y: FT tokens of the tile; thread: one
+// column, FT independent loads per contributor.
 constexpr int FT = 8;
 template <int T>
-__global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmParams p, const SKUnits su) {
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmParams p, const SKUnits su,
+                                                         int by_tile) {
     constexpr int BN = 32 * T;
-    const int bnd = blockIdx.x + 1;
-    const int64_t ub = su.begin(bnd);
-    const int tile = (int)(ub / su.nb);
-    const int64_t tb = (int64_t)tile * su.nb;
-    if (ub == tb || su.begin(bnd - 1) > tb) return;  // not a cut, or cut by an earlier boundary
+    int tile;
+    int64_t tb;
+    if (by_tile) {
+        tile = (int)(su.U0 / su.nb) + (int)blockIdx.x;
+        tb = (int64_t)tile * su.nb;
+    } else {
+        const int bnd = blockIdx.x + 1;
+        const int64_t ub = su.begin(bnd);
+        tile = (int)(ub / su.nb);
+        tb = (int64_t)tile * su.nb;
+        if (ub == tb || su.begin(bnd - 1) > tb) return;  // not a cut, or cut by an earlier boundary
+    }
     const int gf = su.owner(tb), gl = su.owner(tb + su.nb - 1);
+    if (gf == gl) return;  // inside one range: written to Y by its workgroup
     const int rt = tile % su.rtiles, tt = tile / su.rtiles;
     const int cl = threadIdx.x;  // column of the tile
     const int col = rt * BM + cl;
@@ -629,12 +640,15 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     }
     Q4K_HIP(hipGetLastError());
     if (has_split_tiles(su)) {  // implies G >= 2: there are G - 1 range boundaries
-        const dim3 fg((unsigned)(su.G - 1), (unsigned)(32 * L.r / FT));
+        // one x-group per stream-K tile when they are fewer than the boundaries
+        const int64_t sk_tiles = (su.U - su.U0) / su.nb;
+        const int by_tile = sk_tiles < su.G - 1 ? 1 : 0;
+        const dim3 fg((unsigned)(by_tile ? sk_tiles : su.G - 1), (unsigned)(32 * L.r / FT));
         switch (L.r) {
-            case 8: hipLaunchKernelGGL(gemm_fixup_kernel<8>, fg, dim3(256), 0, stream, p, su); break;
-            case 4: hipLaunchKernelGGL(gemm_fixup_kernel<4>, fg, dim3(256), 0, stream, p, su); break;
-            case 2: hipLaunchKernelGGL(gemm_fixup_kernel<2>, fg, dim3(256), 0, stream, p, su); break;
-            default: hipLaunchKernelGGL(gemm_fixup_kernel<1>, fg, dim3(256), 0, stream, p, su); break;
+            case 8: hipLaunchKernelGGL(gemm_fixup_kernel<8>, fg, dim3(256), 0, stream, p, su, by_tile); break;
+            case 4: hipLaunchKernelGGL(gemm_fixup_kernel<4>, fg, dim3(256), 0, stream, p, su, by_tile); break;
+            case 2: hipLaunchKernelGGL(gemm_fixup_kernel<2>, fg, dim3(256), 0, stream, p, su, by_tile); break;
+            default: hipLaunchKernelGGL(gemm_fixup_kernel<1>, fg, dim3(256), 0, stream, p, su, by_tile); break;
         }
         Q4K_HIP(hipGetLastError());
     }
@@ -707,9 +721,10 @@ int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int g
     }
     if (prev != su.U) return fail(Q4K_EINVAL, "check: ranges end at %lld of %lld items",
                                   (long long)prev, (long long)su.U);
-    for (int bnd = 1; bnd < su.G; ++bnd) {  // the fix-up's view
-        const int64_t ub = su.begin(bnd), tile = ub / su.nb, tb = tile * su.nb;
-        if (ub == tb || su.begin(bnd - 1) > tb) continue;
+    // the fix-up's two views (per range boundary, per stream-K tile) must
+    // find the same cut tiles, each read from contributors that wrote it
+    auto check_cut = [&](int64_t tile) -> int {
+        const int64_t tb = tile * su.nb;
         const int gf = su.owner(tb), gl = su.owner(tb + su.nb - 1);
         if (gf >= gl) return fail(Q4K_EINVAL, "check: cut tile %lld has one contributor",
                                   (long long)tile);
@@ -722,7 +737,24 @@ int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int g
                 return fail(Q4K_EINVAL, "check: fix-up of tile %lld reads workgroup %d slot %d "
                             "that it did not write", (long long)tile, w, slot);
         }
+        return Q4K_OK;
+    };
+    int64_t cut_by_boundary = 0, cut_by_tile = 0;
+    for (int bnd = 1; bnd < su.G; ++bnd) {
+        const int64_t ub = su.begin(bnd), tile = ub / su.nb, tb = tile * su.nb;
+        if (ub == tb || su.begin(bnd - 1) > tb) continue;
+        if (int rc = check_cut(tile)) return rc;
+        ++cut_by_boundary;
     }
+    for (int64_t tile = su.U0 / su.nb; tile < su.U / su.nb; ++tile) {
+        const int64_t tb = tile * su.nb;
+        if (su.owner(tb) == su.owner(tb + su.nb - 1)) continue;
+        if (int rc = check_cut(tile)) return rc;
+        ++cut_by_tile;
+    }
+    if (cut_by_boundary != cut_by_tile)
+        return fail(Q4K_EINVAL, "check: %lld tiles cut by range boundaries, %lld by owners",
+                    (long long)cut_by_boundary, (long long)cut_by_tile);
     return Q4K_OK;
 }
 
