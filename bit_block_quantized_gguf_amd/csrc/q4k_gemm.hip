@@ -164,6 +164,10 @@ template <int T>
 __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits &su, int g,
                                              int tile, int jb, int je, int slot,
                                              __bf16 (*xs)[32 * T * KS]) {
+    // X buffers: two (half-blocks alternate) for 256-token tiles; four for
+    // narrower tiles (buffer 2 (j mod 2) + half: both halves of the next
+    // super-block are copied while this one computes, one wait per super-block)
+    constexpr int NBUF = T <= 4 ? 4 : 2;
     constexpr int BN = 32 * T;
     // opaque per segment: nothing derived from the thread index is hoisted out
     // of the caller's segment loop and kept live across the main loop
@@ -199,11 +203,11 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     // k (0: header, 1..4: quant group k-1) of super-block j, row group r, into
     // w.  Issued a few per MFMA block (see compute): a burst of them at once
     // stalls the wave on the memory pipeline's queue.
-    auto copy_x = [&](int j, int half, int i) {
+    auto copy_x = [&](int j, int half, int buf, int i) {
         const int64_t kbyte = ((int64_t)j * 256 + 128 * half) * 2;
         const int b = 4 * i + wave;
         const char *src = xbase + (int64_t)16 * i * p.K * 2 + kbyte;
-        __builtin_amdgcn_global_load_lds((gvoid *)(src + xoff), (lvoid *)&xs[half][b * 4 * KS], 16,
+        __builtin_amdgcn_global_load_lds((gvoid *)(src + xoff), (lvoid *)&xs[buf][b * 4 * KS], 16,
                                          0, 0);
     };
     auto load_w = [&](int j, int r, int k, WBlock (&w)[2]) {
@@ -234,8 +238,12 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     // While computing, block b also issues X copy instructions of step
     // (xj, 1 - half) into the other buffer and (b < 5) W word b of row group
     // `half` of super-block wj into wn.
-    auto compute = [&](int half, const WBlock (&wc)[2], int xj, int wj, WBlock (&wn)[2]) {
-        const __bf16 *xb = &xs[half][arow];
+    // half-block step `half` of the current super-block, from LDS buffer
+    // rbuf; copies X of step (cj, chalf) into buffer cbuf and loads row group
+    // `half` of super-block wj's W into wn
+    auto compute = [&](int half, const WBlock (&wc)[2], int rbuf, int cj, int chalf, int cbuf,
+                       int wj, WBlock (&wn)[2]) {
+        const __bf16 *xb = &xs[rbuf][arow];
         float ds[2][2][2], dm[2][2][2];  // [gg][r][lo/hi sub-block]
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -279,7 +287,7 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
         for (int b = 0; b < 8; ++b) {
             const int c = b & 1;
 #pragma unroll
-            for (int i = b * XI / 8; i < (b + 1) * XI / 8; ++i) copy_x(xj, 1 - half, i);
+            for (int i = b * XI / 8; i < (b + 1) * XI / 8; ++i) copy_x(cj, chalf, cbuf, i);
             if (b < 5) load_w(wj, half, b, wn);
             if (b < 7) {
                 load_a(b + 1, A[c ^ 1]);
@@ -315,7 +323,11 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     WBlock wa[2], wb[2];
     if (jb < je) {
 #pragma unroll
-        for (int i = 0; i < XI; ++i) copy_x(jb, 0, i);
+        for (int i = 0; i < XI; ++i) copy_x(jb, 0, NBUF == 4 ? 2 * (jb & 1) : 0, i);
+        if constexpr (NBUF == 4) {
+#pragma unroll
+            for (int i = 0; i < XI; ++i) copy_x(jb, 1, 2 * (jb & 1) + 1, i);
+        }
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -324,22 +336,43 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     step_end();
     const int last = p.nb - 1;
     int j = jb;
-    for (; j + 1 < je; j += 2) {
-        const int j2 = j + 2 < p.nb ? j + 2 : last;
-        compute(0, wa, j, j + 1, wb);
-        step_end();
-        compute(1, wa, j + 1, j + 1, wb);
-        step_end();
-        compute(0, wb, j + 1, j2, wa);
-        step_end();
-        compute(1, wb, j2, j2, wa);
-        step_end();
-    }
-    if (j < je) {  // odd count: super-block je-1; its X half 0 and W (set wa) are in place
-        compute(0, wa, j, j, wb);
-        step_end();
-        compute(1, wa, j, j, wb);
-        step_end();
+    if constexpr (NBUF == 4) {
+        // super-block j reads buffers 2 (j & 1) + h and fills those of j + 1
+        // (copies past the segment's end re-read an in-range block, unused)
+        for (; j + 1 < je; j += 2) {
+            const int j1 = j + 1, j2 = j + 2 < p.nb ? j + 2 : last;
+            const int bj = 2 * (j & 1), bn = 2 - bj;
+            compute(0, wa, bj, j1, 0, bn, j1, wb);
+            compute(1, wa, bj + 1, j1, 1, bn + 1, j1, wb);
+            step_end();
+            compute(0, wb, bn, j2, 0, bj, j2, wa);
+            compute(1, wb, bn + 1, j2, 1, bj + 1, j2, wa);
+            step_end();
+        }
+        if (j < je) {  // odd count: super-block je-1 (X and W set wa in place)
+            const int bj = 2 * (j & 1), bn = 2 - bj;
+            compute(0, wa, bj, j, 0, bn, j, wb);
+            compute(1, wa, bj + 1, j, 1, bn + 1, j, wb);
+            step_end();
+        }
+    } else {
+        for (; j + 1 < je; j += 2) {
+            const int j2 = j + 2 < p.nb ? j + 2 : last;
+            compute(0, wa, 0, j, 1, 1, j + 1, wb);
+            step_end();
+            compute(1, wa, 1, j + 1, 0, 0, j + 1, wb);
+            step_end();
+            compute(0, wb, 0, j + 1, 1, 1, j2, wa);
+            step_end();
+            compute(1, wb, 1, j2, 0, 0, j2, wa);
+            step_end();
+        }
+        if (j < je) {  // odd count: super-block je-1; its X half 0 and W (set wa) are in place
+            compute(0, wa, 0, j, 1, 1, j, wb);
+            step_end();
+            compute(1, wa, 1, j, 0, 0, j, wb);
+            step_end();
+        }
     }
 
     // ---- epilogue ----
@@ -386,8 +419,8 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
 
 template <int T>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const SKUnits su) {
-    // buffer `half` holds X columns [256j + 128 half, +128) of the tile's tokens
-    __shared__ __attribute__((aligned(1024))) __bf16 xs[2][32 * T * KS];
+    // X buffers of the tile's tokens, 128 columns (half a super-block) each
+    __shared__ __attribute__((aligned(1024))) __bf16 xs[T <= 4 ? 4 : 2][32 * T * KS];
     const int g = blockIdx.x;
     // the whole tiles of the data-parallel rounds, then the stream-K range's
     // segments; one call site, so the segment body is inlined once
