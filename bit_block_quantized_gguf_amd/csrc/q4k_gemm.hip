@@ -21,7 +21,9 @@
 //  * K advances half a super-block (128 columns, quant groups g0, g0+1) per
 //    step.  The step's X slice (32T tokens x 128 columns of bf16) is copied
 //    from global memory straight into LDS with global_load_lds_dwordx4, so
-//    it never occupies registers; it is double-buffered.  Each token row is
+//    it never occupies registers; it is double-buffered (256-token tiles) or
+//    held in four buffers, both halves of the next super-block copied while
+//    this one computes (narrower tiles: one wait per super-block).  Each token row is
 //    256 bytes = 16 chunks of 16 bytes and chunk c of token t is stored at
 //    slot c ^ (t & 15), so the 32 lanes of a fragment read (32 consecutive
 //    tokens, one chunk) cover all banks.
