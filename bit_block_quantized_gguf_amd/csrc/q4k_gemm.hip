@@ -154,14 +154,14 @@ struct WBlock {
 };
 
 // One workgroup: 256 W rows x 32T tokens.  See the file comment for the
-// fragment layout.  Pipeline: while half-block step s is computed from one LDS
-// buffer, the X slice of step s+1 is copied into the other buffer, and the W
+// fragment layout.  Pipeline: while a half-block step is computed from one LDS
+// buffer, the X slice of a later step is copied into another buffer, and the W
 // bytes of the next super-block are loaded into the other register set; the
 // copies are spread over the step's MFMA blocks.
 // One segment: super-blocks [jb, je) of tile `tile`.  A whole tile is written
 // to Y; a part of a tile goes to the workgroup's partial slot (0: the first
-// tile of its range, 1: the last) for the fix-up kernel.  xs: the two LDS X
-// buffers (BN tokens x 128 columns each).
+// tile of its range, 1: the last) for the fix-up kernel.  xs: the LDS X
+// buffers (BN tokens x 128 columns each; two or four, see NBUF).
 template <int T>
 __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits &su, int g,
                                              int tile, int jb, int je, int slot,
@@ -232,17 +232,14 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[r][i][v] = 0.f;
 
-    // Half-block step (quant groups 2 half, 2 half + 1) from LDS buffer buf, in
-    // eight blocks b = (gg, f): block b reads T A fragments (X at column offset
-    // cst(b)) and dequantises two B fragments (one per row group), then issues
-    // 2T MFMAs.  Block b+1's LDS reads and dequantisation are issued in the
-    // shadow of block b's MFMAs (software pipeline).
+    // Half-block step `half` (quant groups 2 half, 2 half + 1) from LDS buffer
+    // rbuf, in eight blocks b = (gg, f): block b reads T A fragments (X at
+    // column offset cst(b)) and dequantises two B fragments (one per row
+    // group), then issues 2T MFMAs.  Block b+1's LDS reads and dequantisation
+    // are issued in the shadow of block b's MFMAs (software pipeline).
     // While computing, block b also issues X copy instructions of step
-    // (xj, 1 - half) into the other buffer and (b < 5) W word b of row group
-    // `half` of super-block wj into wn.
-    // half-block step `half` of the current super-block, from LDS buffer
-    // rbuf; copies X of step (cj, chalf) into buffer cbuf and loads row group
-    // `half` of super-block wj's W into wn
+    // (cj, chalf) into buffer cbuf and (b < 5) W word b of row group `half` of
+    // super-block wj into wn.
     auto compute = [&](int half, const WBlock (&wc)[2], int rbuf, int cj, int chalf, int cbuf,
                        int wj, WBlock (&wn)[2]) {
         const __bf16 *xb = &xs[rbuf][arow];
