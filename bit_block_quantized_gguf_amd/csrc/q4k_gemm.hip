@@ -482,14 +482,27 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(const GemmParams p, con
     float s[FT];
 #pragma unroll
     for (int i = 0; i < FT; ++i) s[i] = 0.f;
-    for (int w = gf; w <= gl; ++w) {
-        const int slot = su.begin(w) / su.nb == tile ? 0 : 1;
-        const float *src = p.ws + ((int64_t)w * 2 + slot) * (BM * BN) + (int64_t)tl0 * BM + cl;
-        float v[FT];
+    // FC contributors per round with all their loads in flight together: a
+    // tile cut among many workgroups (a long K on few tiles) would otherwise
+    // pay one memory round trip per contributor.  Additions stay in
+    // contributor order.
+    constexpr int FC = 4;
+    for (int w0 = gf; w0 <= gl; w0 += FC) {
+        float v[FC][FT];
 #pragma unroll
-        for (int i = 0; i < FT; ++i) v[i] = src[i * BM];
+        for (int c = 0; c < FC; ++c) {
+            const int w = w0 + c <= gl ? w0 + c : gl;  // past gl: loaded, not added
+            const int slot = su.begin(w) / su.nb == tile ? 0 : 1;
+            const float *src = p.ws + ((int64_t)w * 2 + slot) * (BM * BN) + (int64_t)tl0 * BM + cl;
 #pragma unroll
-        for (int i = 0; i < FT; ++i) s[i] += v[i];
+            for (int i = 0; i < FT; ++i) v[c][i] = src[i * BM];
+        }
+#pragma unroll
+        for (int c = 0; c < FC; ++c)
+            if (w0 + c <= gl) {
+#pragma unroll
+                for (int i = 0; i < FT; ++i) s[i] += v[c][i];
+            }
     }
 #pragma unroll
     for (int i = 0; i < FT; ++i)
