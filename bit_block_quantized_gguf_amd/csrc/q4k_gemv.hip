@@ -983,7 +983,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p
 // unit loop, same in-kernel finishing of cut tiles).  Between nodes:
 //   * the workgroup loads its first unit of the next node into LDS and issues
 //     the loads of its second unit, then waits until every workgroup has
-//     finished the current node (a counter per node; weights do not depend on
+//     finished the current node (16 counters per node, workgroup g counting
+//     into counter g mod 16 so arrivals do not queue on one address; weights do not depend on
 //     activations, so the memory pipe keeps streaming across the boundary);
 //   * outputs are written with device-coherent (sc1) stores and each
 //     workgroup counts itself in only after its stores have completed, so
@@ -1012,12 +1013,24 @@ __device__ __forceinline__ T *as_global(T *p) {
     return (T *)(__attribute__((address_space(1))) T *)(uintptr_t)p;
 }
 
-__device__ __forceinline__ void wait_arrivals(unsigned *c, unsigned target, int spin_limit,
-                                              unsigned *err) {
+// Wave 0 waits until every workgroup has counted itself in on the node's
+// kStackSyncLanes counters (lane l reads counter l, which workgroups
+// g = l mod kStackSyncLanes increment once per token); bounded by spin_limit
+// polls, after which the error word is set and the wait gives up.
+__device__ __forceinline__ void wait_arrivals(unsigned *c, unsigned epoch, int G, int lane,
+                                              int spin_limit, unsigned *err) {
+    constexpr int NS = kStackSyncLanes;
+    const bool mine = lane < NS;
+    const unsigned target = mine ? (epoch + 1u) * (unsigned)((G - lane + NS - 1) / NS) : 0u;
     int i = 0;
-    while ((int)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+    while (true) {
+        bool ok = true;
+        if (mine)
+            ok = (int)(__hip_atomic_load(c + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       target) >= 0;
+        if (__all(ok)) return;
         if (++i > spin_limit) {
-            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -1115,7 +1128,8 @@ __global__ __launch_bounds__(64 * WK) void stack_kernel(const StackNode *__restr
                 fetch(lt ? t + 1 : t, lt ? 0 : k + 1);
             }
         }
-        if (n > 0 && tid == 0) wait_arrivals(&done[n - 1], (epoch + 1u) * G, spin_limit, err);
+        if (n > 0 && wave == 0)
+            wait_arrivals(&done[(n - 1) * kStackSyncLanes], epoch, (int)G, lane, spin_limit, err);
         __syncthreads();
         if (have) {
             const float inv = epi == EPI_PLAIN ? 1.f : inv_rms(p, lane);
@@ -1167,7 +1181,8 @@ __global__ __launch_bounds__(64 * WK) void stack_kernel(const StackNode *__restr
         if (wave == 0) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             if (lane == 0)
-                __hip_atomic_fetch_add(&done[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&done[n * kStackSyncLanes + (g % kStackSyncLanes)], 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

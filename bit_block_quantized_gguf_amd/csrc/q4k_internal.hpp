@@ -112,6 +112,11 @@ int launch_gemv_q6(const GemvParams &p, const GemvLaunch &L, hipStream_t stream)
 int gemv_noalloc(const void *w, const float *x, float *y, int64_t M, int64_t K,
                  hipStream_t stream);
 
+// Arrival counters per node of the persistent decode kernel: workgroup g
+// counts into counter g mod kStackSyncLanes, so the arrivals at a node
+// boundary spread over that many addresses; the node's wait reads them all.
+constexpr int kStackSyncLanes = 16;
+
 // Persistent decode kernel (q4k_gemv.hip): grid size (co-resident
 // workgroups, at most two per CU), node descriptor size, filling one node
 // descriptor (host memory), and the cooperative launch over n_nodes nodes.

@@ -73,8 +73,8 @@ struct q4k_stack {
     bool persistent = false;
     int pgroups = 0;                  // co-resident workgroups of the kernel
     void *pnodes = nullptr;           // node descriptors (device)
-    unsigned *psync = nullptr;        // per-node arrival counters, then the error word
-    unsigned epoch = 0;               // tokens launched (counters grow by pgroups each)
+    unsigned *psync = nullptr;        // kStackSyncLanes arrival counters per node, then the error word
+    unsigned epoch = 0;               // tokens launched (each node's counters grow by pgroups in all)
     int spin = 1 << 20;               // polls before a wait gives up
 };
 
@@ -475,7 +475,7 @@ int q4k_decode_stack_create(const q4k_stack_desc *d, void *stream, q4k_stack **o
             release(s);
             return rc;
         }
-        const size_t sync_bytes = ((size_t)nodes + 1) * sizeof(unsigned);
+        const size_t sync_bytes = ((size_t)nodes * kStackSyncLanes + 1) * sizeof(unsigned);
         if (hipMalloc(&s->pnodes, pn.size()) != hipSuccess ||
             hipMalloc(&s->psync, sync_bytes) != hipSuccess) {
             (void)hipGetLastError();
@@ -543,7 +543,8 @@ int q4k_decode_stack(q4k_stack *s, const float *h_in, float *logits, void *strea
                            hipMemcpyDeviceToDevice, st));
     if (s->persistent) {
         const int rc = launch_stack_kernel(s->pnodes, (int)s->n_nodes, s->psync, s->epoch,
-                                           s->psync + s->n_nodes, s->spin, s->pgroups, st);
+                                           s->psync + s->n_nodes * kStackSyncLanes, s->spin,
+                                           s->pgroups, st);
         if (rc) return rc;
         ++s->epoch;
     } else {
@@ -577,12 +578,13 @@ int q4k_decode_stack_status(q4k_stack *s, void *stream, int32_t *status) {
     hipStream_t st = (hipStream_t)stream;
     unsigned word = 0;
     Q4K_HIP(hipStreamSynchronize(st));
-    Q4K_HIP(hipMemcpy(&word, s->psync + s->n_nodes, sizeof word, hipMemcpyDeviceToHost));
+    unsigned *errw = s->psync + s->n_nodes * kStackSyncLanes;
+    Q4K_HIP(hipMemcpy(&word, errw, sizeof word, hipMemcpyDeviceToHost));
     if (word) {
         // A workgroup that gave up may have run into the next node while its
         // tiles were still being finished, leaving split-tile counters off
         // zero: clear them with the record, so later tokens are sound.
-        Q4K_HIP(hipMemset(s->psync + s->n_nodes, 0, sizeof word));
+        Q4K_HIP(hipMemset(errw, 0, sizeof word));
         Q4K_HIP(hipMemset(s->ws.counters, 0, kCounterBytes));
     }
     Q4K_HIP(hipDeviceSynchronize());

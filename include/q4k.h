@@ -354,7 +354,7 @@ int q4k_attn_step(const q4k_attn_params *p, const float *u, float *k_cache, floa
  * With Q4K_STACK_PERSISTENT in flags (stand-in mixer only) a token is ONE
  * cooperative kernel instead of a graph of kernels: every workgroup walks
  * the whole node list, loads its share of the next matrix while it waits for
- * the current one to finish (a counter per node), and hands activations over
+ * the current one to finish (16 arrival counters per node), and hands activations over
  * through device-coherent stores.  The arithmetic of every node is that of
  * the graph plan, so both give the same logits bit for bit.  Each wait is
  * bounded (spin_limit polls, default 2^20); a wait that runs out records an
