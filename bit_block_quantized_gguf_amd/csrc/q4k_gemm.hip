@@ -421,15 +421,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const 
     // X buffers of the tile's tokens, 128 columns (half a super-block) each
     __shared__ __attribute__((aligned(1024))) __bf16 xs[T <= 4 ? 4 : 2][32 * T * KS];
     const int g = blockIdx.x;
-    // the whole tiles of the data-parallel rounds, then the stream-K range's
-    // segments; one call site, so the segment body is inlined once
+    // the whole tiles of the data-parallel rounds and the stream-K range's
+    // segments: even workgroups take the whole tiles first, odd ones the
+    // stream-K range first, so that the tile stores of the two halves of the
+    // grid do not all fall at the same moment.  One call site, so the segment
+    // body is inlined once.
     const int64_t ua = su.begin(g), ub = su.begin(g + 1);
     const int first_tile = (int)(ua / su.nb);
+    const bool sk_first = (g & 1) != 0;
     int r = 0;
     int64_t u = ua;
     while (true) {
         int tile, jb, je;
-        if (r < su.dp) {
+        if (r < su.dp && !(sk_first && u < ub)) {
             tile = r * su.G + g;
             jb = 0;
             je = su.nb;
@@ -440,6 +444,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p, const 
             jb = (int)(u - tb);
             je = (int)((ub < tb + su.nb ? ub : tb + su.nb) - tb);
             u = tb + je;
+        } else if (r < su.dp) {
+            tile = r * su.G + g;
+            jb = 0;
+            je = su.nb;
+            ++r;
         } else {
             break;
         }
