@@ -243,11 +243,13 @@ int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K
  * Prefill GEMM:  Y[p][i] = sum_k w_ik * X[p][k],  X f32 [P][K], Y f32 [P][M].
  * The prompt-phase matmul ("Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §2
  * prefill phases and §4b; "Qwen3.6-27B on Apple M3 Pro — the llama.cpp
- * parity bar", the compute-bound prefill argument).  Weight tiles are
- * dequantised to bf16 (round to nearest even) in LDS, X is rounded to bf16,
- * products accumulate in f32 on the matrix cores; |y - exact| stays within
- * 5e-3 * sum_k |w_ik x_pk| + 1e-6.  Workspace (the bf16 copy of X and the
- * partial tiles of stream-K): q4k_workspace_size(Q4K_OP_GEMM, M, K, P).
+ * parity bar", the compute-bound prefill argument).  Each weight is
+ * dequantised exactly and rounded to bf16 (round to nearest even) straight
+ * into a matrix-core fragment in registers, X is rounded to bf16 and staged
+ * in LDS, products accumulate in f32 on the matrix cores; |y - exact| stays
+ * within 5e-3 * sum_k |w_ik x_pk| + 1e-6.  The result is deterministic for a
+ * given shape and device.  Workspace (the bf16 copy of X and the partial
+ * tiles of stream-K): q4k_workspace_size(Q4K_OP_GEMM, M, K, P).
  * Errors as q4k_gemv.
  */
 int q4k_gemm(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t P,
