@@ -127,24 +127,30 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q0, uint32_t q1, float ds, f
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// Xb[t][k] = bf16(X[t][k]) for t < P, 0 for P <= t < Pp.  Four elements per thread.
+// Xb[t][k] = bf16(X[t][k]) for t < P, 0 for P <= t < Pp.  Eight elements per
+// thread (two 16-byte loads, one 16-byte store); n_pad is a multiple of 8.
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ X,
                                                       __bf16 *__restrict__ Xb, int64_t n,
                                                       int64_t n_pad) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i >= n_pad) return;
-    bf16x4 b;
-    if (i + 3 < n) {
-        const float4 v = *reinterpret_cast<const float4 *>(X + i);
-        b[0] = (__bf16)v.x;
-        b[1] = (__bf16)v.y;
-        b[2] = (__bf16)v.z;
-        b[3] = (__bf16)v.w;
+    bf16x8 b;
+    if (i + 7 < n) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(X + i);
+        const float4 v1 = *reinterpret_cast<const float4 *>(X + i + 4);
+        b[0] = (__bf16)v0.x;
+        b[1] = (__bf16)v0.y;
+        b[2] = (__bf16)v0.z;
+        b[3] = (__bf16)v0.w;
+        b[4] = (__bf16)v1.x;
+        b[5] = (__bf16)v1.y;
+        b[6] = (__bf16)v1.z;
+        b[7] = (__bf16)v1.w;
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = (__bf16)(i + e < n ? X[i + e] : 0.f);
+        for (int e = 0; e < 8; ++e) b[e] = (__bf16)(i + e < n ? X[i + e] : 0.f);
     }
-    *reinterpret_cast<bf16x4 *>(Xb + i) = b;
+    *reinterpret_cast<bf16x8 *>(Xb + i) = b;
 }
 
 // W bytes of one super-block for one 32-row group: the block header and the
@@ -676,7 +682,7 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     __bf16 *xb = reinterpret_cast<__bf16 *>(ws.partials + gemm_partial_floats(L, M, P));
     p.Xb = xb;
     const int64_t n = P * K, n_pad = padded_tokens(P) * K;
-    const int64_t cgroups = (n_pad / 4 + 255) / 256;
+    const int64_t cgroups = (n_pad / 8 + 255) / 256;
     if (cgroups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: X too large");
     hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)cgroups), dim3(256), 0, stream, X, xb, n,
                        n_pad);
