@@ -30,11 +30,12 @@
 //  * W never goes through LDS: lane l handles row l%32 of each of its row
 //    groups and half h = l/32 of every 32-byte quant group.  Its 16 quant
 //    bytes hold 16 low-nibble weights (sub-block 2g) and 16 high-nibble
-//    weights (sub-block 2g+1); each run of 8 converts (w = fma(q, d*sc,
-//    -dmin*m), exact in f32, then bf16 RNE) into one B fragment.  A fragment
-//    may pair any 8 columns per lane as long as X is read at the same
-//    columns, so the lane's column offset is 64g + 32*hi + 16h + 8t and the
-//    A fragment (X) is read from LDS at that offset.  The next step's W bytes
+//    weights (sub-block 2g+1); each run of 8 converts (w = d*sc*q - dmin*m,
+//    exact in f32 by one v_fma_mix_f32 per weight, then bf16 RNE) into one B
+//    fragment.  A fragment may pair any 8 columns per lane as long as X is
+//    read at the same columns, so the lane's column offset is
+//    64g + 32*hi + 16h + 8t and the A fragment (X) is read from LDS at that
+//    offset.  The next step's W bytes
 //    are loaded into registers while the current step computes.
 //  * Output layout of the 32x32 MFMA: lane l holds column l%32 (a W row) and
 //    rows 8(v/4) + 4(l/32) + v%4 (tokens) of accumulator v, so each store
@@ -116,14 +117,44 @@ struct GemmParams {
     float *ws;
 };
 
-// Eight weights q[0..7] (bytes of q0, q1) -> bf16 fragment of fma(q, ds, -dm).
-// The f32 value is exact; each pair is rounded to bf16 (RNE) by one packed convert.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t q0, uint32_t q1, float ds, float dm) {
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Eight weights of one fragment from quant words a0, a1 (bytes 0..3 of each,
+// in K order): the nibbles of bytes 0 and 2, then of bytes 1 and 3, are put
+// in the two 16-bit halves of a dword by one AND each (mask 0x000F000F for the
+// low nibbles, 0x00F000F0 for the high ones, kept in place as 16 q).  Read as
+// binary16, a half holding c is the subnormal c * 2^-24, so with
+// a = d*sc*2^24 (low) or d*sc*2^20 (high) and b = -dmin*m one v_fma_mix_f32
+// gives d*sc*q - dmin*m rounded once: the product is exact, so the value is
+// bit for bit fmaf(q, d*sc, -dmin*m).  That is 2.25 VALU instructions per
+// weight with the pack below, against 2.9 for a byte-to-float convert and an
+// FMA per weight.
+__device__ __forceinline__ void weights8(uint32_t a0, uint32_t a1, uint32_t mask, float a,
+                                         float b, float (&w)[8]) {
+    const half2v e0 = __builtin_bit_cast(half2v, and_mask(a0, mask));
+    const half2v o0 = __builtin_bit_cast(half2v, and_mask(a0 >> 8, mask));
+    const half2v e1 = __builtin_bit_cast(half2v, and_mask(a1, mask));
+    const half2v o1 = __builtin_bit_cast(half2v, and_mask(a1 >> 8, mask));
+    w[0] = fmaf((float)e0.x, a, b);
+    w[1] = fmaf((float)o0.x, a, b);
+    w[2] = fmaf((float)e0.y, a, b);
+    w[3] = fmaf((float)o0.y, a, b);
+    w[4] = fmaf((float)e1.x, a, b);
+    w[5] = fmaf((float)o1.x, a, b);
+    w[6] = fmaf((float)e1.y, a, b);
+    w[7] = fmaf((float)o1.y, a, b);
+}
+
+// Eight exact weights -> one bf16 B fragment (RNE, one packed convert per
+// pair).  make_b forms both row groups' weights before packing either, so no
+// convert directly follows the v_fma_mix_f32 it reads (a wait state each on
+// gfx950).
+__device__ __forceinline__ bf16x8 pack8(const float (&w)[8]) {
     uint4 r;
-    r.x = pack_bf16(fmaf(ubyte(q0, 0), ds, -dm), fmaf(ubyte(q0, 1), ds, -dm));
-    r.y = pack_bf16(fmaf(ubyte(q0, 2), ds, -dm), fmaf(ubyte(q0, 3), ds, -dm));
-    r.z = pack_bf16(fmaf(ubyte(q1, 0), ds, -dm), fmaf(ubyte(q1, 1), ds, -dm));
-    r.w = pack_bf16(fmaf(ubyte(q1, 2), ds, -dm), fmaf(ubyte(q1, 3), ds, -dm));
+    r.x = pack_bf16(w[0], w[1]);
+    r.y = pack_bf16(w[2], w[3]);
+    r.z = pack_bf16(w[4], w[5]);
+    r.w = pack_bf16(w[6], w[7]);
     return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -249,18 +280,20 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     auto compute = [&](int half, const WBlock (&wc)[2], int rbuf, int cj, int chalf, int cbuf,
                        int wj, WBlock (&wn)[2]) {
         const __bf16 *xb = &xs[rbuf][arow];
+        // per sub-block: a = d*sc*2^24 (low nibbles) or d*sc*2^20 (high), b = -dmin*m
         float ds[2][2][2], dm[2][2][2];  // [gg][r][lo/hi sub-block]
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const float d = half_lo(wc[r].hdr.x), dmin = half_hi(wc[r].hdr.x);
+            const float d = half_lo(wc[r].hdr.x), ndmin = -half_hi(wc[r].hdr.x);
+            const float d24 = d * 16777216.f, d20 = d * 1048576.f;
             const Scales sc = unpack_scales(wc[r].hdr.y, wc[r].hdr.z, wc[r].hdr.w);
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
                 const int g = 2 * half + gg;
-                ds[gg][r][0] = d * scale_of(sc, 2 * g);
-                dm[gg][r][0] = dmin * min_of(sc, 2 * g);
-                ds[gg][r][1] = d * scale_of(sc, 2 * g + 1);
-                dm[gg][r][1] = dmin * min_of(sc, 2 * g + 1);
+                ds[gg][r][0] = d24 * scale_of(sc, 2 * g);
+                dm[gg][r][0] = ndmin * min_of(sc, 2 * g);
+                ds[gg][r][1] = d20 * scale_of(sc, 2 * g + 1);
+                dm[gg][r][1] = ndmin * min_of(sc, 2 * g + 1);
             }
         }
         auto load_a = [&](int b, bf16x8 (&A)[T]) {
@@ -273,14 +306,16 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
         };
         auto make_b = [&](int b, bf16x8 (&B)[2]) {
             const int gg = b >> 2, f = b & 3, hi = f >> 1;
+            float wf[2][8];
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const uint4 q = wc[r].q[2 * half + gg];
                 const uint32_t a0 = (f & 1) ? q.z : q.x, a1 = (f & 1) ? q.w : q.y;
-                B[r] = dequant8(and_mask(hi ? a0 >> 4 : a0, 0x0F0F0F0Fu),
-                                and_mask(hi ? a1 >> 4 : a1, 0x0F0F0F0Fu), ds[gg][r][hi],
-                                dm[gg][r][hi]);
+                weights8(a0, a1, hi ? 0x00F000F0u : 0x000F000Fu, ds[gg][r][hi], dm[gg][r][hi],
+                         wf[r]);
             }
+            B[0] = pack8(wf[0]);
+            B[1] = pack8(wf[1]);
         };
         bf16x8 A[2][T], B[2][2];
         load_a(0, A[0]);
