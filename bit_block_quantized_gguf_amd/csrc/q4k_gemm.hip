@@ -68,7 +68,7 @@ typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int BM = 256;        // W rows per tile
 constexpr int KS = 128;        // columns per step (half a super-block)
-constexpr int TOK_PAD = 256;   // token padding of the bf16 X copy (the widest tile)
+constexpr int TOK_PAD = 256;   // tokens the workspace's bf16 X copy is sized for (the widest tile)
 #ifndef GEMM_T1_US
 #define GEMM_T1_US 2.45
 #endif
@@ -109,7 +109,7 @@ struct SKUnits {
 
 struct GemmParams {
     const uint8_t *w;
-    const __bf16 *Xb;   // X rounded to bf16, [P padded to TOK_PAD][K], padding rows zero
+    const __bf16 *Xb;   // X rounded to bf16, [P rounded up to the tile][K], padding rows zero
     float *Y;
     int32_t M, K, P, nb;
     int64_t row_bytes;
@@ -564,6 +564,10 @@ std::atomic<int> g_override_t{0};
 
 int64_t padded_tokens(int64_t P) { return (P + TOK_PAD - 1) / TOK_PAD * TOK_PAD; }
 
+// tokens the bf16 X copy holds for tiles of 32 r tokens: P rounded up to the
+// tile (at most padded_tokens(P), what the workspace is sized for)
+int64_t filled_tokens(int64_t P, int r) { return (P + 32 * r - 1) / (32 * r) * (32 * r); }
+
 }  // namespace
 
 void set_gemm_override(int token_groups, int workgroups) {
@@ -691,7 +695,7 @@ size_t gemm_partial_floats(const GemmLaunch &L, int64_t M, int64_t P) {
 }
 
 size_t gemm_xb_floats(int64_t K, int64_t P) {
-    // bf16 copy of X with the token count padded to the tile
+    // bf16 copy of X with the token count padded to the widest tile
     return (size_t)(padded_tokens(P) * K * 2 / 4);
 }
 
@@ -713,10 +717,10 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     p.row_bytes = (K / 256) * kBlockBytes;
     p.ks = L.ks;
     p.ws = ws.partials;
-    // workspace: [partial tiles][bf16 X, tokens padded]
+    // workspace: [partial tiles][bf16 X, tokens rounded up to the tile]
     __bf16 *xb = reinterpret_cast<__bf16 *>(ws.partials + gemm_partial_floats(L, M, P));
     p.Xb = xb;
-    const int64_t n = P * K, n_pad = padded_tokens(P) * K;
+    const int64_t n = P * K, n_pad = filled_tokens(P, L.r) * K;
     const int64_t cgroups = (n_pad / 8 + 255) / 256;
     if (cgroups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: X too large");
     hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)cgroups), dim3(256), 0, stream, X, xb, n,
@@ -768,8 +772,8 @@ int check_gemm_partition(int64_t M, int64_t K, int64_t P, int tile_tokens, int g
     const SKUnits su = sk_units(M, K, P, L.r, L.ks);
     const int64_t BN = 32 * L.r, tile_floats = (int64_t)BM * BN;
     const int64_t partials = (int64_t)gemm_partial_floats(L, M, P);
-    const int64_t ptok = padded_tokens(P);
-    if ((int64_t)gemm_xb_floats(K, P) * 2 < ptok * K)
+    const int64_t ptok = filled_tokens(P, L.r);
+    if (ptok > padded_tokens(P) || (int64_t)gemm_xb_floats(K, P) * 2 < ptok * K)
         return fail(Q4K_EINVAL, "check: bf16 X copy smaller than its padded tokens");
     if (su.U0 != (int64_t)su.dp * su.G * su.nb || su.U0 > su.U || su.U0 % su.nb != 0)
         return fail(Q4K_EINVAL, "check: %d whole-tile rounds do not end at item %lld",
