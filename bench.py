@@ -406,8 +406,15 @@ def main():
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) * 1e3 / nrep)
             t = float(np.mean(ts))
-            roof_us = max(wbytes(M, K) / HBM_PEAK_GBS / 1e3, 2.0 * M * K * N / 157.3e12 * 1e6)
-            res.append({"N": N, "us": t, "us_per_vector": t / N,
+            # matrix-core bound of the products the kernel issues: f32 MFMA
+            # for N <= 8; for N = 16 three bf16 products per weight and vector
+            # (split operands), at the bf16 rate
+            if N == 16:
+                mm_us, mm = 3 * 2.0 * M * K * N / (BF16_PEAK_TFLOPS * 1e12) * 1e6, "bf16 x3"
+            else:
+                mm_us, mm = 2.0 * M * K * N / 157.3e12 * 1e6, "f32"
+            roof_us = max(wbytes(M, K) / HBM_PEAK_GBS / 1e3, mm_us)
+            res.append({"N": N, "us": t, "us_per_vector": t / N, "matrix_products": mm,
                         "effective_GBps": N * wbytes(M, K) / t / 1e3,
                         "weight_GBps": wbytes(M, K) / t / 1e3,
                         "roofline_us": roof_us, "frac_roofline": roof_us / t})

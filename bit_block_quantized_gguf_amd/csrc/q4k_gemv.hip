@@ -626,6 +626,34 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
 // Four accumulator chains per 4-vector group (low/high nibbles, even/odd
 // byte) keep consecutive MFMAs independent.
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (lo, hi) -> two bf16 (RNE) in one dword, lo in the low half: v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+// the f32 values of the two bf16 halves of a dword (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Eight f32 values -> high parts w1 = bf16(w) and low parts bf16(w - w1)
+// (RNE both; w - w1 is exact in f32).
+__device__ __forceinline__ void split8(const float (&w)[8], bf16x8 &hi, bf16x8 &lo) {
+    uint4 h, l;
+    h.x = pack_bf16(w[0], w[1]);
+    h.y = pack_bf16(w[2], w[3]);
+    h.z = pack_bf16(w[4], w[5]);
+    h.w = pack_bf16(w[6], w[7]);
+    l.x = pack_bf16(w[0] - bf16_lo(h.x), w[1] - bf16_hi(h.x));
+    l.y = pack_bf16(w[2] - bf16_lo(h.y), w[3] - bf16_hi(h.y));
+    l.z = pack_bf16(w[4] - bf16_lo(h.z), w[5] - bf16_hi(h.z));
+    l.w = pack_bf16(w[6] - bf16_lo(h.w), w[7] - bf16_hi(h.w));
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
 
 template <int NV>
 __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(const GemvParams p, const Units un) {
@@ -784,31 +812,36 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(const GemvParams p, 
 }
 
 // ---------------------------------------------------------------------------
-// Batched GEMV for sixteen vectors on v_mfma_f32_16x16x4_f32: one
-// instruction takes 16 rows x 4 columns of W against 4 columns x 16 vectors
-// of X (1,024 multiply-adds in 32 cycles, the rate of four 4x4x1
-// instructions), so each weight formed in a lane feeds one instruction.
-// Same units, staging, ranges and cut-tile finishing as
-// gemv_mfma_kernel.  Wave w computes block w of the unit for the 64 rows as
-// four row groups of 16; lane l = 16 kk + r supplies row r of a group (A)
-// and vector r (B, vector r mod NV when NV < 16: those output columns are
-// never read) at column offset kk:
-//   * it reads quant dwords 2 kk and 2 kk + 1 of each 32-byte group of its
-//     row (one 8-byte LDS read), so the four column offsets of one MFMA are
-//     8 kk + 4 i + e (i = 0, 1; e = byte), and the activations as float4
-//     runs at those offsets;
-//   * each weight is formed exactly (one v_fma_mix_f32, as in gemv_kernel)
-//     from the row's scale and min, which the lane unpacks itself for each
-//     of its four rows;
-//   * lane 16 kk + j ends with rows 4 kk + r (register r) of each group for
-//     vector j; two accumulator chains per group (low and high nibbles).
+// Batched GEMV for sixteen vectors (eight also compile) on
+// v_mfma_f32_16x16x32_bf16, with each exact f32 weight and activation split into two bf16 parts:
+// w = w1 + w2 + e_w and x = x1 + x2 + e_x (w1 = bf16(w), w2 = bf16(w - w1),
+// both RNE; w - w1 is exact in f32), so |e_w| <= 2^-18 |w| and likewise for
+// x.  Three products w1 x1 + w1 x2 + w2 x1 leave out w2 x2 and the e terms,
+// at most about 3 * 2^-18 |w x| per product: well inside an f32 bound of
+// 1e-4 sum |w x|.  A weight that is exactly zero (a row whose scale and min
+// cancel) stays exactly zero in both parts.  One instruction takes 16 rows x
+// 32 columns of W against 32 columns x 16 vectors, so the three of them
+// replace eight 16x16x4 f32 instructions.
+// Same units, staging, ranges and cut-tile finishing as gemv_mfma_kernel.
+// Lane l = 16 kk + r supplies row r of a 16-row group (A) and vector r (B,
+// vector r mod NV when NV < 16: those output columns are never read) for
+// columns 8 kk .. 8 kk + 7 of a 32-column sub-block: its 8 quant bytes
+// 8 kk .. 8 kk + 7 of the 32-byte group hold the low-nibble weights of
+// sub-block 2 gq and the high-nibble ones of sub-block 2 gq + 1 at exactly
+// those columns.  The activations are split once per unit when they are
+// staged, into two bf16 copies whose vector rows are padded by 16 bytes (the
+// sixteen vectors of one fragment read then start on different banks).
+// Lane 16 kk + j ends with rows 4 kk + r (register r) of each group for
+// vector j (the 16x16 output layout); two accumulator chains per group (low
+// and high nibbles), and consecutive instructions use different ones.
 template <int NV>
-__global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p,
-                                                               const Units un) {
-    static_assert(NV == 4 || NV == 8 || NV == 16, "four, eight or sixteen vectors");
-    constexpr int XQ = NV;  // float4s of activations per thread per unit
+__global__ __launch_bounds__(64 * WK) void gemv_split_kernel(const GemvParams p, const Units un) {
+    static_assert(NV == 8 || NV == 16, "eight or sixteen vectors");
+    constexpr int XQ = NV;              // float4s of activations per thread per unit
+    constexpr int XR = 256 * WK + 8;    // bf16 per staged vector row (16-byte pad)
     __shared__ __attribute__((aligned(16))) uint8_t stage[64 * SEGP];
-    __shared__ __attribute__((aligned(16))) float xs[NV][256 * WK];
+    __shared__ __attribute__((aligned(16))) __bf16 x1s[NV][XR];
+    __shared__ __attribute__((aligned(16))) __bf16 x2s[NV][XR];
     __shared__ float red[WK][NV][64];
 
     const int tid = threadIdx.x;
@@ -840,8 +873,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p
             const int co = coff[i] < valid ? coff[i] : 0;
             reg[i] = ldg16(b0 + (uint32_t)min(crow[i], rmax) * (uint32_t)p.row_bytes + (uint32_t)co);
         }
-        // activations of the unit's columns: float4 q = tid + 256 m is vector
-        // q / 256, columns 4 (q % 256) .. +3 of the unit (zero past K)
+        // float4 q = tid + 256 m is vector q / 256, columns 4 (q % 256) .. +3
+        // of the unit (zero past K)
 #pragma unroll
         for (int m = 0; m < XQ; ++m) {
             const int q = tid + 256 * m;
@@ -858,7 +891,12 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p
 #pragma unroll
         for (int m = 0; m < XQ; ++m) {
             const int q = tid + 256 * m;
-            *reinterpret_cast<float4 *>(&xs[q >> 8][4 * (q & 255)]) = xreg[m];
+            const float4 v = xreg[m];
+            const uint32_t h01 = pack_bf16(v.x, v.y), h23 = pack_bf16(v.z, v.w);
+            const uint32_t l01 = pack_bf16(v.x - bf16_lo(h01), v.y - bf16_hi(h01));
+            const uint32_t l23 = pack_bf16(v.z - bf16_lo(h23), v.w - bf16_hi(h23));
+            *reinterpret_cast<uint2 *>(&x1s[q >> 8][4 * (q & 255)]) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2 *>(&x2s[q >> 8][4 * (q & 255)]) = make_uint2(l01, l23);
         }
     };
 
@@ -892,49 +930,51 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma16_kernel(const GemvParams p
                 d20[rg] = d * 1048576.0f;
                 sc[rg] = unpack_scales(h.y, h.z, h.w);
             }
-            const float *xrow = &xs[r16 % NV][256 * wave + 8 * kk];
+            const int xo = 256 * wave + 8 * kk;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                float4 xv[2][2];  // [dword i][low / high nibbles]
+                bf16x8 b1[2], b2[2];  // [low / high nibble sub-block]
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-                        xv[i][hf] = *reinterpret_cast<const float4 *>(xrow + 64 * gq + 32 * hf + 4 * i);
-                GroupF f[4];
-                uint2 qd[4];
+                for (int hf = 0; hf < 2; ++hf) {
+                    b1[hf] = *reinterpret_cast<const bf16x8 *>(&x1s[r16 % NV][xo + 64 * gq + 32 * hf]);
+                    b2[hf] = *reinterpret_cast<const bf16x8 *>(&x2s[r16 % NV][xo + 64 * gq + 32 * hf]);
+                }
+                bf16x8 a1[4][2], a2[4][2];  // [row group][low / high]
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    f[rg] = group_factors(sc[rg], gq, d24[rg], d20[rg], ndm[rg]);
-                    qd[rg] = *reinterpret_cast<const uint2 *>(blk + 16 * rg * SEGP + 16 + 32 * gq +
-                                                              8 * kk);
-                }
+                    const GroupF f = group_factors(sc[rg], gq, d24[rg], d20[rg], ndm[rg]);
+                    const uint2 qd =
+                        *reinterpret_cast<const uint2 *>(blk + 16 * rg * SEGP + 16 + 32 * gq + 8 * kk);
+                    const WordQ q0 = word_unpack(qd.x), q1 = word_unpack(qd.y);
+                    float wl[8], wh[8];  // columns 8 kk + e, e = 4 i + byte
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    WordQ q[4];
-#pragma unroll
-                    for (int rg = 0; rg < 4; ++rg) q[rg] = word_unpack(i ? qd[rg].y : qd[rg].x);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float xle = e == 0 ? xv[i][0].x : e == 1 ? xv[i][0].y
-                                        : e == 2 ? xv[i][0].z : xv[i][0].w;
-                        const float xhe = e == 0 ? xv[i][1].x : e == 1 ? xv[i][1].y
-                                        : e == 2 ? xv[i][1].z : xv[i][1].w;
-#pragma unroll
-                        for (int rg = 0; rg < 4; ++rg) {
-                            const half2v ql = (e & 1) ? q[rg].l13 : q[rg].l02;
-                            const half2v qh = (e & 1) ? q[rg].h13 : q[rg].h02;
-                            const float wl =
-                                fmaf((e & 2) ? (float)ql.y : (float)ql.x, f[rg].al, f[rg].bl);
-                            const float wh =
-                                fmaf((e & 2) ? (float)qh.y : (float)qh.x, f[rg].ah, f[rg].bh);
-                            acc[rg][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(wl, xle, acc[rg][0],
-                                                                             0, 0, 0);
-                            acc[rg][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wh, xhe, acc[rg][1],
-                                                                             0, 0, 0);
-                        }
+                    for (int i = 0; i < 2; ++i) {
+                        const WordQ &q = i ? q1 : q0;
+                        wl[4 * i + 0] = fmaf((float)q.l02.x, f.al, f.bl);
+                        wl[4 * i + 1] = fmaf((float)q.l13.x, f.al, f.bl);
+                        wl[4 * i + 2] = fmaf((float)q.l02.y, f.al, f.bl);
+                        wl[4 * i + 3] = fmaf((float)q.l13.y, f.al, f.bl);
+                        wh[4 * i + 0] = fmaf((float)q.h02.x, f.ah, f.bh);
+                        wh[4 * i + 1] = fmaf((float)q.h13.x, f.ah, f.bh);
+                        wh[4 * i + 2] = fmaf((float)q.h02.y, f.ah, f.bh);
+                        wh[4 * i + 3] = fmaf((float)q.h13.y, f.ah, f.bh);
                     }
+                    split8(wl, a1[rg][0], a2[rg][0]);
+                    split8(wh, a1[rg][1], a2[rg][1]);
                 }
+                // three products per fragment; consecutive instructions go to
+                // different accumulators
+#pragma unroll
+                for (int term = 0; term < 3; ++term)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const bf16x8 &A = term == 2 ? a2[rg][hf] : a1[rg][hf];
+                            const bf16x8 &B = term == 1 ? b2[hf] : b1[hf];
+                            acc[rg][hf] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[rg][hf], 0, 0, 0);
+                        }
             }
         }
         const bool seg_end = !more || last_of_tile;
@@ -1572,18 +1612,21 @@ int64_t units_of(int64_t M, int64_t K, int nmat) {
 // 138.0 at three and 152.7 at four (interleaved runs).  One tile per
 // workgroup (no cut tiles) was slower still.
 // Four, eight and sixteen plain vectors run on the matrix cores: four and
-// eight on the 4x4x1 form, sixteen on the 16x16x4 form, which uses all of
-// its sixteen vector columns there (17408x5120: 60.0 against 68.0 us; for
-// eight vectors half its columns would idle: 48.8 against 37.9 us).
+// eight on the f32 4x4x1 form, sixteen on bf16 16x16x32 instructions with
+// split operands (17408x5120: 42.8 us against 58.4-59.1 on the f32 16x16x4
+// form and 68.0 on the 4x4x1 one).  For eight vectors the split kernel,
+// whose instructions then idle half their columns, measured only 2-3%
+// faster than the 4x4x1 one (37.2-38.1 against 38.5-39.5 us), so eight
+// keep the f32 products.
 template <int NV, int NMAT, int EPI>
 constexpr bool kMfma = NMAT == 1 && EPI == EPI_PLAIN && (NV == 4 || NV == 8 || NV == 16);
 template <int NV>
-constexpr bool kMfma16 = NV == 16;
+constexpr bool kSplit = NV == 16;
 
 template <int NV, int NMAT, int EPI>
 const void *gemv_fn() {
     if constexpr (kMfma<NV, NMAT, EPI>) {
-        if constexpr (kMfma16<NV>) return (const void *)gemv_mfma16_kernel<NV>;
+        if constexpr (kSplit<NV>) return (const void *)gemv_split_kernel<NV>;
         else return (const void *)gemv_mfma_kernel<NV>;
     } else {
         return (const void *)gemv_kernel<NV, NMAT, EPI>;
@@ -1624,8 +1667,8 @@ int launch_t(const GemvParams &p, const GemvLaunch &L, hipStream_t stream) {
     const Units un = make_units(p.M, p.nb, NMAT, L.ks);
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemv: too many rows");
     if constexpr (kMfma<NV, NMAT, EPI>) {
-        if constexpr (kMfma16<NV>)
-            hipLaunchKernelGGL((gemv_mfma16_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0,
+        if constexpr (kSplit<NV>)
+            hipLaunchKernelGGL((gemv_split_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0,
                                stream, p, un);
         else
             hipLaunchKernelGGL((gemv_mfma_kernel<NV>), dim3((unsigned)un.G), dim3(64 * WK), 0,

@@ -233,7 +233,11 @@ int q4k_mlp(const void *w_gate, const void *w_up, const void *w_down, int64_t hi
  *   Y[n][i] = sum_k w_ik * X[n][k],  X f32 [N][K], Y f32 [N][M].
  * The batched witness of "Mac Qwen3.6-27B Metal Q4_K perf diagnosis", §4b,
  * with N distinct activation vectors.  Any N >= 0; the kernels handle up to 16
- * vectors per weight pass (N = 1 gives the q4k_gemv bits).  Workspace:
+ * vectors per weight pass (N = 1 gives the q4k_gemv bits).  Every weight is
+ * formed exactly in f32.  Passes of up to eight vectors multiply in f32; a
+ * pass of sixteen splits each weight and activation into two bf16 parts and
+ * accumulates three bf16 products in f32 (w1 x1 + w1 x2 + w2 x1), which
+ * leaves out at most about 3 * 2^-18 |w x| per product.  Workspace:
  * q4k_workspace_size(Q4K_OP_GEMV_BATCH, M, K, N).  Errors as q4k_gemv.
  */
 int q4k_gemv_batch(const void *w, const float *X, float *Y, int64_t M, int64_t K, int64_t N,
