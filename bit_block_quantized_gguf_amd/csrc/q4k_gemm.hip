@@ -6,10 +6,13 @@
 // that runs on the matrix cores: v_mfma_f32_32x32x16_bf16 with f32
 // accumulation.
 //
-//  * X is rounded to bf16 once (round to nearest even) by a prologue kernel
-//    into a workspace whose token count is padded to the tile with zeros, so
-//    the main loop moves half the bytes, spends no VALU on conversion and
-//    needs no token clamping.
+//  * For tiles of 64 or more tokens, X is rounded to bf16 once (round to
+//    nearest even) by a prologue kernel into a workspace whose token count
+//    is padded to the tile with zeros, so the main loop moves half the
+//    bytes, spends no VALU on conversion and needs no token clamping.
+//    32-token tiles (short prompts) read X in f32 and round it on its way
+//    into LDS instead, which saves the prologue launch; the LDS contents
+//    are the same bits either way.
 //  * Workgroup tile: 256 W rows x (32 * T) tokens, T = 1, 2, 4 or 8 (the
 //    narrow tiles serve short prompts: the dequantisation of a super-block
 //    costs the same at every width, the MFMA work shrinks with it), four
@@ -21,7 +24,8 @@
 //  * K advances half a super-block (128 columns, quant groups g0, g0+1) per
 //    step.  The step's X slice (32T tokens x 128 columns of bf16) is copied
 //    from global memory straight into LDS with global_load_lds_dwordx4, so
-//    it never occupies registers; it is double-buffered (256-token tiles) or
+//    it never occupies registers (32-token tiles: through registers, see
+//    copy_x); it is double-buffered (256-token tiles) or
 //    held in four buffers, both halves of the next super-block copied while
 //    this one computes (narrower tiles: one wait per super-block).  Each token row is
 //    256 bytes = 16 chunks of 16 bytes and chunk c of token t is stored at
@@ -110,6 +114,7 @@ struct SKUnits {
 struct GemmParams {
     const uint8_t *w;
     const __bf16 *Xb;   // X rounded to bf16, [P rounded up to the tile][K], padding rows zero
+    const float *X;     // X itself, [P][K] (read directly by 32-token tiles)
     float *Y;
     int32_t M, K, P, nb;
     int64_t row_bytes;
@@ -242,12 +247,48 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     // k (0: header, 1..4: quant group k-1) of super-block j, row group r, into
     // w.  Issued a few per MFMA block (see compute): a burst of them at once
     // stalls the wave on the memory pipeline's queue.
+    // 32-token tiles read X in f32 and round it to bf16 on its way into LDS,
+    // so no separate rounding launch precedes them: each copy instruction
+    // becomes two 16-byte loads into registers (token rows past P load row
+    // P-1 and are zeroed), and step_end converts them and writes the 16
+    // bytes the DMA would have written, once the step's loads have landed.
+    constexpr bool XF = T == 1;
+    constexpr int XS = XF ? 2 * XI : 1;  // copies staged per super-block
+    const int cx = (lane & 15) ^ ((4 * wave + t_in) & 15);
+    float4 xst[XS][2];
     auto copy_x = [&](int j, int half, int buf, int i) {
-        const int64_t kbyte = ((int64_t)j * 256 + 128 * half) * 2;
-        const int b = 4 * i + wave;
-        const char *src = xbase + (int64_t)16 * i * p.K * 2 + kbyte;
-        __builtin_amdgcn_global_load_lds((gvoid *)(src + xoff), (lvoid *)&xs[buf][b * 4 * KS], 16,
-                                         0, 0);
+        if constexpr (XF) {
+            const int t = tok0 + 16 * i + 4 * wave + t_in;
+            const float *src = p.X + (int64_t)(t < p.P ? t : p.P - 1) * p.K + j * 256 +
+                               128 * half + 8 * cx;
+            xst[half * XI + i][0] = *reinterpret_cast<const float4 *>(src);
+            xst[half * XI + i][1] = *reinterpret_cast<const float4 *>(src + 4);
+        } else {
+            const int64_t kbyte = ((int64_t)j * 256 + 128 * half) * 2;
+            const int b = 4 * i + wave;
+            const char *src = xbase + (int64_t)16 * i * p.K * 2 + kbyte;
+            __builtin_amdgcn_global_load_lds((gvoid *)(src + xoff), (lvoid *)&xs[buf][b * 4 * KS],
+                                             16, 0, 0);
+        }
+    };
+    // staged copies of the two halves -> LDS buffers cb and cb + 1
+    auto flush_x = [&](int cb) {
+        if constexpr (XF) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int i = 0; i < XI; ++i) {
+                    const int b = 4 * i + wave;
+                    const bool in = tok0 + 4 * b + t_in < p.P;
+                    const float4 u = xst[half * XI + i][0], v = xst[half * XI + i][1];
+                    uint4 r;
+                    r.x = in ? pack_bf16(u.x, u.y) : 0u;
+                    r.y = in ? pack_bf16(u.z, u.w) : 0u;
+                    r.z = in ? pack_bf16(v.x, v.y) : 0u;
+                    r.w = in ? pack_bf16(v.z, v.w) : 0u;
+                    *reinterpret_cast<uint4 *>(&xs[cb + half][b * 4 * KS + 8 * lane]) = r;
+                }
+        }
     };
     auto load_w = [&](int j, int r, int k, WBlock (&w)[2]) {
         const uint8_t *bp = wr[r] + (int64_t)j * kBlockBytes;
@@ -356,8 +397,9 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
     // Super-blocks alternate between register sets wa and wb.  Copies past
     // the split's end re-read an in-range block (clamped) and are never used,
     // so the loop body has no branches.
-    auto step_end = [&]() {
+    auto step_end = [&](int cb) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        flush_x(cb);
         __syncthreads();
     };
     WBlock wa[2], wb[2];
@@ -373,7 +415,7 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
 #pragma unroll
             for (int k = 0; k < 5; ++k) load_w(jb, r, k, wa);
     }
-    step_end();
+    step_end(NBUF == 4 ? 2 * (jb & 1) : 0);
     const int last = p.nb - 1;
     int j = jb;
     if constexpr (NBUF == 4) {
@@ -384,34 +426,34 @@ __device__ __forceinline__ void gemm_segment(const GemmParams &p, const SKUnits 
             const int bj = 2 * (j & 1), bn = 2 - bj;
             compute(0, wa, bj, j1, 0, bn, j1, wb);
             compute(1, wa, bj + 1, j1, 1, bn + 1, j1, wb);
-            step_end();
+            step_end(bn);
             compute(0, wb, bn, j2, 0, bj, j2, wa);
             compute(1, wb, bn + 1, j2, 1, bj + 1, j2, wa);
-            step_end();
+            step_end(bj);
         }
         if (j < je) {  // odd count: super-block je-1 (X and W set wa in place)
             const int bj = 2 * (j & 1), bn = 2 - bj;
             compute(0, wa, bj, j, 0, bn, j, wb);
             compute(1, wa, bj + 1, j, 1, bn + 1, j, wb);
-            step_end();
+            step_end(bn);
         }
     } else {
         for (; j + 1 < je; j += 2) {
             const int j2 = j + 2 < p.nb ? j + 2 : last;
             compute(0, wa, 0, j, 1, 1, j + 1, wb);
-            step_end();
+            step_end(0);
             compute(1, wa, 1, j + 1, 0, 0, j + 1, wb);
-            step_end();
+            step_end(0);
             compute(0, wb, 0, j + 1, 1, 1, j2, wa);
-            step_end();
+            step_end(0);
             compute(1, wb, 1, j2, 0, 0, j2, wa);
-            step_end();
+            step_end(0);
         }
         if (j < je) {  // odd count: super-block je-1; its X half 0 and W (set wa) are in place
             compute(0, wa, 0, j, 1, 1, j, wb);
-            step_end();
+            step_end(0);
             compute(1, wa, 1, j, 0, 0, j, wb);
-            step_end();
+            step_end(0);
         }
     }
 
@@ -720,12 +762,15 @@ int launch_gemm(const uint8_t *w, const float *X, float *Y, int64_t M, int64_t K
     // workspace: [partial tiles][bf16 X, tokens rounded up to the tile]
     __bf16 *xb = reinterpret_cast<__bf16 *>(ws.partials + gemm_partial_floats(L, M, P));
     p.Xb = xb;
-    const int64_t n = P * K, n_pad = filled_tokens(P, L.r) * K;
-    const int64_t cgroups = (n_pad / 8 + 255) / 256;
-    if (cgroups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: X too large");
-    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)cgroups), dim3(256), 0, stream, X, xb, n,
-                       n_pad);
-    Q4K_HIP(hipGetLastError());
+    p.X = X;
+    if (L.r != 1) {  // 32-token tiles round X themselves
+        const int64_t n = P * K, n_pad = filled_tokens(P, L.r) * K;
+        const int64_t cgroups = (n_pad / 8 + 255) / 256;
+        if (cgroups > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: X too large");
+        hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)cgroups), dim3(256), 0, stream, X, xb,
+                           n, n_pad);
+        Q4K_HIP(hipGetLastError());
+    }
     const SKUnits su = sk_units(M, K, P, L.r, L.ks);
     const int64_t tiles = su.U / su.nb;
     if (tiles > 0x7FFFFFFF) return fail(Q4K_EUNSUPPORTED, "gemm: too many tiles");
