@@ -8,7 +8,7 @@ dispatch from the FETCH_SIZE / WRITE_SIZE counters, scaled by the reading the
 same counter gives for a plain device copy of known size.
 
     python -m bit_block_quantized_gguf_amd.profiling trace DIR [--kernel SUBSTR] [--grid N]
-    python -m bit_block_quantized_gguf_amd.profiling calls DIR --start SUBSTR [--include SUBSTR]
+    python -m bit_block_quantized_gguf_amd.profiling calls DIR --start SUBSTR[|SUBSTR...] [--include SUBSTR]
     python -m bit_block_quantized_gguf_amd.profiling traffic --fetch DIR --write DIR \
         --kernel SUBSTR --grid N --calib-kernel SUBSTR --calib-bytes B \
         --algorithmic-bytes A --source-hash H --out FILE.json
@@ -49,10 +49,12 @@ def dispatches(directory: str, kernel: str = "", grid: int | None = None) -> lis
 
 def calls(directory: str, start: str, include: str = "") -> list[dict]:
     """Group the dispatches (in time order) into library calls: a call begins
-    at a dispatch whose name contains `start` and takes the following
-    dispatches whose names contain `include` (others are skipped).  Returns,
-    per distinct (grid of the first dispatch, kernel sequence), the number of
-    calls and the median duration of each kernel position and of their sum."""
+    at a dispatch whose name contains `start` (or any of several substrings
+    separated by '|') and takes the following dispatches whose names contain
+    `include` (others are skipped).  Returns, per distinct (grids of its
+    dispatches, kernel sequence), the number of calls and the median duration
+    of each kernel position and of their sum; "grid" is the first
+    dispatch's grid."""
     rows = []
     with open(_csv(directory, "kernel_trace.csv")) as f:
         for r in csv.DictReader(f):
@@ -60,28 +62,31 @@ def calls(directory: str, start: str, include: str = "") -> list[dict]:
                          int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0),
                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     rows.sort()
+    starts = [x for x in start.split("|") if x]
     groups: dict = {}
     cur = None
     for _, name, grid, ns in rows:
-        if start in name:
-            cur = {"grid": grid, "names": [_short(name)], "ns": [ns]}
+        if any(x in name for x in starts):
+            cur = {"grids": [grid], "names": [_short(name)], "ns": [ns]}
             key = None
         elif cur is not None and include and include in name:
+            cur["grids"].append(grid)
             cur["names"].append(_short(name))
             cur["ns"].append(ns)
         else:
             continue
-        # (re)file the call under its current kernel sequence
+        # (re)file the call under its current grids and kernel sequence
         if key is not None:
             groups[key].remove(cur)
-        key = (cur["grid"], tuple(cur["names"]))
+        key = (tuple(cur["grids"]), tuple(cur["names"]))
         groups.setdefault(key, []).append(cur)
     out = []
-    for (grid, names), cs in groups.items():
+    for (grids, names), cs in groups.items():
         if not cs:
             continue
         med = [statistics.median(c["ns"][i] for c in cs) / 1e3 for i in range(len(names))]
-        out.append({"grid": grid, "kernels": list(names), "calls": len(cs), "median_us": med,
+        out.append({"grid": grids[0], "grids": list(grids), "kernels": list(names),
+                    "calls": len(cs), "median_us": med,
                     "median_sum_us": statistics.median(sum(c["ns"]) for c in cs) / 1e3})
     return out
 
@@ -169,8 +174,8 @@ def main(argv=None) -> int:
         return 0
     if a.cmd == "calls":
         for g in calls(a.dir, a.start, a.include):
-            print("first grid %9d  calls %4d  %s  sum %.1f us" % (
-                g["grid"], g["calls"],
+            print("grids %-24s  calls %4d  %s  sum %.1f us" % (
+                "/".join(str(x) for x in g["grids"]), g["calls"],
                 "  ".join("%s %.1f us" % (n, u) for n, u in zip(g["kernels"], g["median_us"])),
                 g["median_sum_us"]))
         return 0

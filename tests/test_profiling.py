@@ -98,3 +98,28 @@ def test_calls_group_consecutive_dispatches(tmp_path):
     assert a["median_sum_us"] == 7.5
     assert b["kernels"] == ["to_bf16_kernel", "gemm_kernel<8>"] and b["calls"] == 1
     assert b["median_sum_us"] == 10.0
+
+
+def test_calls_alternative_starts_keyed_by_all_grids(tmp_path):
+    """A call may start at any of several kernels ('|'); calls whose first
+    kernel has the same grid stay apart when a later kernel's grid differs."""
+    d = tmp_path / "c"
+    d.mkdir()
+    with open(d / "r_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size"])
+        # two shapes of 32-token calls (no rounding prologue): same main grid,
+        # fix-up grids 68 and 20
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<1>(x)", 0, 2000, 65536])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_fixup_kernel<1>(x)", 2000, 2500, 68])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<1>(x)", 3000, 5000, 65536])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_fixup_kernel<1>(x)", 5000, 5700, 20])
+        # a call that does start with the prologue
+        w.writerow(["void q4k::(anonymous namespace)::to_bf16_kernel(float const*)", 6000, 7000, 10])
+        w.writerow(["void q4k::(anonymous namespace)::gemm_kernel<4>(x)", 7000, 9000, 65536])
+    res = {tuple(g["grids"]): g for g in
+           profiling.calls(str(d), "to_bf16_kernel|gemm_kernel<1>", "gemm")}
+    assert set(res) == {(65536, 68), (65536, 20), (10, 65536)}
+    assert res[(65536, 68)]["median_sum_us"] == 2.5
+    assert res[(65536, 20)]["median_sum_us"] == 2.7
+    assert res[(10, 65536)]["kernels"] == ["to_bf16_kernel", "gemm_kernel<4>"]
