@@ -195,6 +195,26 @@ def test_gemv_batch_full_shape(q4k, N):
         assert_gemv(Y[n], Yr[n], S[n], "N=%d n=%d" % (N, n))
 
 
+@pytest.mark.parametrize("N", [8, 16])
+def test_gemv_batch_wide_range(q4k, N):
+    """Activations spread over 2^-80 .. 2^80: vector n is scaled by
+    2^(8n - 60) and each column by a further 2^e, e in [-20, 20].  Sixteen
+    vectors run on bf16 matrix instructions with each f32 operand split into
+    two bf16 parts, which keep the full f32 exponent range; every vector must
+    still meet the f32 bar."""
+    M, K = 512, 2048
+    w, _ = _case(4, 7, M, K)
+    X = synth.activations(4, N, K, first=200)
+    e = np.clip(np.round(synth.normal(synth.key(4, 77), K) * 10.0), -20, 20)
+    X = (X * np.exp2(e)[None, :] * np.exp2(8.0 * np.arange(N) - 60.0)[:, None]).astype(np.float32)
+    note("gemv_batch wide range N=%d" % N)
+    Y = down(q4k.gemv_batch(up(w), up(X), M=M, K=K))
+    Yr, S = oracle.gemv_batch(w, X, M, K)
+    assert np.all(np.isfinite(Y))
+    for n in range(N):
+        assert_gemv(Y[n], Yr[n], S[n], "N=%d n=%d" % (N, n))
+
+
 def test_gemv_batch_one_equals_gemv(q4k):
     M, K = 2000, 5120
     w, x = _case(4, 3, M, K)
