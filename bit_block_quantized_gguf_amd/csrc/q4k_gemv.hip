@@ -609,7 +609,8 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const GemvParams p, const
 }
 
 // ---------------------------------------------------------------------------
-// Batched GEMV on the matrix cores (four, eight or sixteen vectors).  Same
+// Batched GEMV on the matrix cores (four or eight vectors; sixteen compile
+// too but run on gemv_split_kernel below).  Same
 // units, ranges, LDS staging and cut-tile finishing as gemv_kernel: lane l
 // reads row l of the wave's block from LDS and forms each of its 256 weights
 // exactly (one v_fma_mix_f32: d*sc*q - dmin*m).  The products go to
